@@ -1,0 +1,247 @@
+#!/usr/bin/env python3
+"""Benchmark of MoE expert-parallel dispatch + combine on one MI355X.
+
+A step is one pass of the whole path over one batch: routing layout, pack +
+TransferCmd emission (with the CPU proxy threads draining the ring), and the
+gate-weighted combine of the returned rows.  The returned rows are the packed
+rows themselves (identity experts) for bf16, seeded N(0,1) bf16 rows for fp8.
+
+Prints one JSON line: effective HBM GB/s over the algorithmic bytes of the
+step, tokens/s, per-op times from HIP events recorded on the launch stream,
+the roofline of the dominant kernel, and the CPU oracle timed on the host.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload train]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "dispatch+combine effective HBM GB/s (% of peak) and tokens/s, EP32 top-8"
+PEAK_HBM_GBS = 8000.0   # MI355X HBM3E, 8 TB/s
+
+
+def eprint(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def row_bytes(H: int, fmt: int) -> int:
+    return 2 * H if fmt == 0 else H + 4 * (H // 128)
+
+
+def algorithmic_bytes(w, P: int) -> dict:
+    """Bytes the method must move per step (each input read once, each output
+    written once)."""
+    T, H, E, R, k = w.T, w.H, w.E, w.R, w.k
+    rb = row_bytes(H, w.fmt)
+    layout_r = 4 * T * k
+    layout_w = 4 * (2 * R + 2 * E + 2) + T * R + 4 * T * R
+    pack_r = 2 * T * H + 8 * T * k + 4 * T * R + 4 * (R + 1)
+    pack_w = P * rb + P * (4 + 8 * k)
+    comb_r = 2 * P * H + 8 * T * k + 4 * T * R
+    comb_w = 2 * T * H
+    return {"layout": layout_r + layout_w, "dispatch": pack_r + pack_w,
+            "combine": comb_r + comb_w,
+            "total": layout_r + layout_w + pack_r + pack_w + comb_r + comb_w}
+
+
+def cpu_baseline(w, inp, budget_s: float) -> dict:
+    """The oracle as it stands, single thread, on whole passes of the same
+    workload until about budget_s seconds of CPU work."""
+    import numpy as np
+    import oracle
+    oracle.default()
+    passes, t_total, P = 0, 0.0, 0
+    while True:
+        t0 = time.perf_counter()
+        L = oracle.layout(inp["topk_idx"], w.E, w.R)
+        P = L["P"]
+        pk = oracle.pack(inp["x"], inp["topk_idx"], inp["topk_w"], L["send_slot"], w.E, w.R,
+                         w.fmt, capacity_rows=P)
+        oracle.descriptors(L["num_tokens_per_rank"], L["rank_offset"], row_bytes(w.H, w.fmt),
+                           w.channels)
+        if w.fmt == 0:
+            y = pk["send_buf"].view(np.uint16).reshape(P, w.H)
+        else:
+            y = np.zeros((P, w.H), np.uint16)
+        oracle.combine(y, inp["topk_idx"], inp["topk_w"], L["send_slot"], w.E, w.R)
+        t_total += time.perf_counter() - t0
+        passes += 1
+        del pk, y
+        if t_total >= budget_s:
+            break
+    per = t_total / passes
+    gbs = algorithmic_bytes(w, P)["total"] / per / 1e9
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{passes} whole pass(es) of the {w.name} workload (layout, pack, "
+                      f"descriptors, combine); {per:.3f} s per pass, "
+                      f"{w.T / per:.0f} tokens/s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="train")
+    ap.add_argument("--proxy-threads", type=int, default=4)
+    ap.add_argument("--cpu-budget", type=float, default=10.0,
+                    help="seconds of oracle work for the CPU baseline (0: skip)")
+    ap.add_argument("--cold-steps", type=int, default=20,
+                    help="extra steps with the 256 MB last-level cache flushed before each")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the EP ranks are "
+              "simulated as regions of one GPU's HBM", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import combine_topk_rank_amd as ep
+    import workloads as W
+
+    w = W.WORKLOADS[args.workload]
+    eprint(f"bench: workload {w.name} T={w.T} H={w.H} E={w.E} R={w.R} k={w.k} fmt={w.fmt}")
+    inp = W.make_inputs(w, 0)
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    d_x = torch.from_numpy(inp["x"].view(np.int16)).to(dev).view(torch.bfloat16)
+    d_idx = torch.from_numpy(inp["topk_idx"]).to(dev)
+    d_w = torch.from_numpy(inp["topk_w"]).to(dev)
+    s = ep.shape(w.T, w.H, w.E, w.R, w.k, w.fmt)
+    b = ep.Buffers(s, device=dev)
+    cap = b.capacity_rows
+    if w.fmt == 0:
+        y = b.send_buf.view(torch.bfloat16).reshape(cap, w.H)
+    else:
+        g = torch.Generator(device=dev).manual_seed(0)
+        y = torch.randn((cap, w.H), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    ring = ep.Ring(w.depth, w.channels, w.max_inflight, 10_000_000_000)
+    ring.proxy_start(args.proxy_threads, 0)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        b.layout(d_idx, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        b.dispatch(d_x, d_idx, d_w, ring=ring, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        b.combine(y, d_idx, d_w, stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    st = int(b.dev_status.item())
+    if st != 0:
+        eprint(f"device status after warmup: {ep.status_str(st)}")
+        return 1
+    P = int(b.rank_offset[-1].item())
+    ab = algorithmic_bytes(w, P)
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    drained0 = ring.proxy_drained()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    elapsed = t1 - t0
+    st = int(b.dev_status.item())
+    if st != 0:
+        eprint(f"device status after the timed steps: {ep.status_str(st)}")
+        return 1
+    n_cmds = (ring.proxy_drained() - drained0) / K
+
+    def avg_ms(a, z):
+        return sum(e[a].elapsed_time(e[z]) for e in evs) / K
+
+    t_layout, t_disp, t_comb = avg_ms(0, 1), avg_ms(1, 2), avg_ms(2, 3)
+
+    # cold: flush the 256 MB memory-side cache before each step
+    cold = None
+    if args.cold_steps > 0:
+        scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.cold_steps)]
+        for i in range(args.cold_steps):
+            scratch.zero_()
+            step(cev[i])
+        torch.cuda.synchronize()
+        n = args.cold_steps
+        c_l = sum(e[0].elapsed_time(e[1]) for e in cev) / n
+        c_d = sum(e[1].elapsed_time(e[2]) for e in cev) / n
+        c_c = sum(e[2].elapsed_time(e[3]) for e in cev) / n
+        tot = c_l + c_d + c_c
+        cold = {"layout_us": round(c_l * 1e3, 2), "dispatch_us": round(c_d * 1e3, 2),
+                "combine_us": round(c_c * 1e3, 2),
+                "GBps": round(ab["total"] / (tot * 1e-3) / 1e9, 1),
+                "note": "1 GiB written before each step; kernel spans from HIP events"}
+        del scratch
+    ring.proxy_stop(0)
+    ring.destroy()
+
+    value = ab["total"] * K / elapsed / 1e9
+    tokens_s = w.T * K / elapsed
+    # dominant kernel: the longer of pack (inside ep_dispatch) and combine
+    if t_disp >= t_comb:
+        dom, dom_ms, dom_bytes = "pack_kernel (ep_dispatch)", t_disp, ab["dispatch"]
+    else:
+        dom, dom_ms, dom_bytes = "combine_kernel (ep_combine)", t_comb, ab["combine"]
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+
+    cpu = None
+    if args.cpu_budget > 0:
+        eprint("bench: timing the CPU oracle")
+        cpu = cpu_baseline(w, inp, args.cpu_budget)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed * 1e3 / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.fmt == 0 else "fp8-e4m3 pack, bf16 combine",
+        "data": "synthetic (seeded routing and token rows)",
+        "config": {"workload": f"{w.name}: T={w.T} H={w.H} E={w.E} ranks={w.R} top-{w.k}, "
+                               f"{w.channels} ring channels, depth {w.depth}, "
+                               f"{w.max_inflight} in flight",
+                   "tokens": w.T, "hidden": w.H, "experts": w.E, "ranks": w.R, "top_k": w.k,
+                   "pairs_P": P, "parallelism": "one GPU's share of EP"},
+        "tokens_per_s": round(tokens_s, 1),
+        "pct_of_hbm_peak": round(100 * value / PEAK_HBM_GBS, 2),
+        "algorithmic_bytes_per_step": ab,
+        "per_op_us": {"layout": round(t_layout * 1e3, 2), "dispatch": round(t_disp * 1e3, 2),
+                      "combine": round(t_comb * 1e3, 2)},
+        "descriptors_per_step": n_cmds,
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None},
+        "cold": cold,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,97 @@
+// ep_common.h — definitions shared by the HIP sources of the dispatch/combine
+// library (device-side ring view, workspace carving, shape validation).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "ep.h"
+
+namespace ep {
+
+constexpr int kWave = 64;          // CDNA wavefront width (UCCL-EP article s5.1: 32 -> 64)
+constexpr int kBlock = 256;        // threads per workgroup: 4 wavefronts
+constexpr int kLayoutTile = 256;   // tokens per layout workgroup
+constexpr int kMsgRows = 8;        // rows per WRITE message (UCCL-EP s4.1 packing, s5.3 batch 8)
+constexpr int kMaxR = 64;          // a rank set is one 64-bit mask
+constexpr int kMaxE = 4096;        // per-expert LDS histogram bound
+constexpr int kMaxK = 32;          // experts of a token sit in lanes 0..k-1
+constexpr int kPad = 8;            // 64-byte stride between per-channel counters
+
+// Device view of a TransferCmd ring.
+struct RingDev {
+    ep_transfer_cmd_t* slots;              // host-pinned, [channels][depth]
+    const unsigned long long* host_tail;   // host-pinned, consumer position, stride kPad
+    unsigned long long* head;              // device, ticket counter, stride kPad
+    unsigned long long* tail_cache;        // device, last consumer position seen, stride kPad
+    int32_t depth;
+    int32_t channels;
+    int32_t max_inflight;
+    int32_t pad_;
+    unsigned long long timeout_ticks;      // in s_memrealtime ticks
+};
+
+// Carved workspace (all int32).
+struct Workspace {
+    int32_t* blk_rank_cnt;    // [NB, R] per-layout-block rank counts
+    int32_t* blk_exp_cnt;     // [NB, E] per-layout-block expert counts
+    int32_t* msg_base;        // [R+1]   first message index of each rank
+    int32_t* msg_arrivals;    // [max_msgs] rows (x chunks) written per message
+    int32_t* rank_msgs_done;  // [R]     messages of a rank published
+    int64_t max_msgs;
+    int64_t counters_n;       // msg_arrivals .. rank_msgs_done, contiguous
+    int32_t layout_blocks;
+};
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+inline int32_t layout_blocks(int32_t T) {
+    return (int32_t)(T <= 0 ? 1 : ceil_div(T, kLayoutTile));
+}
+
+inline int64_t max_messages(const ep_shape_t& s) {
+    int64_t kr = s.k < s.R ? s.k : s.R;
+    return ceil_div((int64_t)s.T * kr, kMsgRows) + s.R;
+}
+
+size_t workspace_bytes(const ep_shape_t& s);
+Workspace carve_workspace(const ep_shape_t& s, void* base);
+int validate_shape(const ep_shape_t* s);
+size_t row_bytes(int32_t H, int32_t fmt);
+
+#define EP_HIP_CHECK(expr)                          \
+    do {                                            \
+        hipError_t e_ = (expr);                     \
+        if (e_ != hipSuccess) return EP_ERR_HIP;    \
+    } while (0)
+
+// First error wins.
+__device__ inline void set_error(int32_t* st, int code) {
+    atomicCAS(st, 0, code);
+}
+
+__device__ inline int32_t read_status(const int32_t* st) {
+    return __hip_atomic_load(st, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ inline int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
+
+// Broadcast lane `l` (wave-uniform) of a 32-bit value.
+__device__ inline int32_t bcast(int32_t v, int l) { return __builtin_amdgcn_readlane(v, l); }
+__device__ inline uint64_t bcast64(uint64_t v, int l) {
+    uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+    uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+    return ((uint64_t)hi << 32) | lo;
+}
+__device__ inline float bcastf(float v, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+// Number of set bits of `m` below this lane.
+__device__ inline int lane_prefix(uint64_t m) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                          __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+}  // namespace ep

@@ -1,0 +1,386 @@
+// ep_dispatch.hip — pack/permute of token rows into rank-contiguous send
+// buffers (bf16, or OCP e4m3 with per-128 float scales) and emission of
+// batched TransferCmd descriptors into the FIFO a CPU proxy drains.
+//
+// UCCL-EP article:
+//   s4.1 the dispatch kernel prepares the token data, synchronises, then posts
+//        the transfer and goes on without waiting;  small tokens are packed,
+//        several per message (s5.3: batch of 8);
+//   s2.2 the FIFO: lock-free head reservation with atomics, a producer blocks
+//        while 256 commands are in flight;
+//   s2.3 WRITE fields (dst_rank, src_offset, dst_offset, size);
+//   s3.1/s3.2 the Atomic message with an op and a 28-bit value;
+//   s4.2 one FIFO per channel.
+//
+// Work decomposition (token-major): wavefront g handles chunk g % nchunks of
+// token g / nchunks.  It reads its chunk of x once (16-byte loads), and stores
+// it to every destination slot of the token (16-byte stores; 8-byte stores of
+// codes for fp8), so x is read once and the packed rows written once.  A
+// message is the <= 8 consecutive rows [o_r + 8m, ...) of rank r; those rows
+// come from different tokens, hence different wavefronts.  Each wavefront
+// makes its stores visible system-wide (release fence) and then counts itself
+// into the message's arrival counter; the last arrival publishes the WRITE.
+// The last WRITE of a rank is followed by that rank's ATOMIC (its row count),
+// reserved after every WRITE ticket of the rank, so the proxy, which pops in
+// ticket order, sees the count after the rows.
+
+#include "ep_common.h"
+
+namespace ep {
+RingDev ring_device_view(ep_ring_t* r);
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+struct PackArgs {
+    const u32x4* x;               // [T, H/8] 16-byte vectors
+    const int32_t* idx;           // [T, k]
+    const float* w;               // [T, k]
+    const int32_t* rank_off;      // [R+1]
+    const int32_t* send_slot;     // [T, R]
+    uint8_t* send_buf;            // [cap, row_bytes]
+    int32_t* slot_src;            // [cap]
+    int32_t* slot_local_idx;      // [cap, k]
+    float* slot_local_w;          // [cap, k]
+    const int32_t* msg_base;      // [R+1]
+    int32_t* msg_arrivals;        // [max_msgs]
+    int32_t* rank_msgs_done;      // [R]
+    int32_t* st;
+    RingDev ring;
+    int64_t max_msgs;             // entries of msg_arrivals
+    int64_t cap;
+    int64_t row_bytes;
+    int32_t T, H, E, R, k, epr;
+    int32_t nv;                   // 16-byte vectors per x row (H/8)
+    int32_t nchunks;              // wavefronts per token
+    int32_t has_ring;
+};
+
+// ------------------------------------------------------------------ ring
+__device__ inline unsigned long long realtime() { return __builtin_amdgcn_s_memrealtime(); }
+
+// Wait until `ticket` may be written on channel c: fewer than max_inflight
+// commands of the channel may be published but not yet drained.  Returns
+// false on timeout (status set) or when another producer already failed.
+__device__ bool ring_wait(const RingDev& g, int c, unsigned long long ticket, int32_t* st) {
+    unsigned long long* cache = g.tail_cache + (size_t)c * kPad;
+    const unsigned long long* htail = g.host_tail + (size_t)c * kPad;
+    const unsigned long long lim = (unsigned long long)g.max_inflight;
+    unsigned long long seen = __hip_atomic_load(cache, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (ticket < seen + lim) return true;
+    const unsigned long long t0 = realtime();
+    for (;;) {
+        unsigned long long h = __hip_atomic_load(htail, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        if (h > seen) {
+            atomicMax(cache, h);
+            seen = h;
+        }
+        if (ticket < seen + lim) return true;
+        if (read_status(st) != 0) return false;
+        if (realtime() - t0 > g.timeout_ticks) {
+            set_error(st, EP_ERR_RING_TIMEOUT);
+            return false;
+        }
+        __builtin_amdgcn_s_sleep(16);
+    }
+}
+
+// Write one command into its slot: payload first, then seq with a
+// system-scope release, so a consumer that sees seq sees the payload.
+__device__ inline void ring_write(const RingDev& g, int c, unsigned long long ticket, uint32_t type,
+                                  uint32_t op, uint32_t ntok, uint32_t dst_rank, uint32_t size_val,
+                                  uint64_t src_off, uint64_t dst_off) {
+    ep_transfer_cmd_t* slot =
+        g.slots + (size_t)c * g.depth + (size_t)(ticket % (unsigned long long)g.depth);
+    uint32_t* wds = reinterpret_cast<uint32_t*>(slot);
+    wds[1] = type | (op << 8) | (ntok << 16);
+    wds[2] = dst_rank;
+    wds[3] = size_val;
+    u32x4 tail;
+    tail.x = (uint32_t)src_off;
+    tail.y = (uint32_t)(src_off >> 32);
+    tail.z = (uint32_t)dst_off;
+    tail.w = (uint32_t)(dst_off >> 32);
+    *reinterpret_cast<u32x4*>(wds + 4) = tail;
+    __hip_atomic_store(&slot->seq, (uint32_t)(ticket + 1), __ATOMIC_RELEASE,
+                       __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+// Reserve n consecutive tickets on channel c (one atomic per reservation).
+__device__ inline unsigned long long ring_reserve(const RingDev& g, int c, unsigned n) {
+    return atomicAdd(g.head + (size_t)c * kPad, (unsigned long long)n);
+}
+
+// ATOMIC{ADD, cnt} for ranks that receive no rows (nothing to order after).
+__device__ void publish_empty_ranks(const PackArgs& a) {
+    const int lane = lane_id();
+    if (lane < a.R) {
+        int32_t cnt = a.rank_off[lane + 1] - a.rank_off[lane];
+        if (cnt == 0) {
+            const int c = lane % a.ring.channels;
+            unsigned long long tk = ring_reserve(a.ring, c, 1);
+            if (ring_wait(a.ring, c, tk, a.st))
+                ring_write(a.ring, c, tk, EP_CMD_ATOMIC, EP_ATOMIC_ADD, 0, (uint32_t)lane, 0, 0, 0);
+        }
+    }
+}
+
+// Called by lane r of a wavefront that wrote (one chunk of) the row in slot s
+// of rank r, after its release fence.  The last arrival of a message publishes
+// the WRITE, and the last WRITE of a rank is followed by its ATOMIC.
+__device__ void arrive_and_publish(const PackArgs& a, int r, int32_t s) {
+    const int32_t o = a.rank_off[r];
+    const int32_t cnt = a.rank_off[r + 1] - o;
+    const int32_t m = (s - o) / kMsgRows;
+    const int32_t nrows = min(kMsgRows, cnt - m * kMsgRows);
+    const int32_t gm = a.msg_base[r] + m;
+    if (s < o || s >= o + cnt || gm < 0 || gm >= a.max_msgs) {
+        // send_slot does not belong to rank_offset: not from the same layout
+        set_error(a.st, EP_ERR_INVALID_ARG);
+        return;
+    }
+    const int32_t need = nrows * a.nchunks;
+    int32_t old = atomicAdd(&a.msg_arrivals[gm], 1);
+    if (old != need - 1) return;
+    a.msg_arrivals[gm] = 0;   // every arrival is in: leave the counter clean
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    const int c = r % a.ring.channels;
+    const int32_t st0 = read_status(a.st);
+    unsigned long long tk = ring_reserve(a.ring, c, 1);
+    if (st0 == 0 && ring_wait(a.ring, c, tk, a.st)) {
+        const uint64_t rb = (uint64_t)a.row_bytes;
+        ring_write(a.ring, c, tk, EP_CMD_WRITE, 0, (uint32_t)nrows, (uint32_t)r,
+                   (uint32_t)(nrows * rb), (uint64_t)(o + m * kMsgRows) * rb,
+                   (uint64_t)(m * kMsgRows) * rb);
+    }
+    // count this message into its rank only after its WRITE ticket exists: the
+    // added value depends on the ticket, so the two atomics cannot reorder
+    const int32_t nmsgs = (cnt + kMsgRows - 1) / kMsgRows;
+    int32_t one = 1 + (int32_t)(tk >> 62);
+    int32_t done = atomicAdd(&a.rank_msgs_done[r], one);
+    if (done != nmsgs - 1) return;
+    a.rank_msgs_done[r] = 0;
+    unsigned long long tka = ring_reserve(a.ring, c, 1);
+    if (read_status(a.st) == 0 && ring_wait(a.ring, c, tka, a.st))
+        ring_write(a.ring, c, tka, EP_CMD_ATOMIC, EP_ATOMIC_ADD, 0, (uint32_t)r, (uint32_t)cnt, 0, 0);
+}
+
+// ------------------------------------------------------------------ fp8
+// Round to nearest even with saturation to +-448: clamp, then the gfx950
+// OCP e4m3 conversion (round to nearest even).
+template <bool HI>
+__device__ inline uint32_t e4m3x2(float a, float b, uint32_t old) {
+    a = fminf(fmaxf(a, -448.0f), 448.0f);
+    b = fminf(fmaxf(b, -448.0f), 448.0f);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HI);
+}
+
+__device__ inline float bf16lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ inline float bf16hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+
+// max over the 16 lanes of a row group (a 128-element block is 16 lanes x 8)
+__device__ inline float group16_max(float v) {
+    v = fmaxf(v, __shfl_xor(v, 1));
+    v = fmaxf(v, __shfl_xor(v, 2));
+    v = fmaxf(v, __shfl_xor(v, 4));
+    v = fmaxf(v, __shfl_xor(v, 8));
+    return v;
+}
+
+// ------------------------------------------------------------------ kernel
+template <int VPL, int FMT>
+__global__ __launch_bounds__(kBlock) void pack_kernel(PackArgs a) {
+    const int lane = lane_id();
+    const int64_t gw = (int64_t)blockIdx.x * (kBlock / kWave) + (threadIdx.x / kWave);
+    const int64_t P = a.rank_off[a.R];
+    const bool cap_ok = P <= a.cap;
+    if (gw == 0) {
+        if (!cap_ok && lane == 0) set_error(a.st, EP_ERR_CAPACITY);
+        if (a.has_ring && cap_ok) publish_empty_ranks(a);
+    }
+    const int64_t t = gw / a.nchunks;
+    const int chunk = (int)(gw - t * a.nchunks);
+    if (t >= a.T) return;
+
+    int32_t s_lane = -1;
+    if (lane < a.R) s_lane = a.send_slot[t * a.R + lane];
+    const uint64_t dmask = __ballot(s_lane >= 0);
+
+    // load this wavefront's chunk of the row: vectors v0 + lane + 64 i
+    const int v0 = chunk * VPL * kWave;
+    const u32x4* xr = a.x + t * a.nv;
+    u32x4 v[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        int vi = v0 + lane + i * kWave;
+        if (vi < a.nv) v[i] = xr[vi];
+        else v[i] = u32x4{0, 0, 0, 0};
+    }
+
+    if (FMT == EP_FMT_BF16) {
+        for (uint64_t m = dmask; m; m &= m - 1) {
+            const int r = __builtin_ctzll(m);
+            const int32_t s = bcast(s_lane, r);
+            if (s >= a.cap) continue;
+            u32x4* dst = reinterpret_cast<u32x4*>(a.send_buf + (int64_t)s * a.row_bytes);
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) {
+                int vi = v0 + lane + i * kWave;
+                if (vi < a.nv) __builtin_nontemporal_store(v[i], dst + vi);
+            }
+        }
+    } else {
+        // quantise once: per 128-element block, a = max(amax, 1e-4),
+        // codes = e4m3(x * (448 / a)), scale = a / 448
+        u32x2 q[VPL];
+        float scale[VPL];
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            const u32x4 u = v[i];
+            float f0 = bf16lo(u.x), f1 = bf16hi(u.x), f2 = bf16lo(u.y), f3 = bf16hi(u.y);
+            float f4 = bf16lo(u.z), f5 = bf16hi(u.z), f6 = bf16lo(u.w), f7 = bf16hi(u.w);
+            float am = fmaxf(fmaxf(fmaxf(fabsf(f0), fabsf(f1)), fmaxf(fabsf(f2), fabsf(f3))),
+                             fmaxf(fmaxf(fabsf(f4), fabsf(f5)), fmaxf(fabsf(f6), fabsf(f7))));
+            am = group16_max(am);
+            const float av = fmaxf(am, 1e-4f);
+            const float inv = 448.0f / av;
+            scale[i] = av / 448.0f;
+            uint32_t lo = e4m3x2<false>(f0 * inv, f1 * inv, 0);
+            lo = e4m3x2<true>(f2 * inv, f3 * inv, lo);
+            uint32_t hi = e4m3x2<false>(f4 * inv, f5 * inv, 0);
+            hi = e4m3x2<true>(f6 * inv, f7 * inv, hi);
+            q[i] = u32x2{lo, hi};
+        }
+        for (uint64_t m = dmask; m; m &= m - 1) {
+            const int r = __builtin_ctzll(m);
+            const int32_t s = bcast(s_lane, r);
+            if (s >= a.cap) continue;
+            uint8_t* row = a.send_buf + (int64_t)s * a.row_bytes;
+            u32x2* codes = reinterpret_cast<u32x2*>(row);
+            float* scales = reinterpret_cast<float*>(row + a.H);
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) {
+                int vi = v0 + lane + i * kWave;
+                if (vi < a.nv) {
+                    __builtin_nontemporal_store(q[i], codes + vi);
+                    if ((lane & 15) == 0) __builtin_nontemporal_store(scale[i], scales + vi / 16);
+                }
+            }
+        }
+    }
+
+    // per-slot metadata, written by the token's first chunk
+    if (chunk == 0) {
+        int e = -1;
+        float wt = 0.0f;
+        if (lane < a.k) {
+            e = a.idx[t * a.k + lane];
+            wt = a.w[t * a.k + lane];
+        }
+        for (uint64_t m = dmask; m; m &= m - 1) {
+            const int r = __builtin_ctzll(m);
+            const int32_t s = bcast(s_lane, r);
+            if (s >= a.cap) continue;
+            if (lane < a.k) {
+                const bool local = e >= 0 && e < a.E && e / a.epr == r;
+                a.slot_local_idx[(int64_t)s * a.k + lane] = local ? e - r * a.epr : -1;
+                a.slot_local_w[(int64_t)s * a.k + lane] = local ? wt : 0.0f;
+            }
+            if (lane == 0) a.slot_src[s] = (int32_t)t;
+        }
+    }
+
+    if (a.has_ring && cap_ok) {
+        // rows (and metadata) visible to the system before any descriptor
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");
+        if ((dmask >> lane) & 1ull) arrive_and_publish(a, lane, s_lane);
+    }
+}
+
+}  // namespace ep
+
+using namespace ep;
+
+namespace {
+
+template <int VPL>
+int launch_pack(const PackArgs& a, int fmt, int64_t waves, hipStream_t stream) {
+    const int64_t blocks = ceil_div(waves, kBlock / kWave);
+    if (fmt == EP_FMT_BF16)
+        hipLaunchKernelGGL((pack_kernel<VPL, EP_FMT_BF16>), dim3((unsigned)blocks), dim3(kBlock), 0,
+                           stream, a);
+    else
+        hipLaunchKernelGGL((pack_kernel<VPL, EP_FMT_FP8_E4M3_B128>), dim3((unsigned)blocks),
+                           dim3(kBlock), 0, stream, a);
+    return hipGetLastError() == hipSuccess ? EP_OK : EP_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" int ep_dispatch(const ep_shape_t* shape, const void* x, const int32_t* topk_idx,
+                           const float* topk_w, const int32_t* rank_offset,
+                           const int32_t* send_slot, void* send_buf, int64_t capacity_rows,
+                           int32_t* slot_src, int32_t* slot_local_idx, float* slot_local_w,
+                           ep_ring_t* ring, void* workspace, size_t ws_bytes, int32_t* dev_status,
+                           hipStream_t stream) {
+    int v = validate_shape(shape);
+    if (v != EP_OK) return v;
+    const ep_shape_t s = *shape;
+    if (!rank_offset || !dev_status || !workspace || capacity_rows < 0) return EP_ERR_INVALID_ARG;
+    if (s.T > 0 && (!x || !topk_idx || !topk_w || !send_slot)) return EP_ERR_INVALID_ARG;
+    if (capacity_rows > 0 && (!send_buf || !slot_src || !slot_local_idx || !slot_local_w))
+        return EP_ERR_INVALID_ARG;
+    if (((uintptr_t)x | (uintptr_t)send_buf) & 15) return EP_ERR_INVALID_ARG;
+    if (ws_bytes < workspace_bytes(s)) return EP_ERR_INVALID_ARG;
+    Workspace w = carve_workspace(s, workspace);
+
+    PackArgs a{};
+    a.x = reinterpret_cast<const u32x4*>(x);
+    a.idx = topk_idx;
+    a.w = topk_w;
+    a.rank_off = rank_offset;
+    a.send_slot = send_slot;
+    a.send_buf = reinterpret_cast<uint8_t*>(send_buf);
+    a.slot_src = slot_src;
+    a.slot_local_idx = slot_local_idx;
+    a.slot_local_w = slot_local_w;
+    a.msg_base = w.msg_base;
+    a.msg_arrivals = w.msg_arrivals;
+    a.rank_msgs_done = w.rank_msgs_done;
+    a.max_msgs = w.max_msgs;
+    a.st = dev_status;
+    a.ring = ring_device_view(ring);
+    a.has_ring = ring != nullptr;
+    a.cap = capacity_rows;
+    a.row_bytes = (int64_t)row_bytes(s.H, s.fmt);
+    a.T = s.T;
+    a.H = s.H;
+    a.E = s.E;
+    a.R = s.R;
+    a.k = s.k;
+    a.epr = s.E / s.R;
+    a.nv = s.H / 8;
+
+    // vectors per lane: one pass over the row when it fits 16 per lane
+    int vpl;
+    if (a.nv <= 64) vpl = 1;
+    else if (a.nv <= 128) vpl = 2;
+    else if (a.nv <= 256) vpl = 4;
+    else if (a.nv <= 512) vpl = 8;
+    else if (a.nv <= 896) vpl = 14;
+    else vpl = 16;
+    a.nchunks = (int32_t)ceil_div(a.nv, (int64_t)vpl * kWave);
+    int64_t waves = (int64_t)s.T * a.nchunks;
+    if (waves == 0) {
+        if (!a.has_ring) return EP_OK;
+        waves = 1;   // the zero-count ATOMICs still go out
+    }
+    switch (vpl) {
+        case 1: return launch_pack<1>(a, s.fmt, waves, stream);
+        case 2: return launch_pack<2>(a, s.fmt, waves, stream);
+        case 4: return launch_pack<4>(a, s.fmt, waves, stream);
+        case 8: return launch_pack<8>(a, s.fmt, waves, stream);
+        case 14: return launch_pack<14>(a, s.fmt, waves, stream);
+        default: return launch_pack<16>(a, s.fmt, waves, stream);
+    }
+}

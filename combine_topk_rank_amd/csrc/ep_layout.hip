@@ -1,0 +1,262 @@
+// ep_layout.hip — routing layout (per-rank and per-expert histograms, offsets,
+// stable send slots) for one GPU's share of an EP group.
+//
+// A token is sent once to every rank that owns one of its top-k experts
+// (NCCL GIN article, s3.1.1 device-side token routing; UCCL-EP article, s1
+// token-level exchange); expert e lives on rank e / (E/R).  Rank r's rows are
+// [o_r, o_{r+1}) in ascending token order, so the slot of (t, r) is
+// o_r + #{t' < t routed to r}: a stable compaction over T x R bits.  It is
+// computed with wavefront ballots (64-lane, UCCL-EP s5.1) and integer prefix
+// sums only, so the result never depends on scheduling order.
+//
+// Two passes when T spans several 256-token tiles:
+//   layout_count_kernel : per tile, rank counts (ballot + popcount per rank)
+//                         and an LDS expert histogram -> workspace;
+//   layout_main_kernel  : per tile, prefix over the earlier tiles' counts,
+//                         then the slots of its tokens.  Tile 0 also writes
+//                         the counts, offsets and message bases.
+// One pass (layout_main_kernel<true>) when T fits one tile.
+
+#include "ep_common.h"
+
+namespace ep {
+
+// Rank mask of token t; bad ids are reported and skipped.  When `hist` is
+// given, the token's valid experts are counted in it (LDS).
+__device__ inline uint64_t token_rank_mask(const int32_t* __restrict__ idx, int64_t t, int T,
+                                           int E, int k, int epr, int32_t* st, int32_t* hist) {
+    uint64_t m = 0;
+    if (t < T) {
+        const int32_t* row = idx + t * k;
+        for (int j = 0; j < k; ++j) {
+            int e = row[j];
+            if (e == -1) continue;
+            if (e < -1 || e >= E) {
+                set_error(st, EP_ERR_BAD_EXPERT);
+                continue;
+            }
+            m |= 1ull << (e / epr);
+            if (hist) atomicAdd(&hist[e], 1);
+        }
+    }
+    return m;
+}
+
+// Per-wave count of tokens routed to each rank -> wcnt[r].
+__device__ inline void wave_rank_counts(uint64_t mask, int R, int32_t* wcnt) {
+    for (int r = 0; r < R; ++r) {
+        uint64_t b = __ballot((mask >> r) & 1ull);
+        if (lane_id() == 0) wcnt[r] = (int32_t)__popcll(b);
+    }
+}
+
+// Exclusive scan of n (<= kMaxE) ints held in LDS `v`, written to `out`
+// (n+1 entries, out[n] = total).  All kBlock threads take part.
+__device__ inline void block_exclusive_scan_store(const int32_t* v, int n, int32_t* out,
+                                                  int32_t* s_part) {
+    const int tid = threadIdx.x;
+    const int per = (n + kBlock - 1) / kBlock;
+    const int b0 = tid * per;
+    int32_t sum = 0;
+    for (int i = 0; i < per; ++i)
+        if (b0 + i < n) sum += v[b0 + i];
+    s_part[tid] = sum;
+    __syncthreads();
+    if (tid == 0) {
+        int32_t run = 0;
+        for (int i = 0; i < kBlock; ++i) {
+            int32_t x = s_part[i];
+            s_part[i] = run;
+            run += x;
+        }
+        out[n] = run;
+    }
+    __syncthreads();
+    int32_t run = s_part[tid];
+    for (int i = 0; i < per; ++i) {
+        if (b0 + i < n) {
+            out[b0 + i] = run;
+            run += v[b0 + i];
+        }
+    }
+}
+
+__device__ inline void zero_counters(int32_t* p, int64_t n, int64_t first, int64_t stride) {
+    for (int64_t i = first; i < n; i += stride) p[i] = 0;
+}
+
+__global__ __launch_bounds__(kBlock) void layout_count_kernel(
+    const int32_t* __restrict__ idx, int T, int E, int R, int k, int epr,
+    int32_t* __restrict__ blk_rank_cnt, int32_t* __restrict__ blk_exp_cnt,
+    int32_t* __restrict__ counters, int64_t counters_n, int32_t* st) {
+    __shared__ int32_t s_hist[kMaxE];
+    __shared__ int32_t s_wcnt[kBlock / kWave][kMaxR];
+    const int tid = threadIdx.x;
+    const int wave = tid / kWave;
+    for (int e = tid; e < E; e += kBlock) s_hist[e] = 0;
+    __syncthreads();
+    const int64_t t = (int64_t)blockIdx.x * kLayoutTile + tid;
+    uint64_t mask = token_rank_mask(idx, t, T, E, k, epr, st, s_hist);
+    wave_rank_counts(mask, R, s_wcnt[wave]);
+    __syncthreads();
+    if (tid < R) {
+        int32_t c = 0;
+        for (int w = 0; w < kBlock / kWave; ++w) c += s_wcnt[w][tid];
+        blk_rank_cnt[(int64_t)blockIdx.x * R + tid] = c;
+    }
+    for (int e = tid; e < E; e += kBlock) blk_exp_cnt[(int64_t)blockIdx.x * E + e] = s_hist[e];
+    zero_counters(counters, counters_n, (int64_t)blockIdx.x * kBlock + tid,
+                  (int64_t)gridDim.x * kBlock);
+}
+
+template <bool SINGLE>
+__global__ __launch_bounds__(kBlock) void layout_main_kernel(
+    const int32_t* __restrict__ idx, int T, int E, int R, int k, int epr, int nblocks,
+    const int32_t* __restrict__ blk_rank_cnt, const int32_t* __restrict__ blk_exp_cnt,
+    int32_t* __restrict__ cnt_rank, int32_t* __restrict__ cnt_exp,
+    int32_t* __restrict__ rank_off, int32_t* __restrict__ exp_off, int32_t* __restrict__ msg_base,
+    uint8_t* __restrict__ in_rank, int32_t* __restrict__ send_slot,
+    int32_t* __restrict__ counters, int64_t counters_n, int32_t* st) {
+    __shared__ int32_t s_hist[SINGLE ? kMaxE : 1];
+    __shared__ int32_t s_exp[kMaxE];
+    __shared__ int32_t s_wcnt[kBlock / kWave][kMaxR];
+    __shared__ int32_t s_pre[kMaxR];     // rows of rank r in earlier tiles
+    __shared__ int32_t s_tot[kMaxR];     // rows of rank r in all tiles
+    __shared__ int32_t s_base[kMaxR];    // first slot of rank r in this tile
+    __shared__ int32_t s_part[kBlock];
+    const int tid = threadIdx.x;
+    const int lane = lane_id();
+    const int wave = tid / kWave;
+    const int b = blockIdx.x;
+
+    if (SINGLE) {
+        for (int e = tid; e < E; e += kBlock) s_hist[e] = 0;
+        __syncthreads();
+    }
+    const int64_t t_first = (int64_t)b * kLayoutTile;
+    const int64_t t = t_first + tid;
+    uint64_t mask = token_rank_mask(idx, t, T, E, k, epr, st, SINGLE ? s_hist : nullptr);
+    wave_rank_counts(mask, R, s_wcnt[wave]);
+    __syncthreads();
+
+    // rank totals and the prefix over earlier tiles
+    if (tid < R) {
+        int32_t pre = 0, tot = 0;
+        if (SINGLE) {
+            for (int w = 0; w < kBlock / kWave; ++w) tot += s_wcnt[w][tid];
+        } else {
+            for (int bb = 0; bb < nblocks; ++bb) {
+                int32_t c = blk_rank_cnt[(int64_t)bb * R + tid];
+                if (bb < b) pre += c;
+                tot += c;
+            }
+        }
+        s_pre[tid] = pre;
+        s_tot[tid] = tot;
+    }
+    __syncthreads();
+    if (wave == 0) {
+        // exclusive scan of the rank totals across lanes (R <= 64)
+        int32_t tot = lane < R ? s_tot[lane] : 0;
+        int32_t msgs = (tot + kMsgRows - 1) / kMsgRows;
+        int32_t incl = tot, mincl = msgs;
+        for (int d = 1; d < kWave; d <<= 1) {
+            int32_t o = __shfl_up(incl, d);
+            int32_t mo = __shfl_up(mincl, d);
+            if (lane >= d) {
+                incl += o;
+                mincl += mo;
+            }
+        }
+        int32_t off = incl - tot;
+        if (lane < R) s_base[lane] = off + s_pre[lane];
+        if (b == 0) {
+            if (lane < R) {
+                cnt_rank[lane] = tot;
+                rank_off[lane] = off;
+                msg_base[lane] = mincl - msgs;
+            }
+            if (lane == R - 1) {
+                rank_off[R] = incl;
+                msg_base[R] = mincl;
+            }
+        }
+    }
+    if (b == 0) {
+        // per-expert totals and their exclusive scan
+        for (int e = tid; e < E; e += kBlock) {
+            int32_t c = 0;
+            if (SINGLE) {
+                c = s_hist[e];
+            } else {
+                for (int bb = 0; bb < nblocks; ++bb) c += blk_exp_cnt[(int64_t)bb * E + e];
+            }
+            s_exp[e] = c;
+            cnt_exp[e] = c;
+        }
+        __syncthreads();
+        block_exclusive_scan_store(s_exp, E, exp_off, s_part);
+    }
+    __syncthreads();
+
+    // slots: lane r < R walks this wave's 64 tokens in order
+    int32_t run = 0;
+    if (lane < R) {
+        run = s_base[lane];
+        for (int w = 0; w < wave; ++w) run += s_wcnt[w][lane];
+    }
+    const int64_t t_wave = t_first + (int64_t)wave * kWave;
+    for (int i = 0; i < kWave; ++i) {
+        const int64_t tt = t_wave + i;
+        if (tt >= T) break;
+        uint64_t m = bcast64(mask, i);
+        if (lane < R) {
+            int bit = (int)((m >> lane) & 1ull);
+            send_slot[tt * R + lane] = bit ? run : -1;
+            in_rank[tt * R + lane] = (uint8_t)bit;
+            run += bit;
+        }
+    }
+    if (SINGLE) zero_counters(counters, counters_n, tid, kBlock);
+}
+
+}  // namespace ep
+
+using namespace ep;
+
+extern "C" int ep_dispatch_layout(const ep_shape_t* shape, const int32_t* topk_idx,
+                                  int32_t* num_tokens_per_rank, int32_t* num_tokens_per_expert,
+                                  int32_t* rank_offset, int32_t* expert_offset,
+                                  uint8_t* is_token_in_rank, int32_t* send_slot, void* workspace,
+                                  size_t ws_bytes, int32_t* dev_status, hipStream_t stream) {
+    int v = validate_shape(shape);
+    if (v != EP_OK) return v;
+    const ep_shape_t s = *shape;
+    if (!num_tokens_per_rank || !num_tokens_per_expert || !rank_offset || !expert_offset ||
+        !dev_status || !workspace)
+        return EP_ERR_INVALID_ARG;
+    if (s.T > 0 && (!topk_idx || !is_token_in_rank || !send_slot)) return EP_ERR_INVALID_ARG;
+    if (ws_bytes < workspace_bytes(s)) return EP_ERR_INVALID_ARG;
+    Workspace w = carve_workspace(s, workspace);
+    const int epr = s.E / s.R;
+    const int nb = w.layout_blocks;
+    int32_t* counters = w.msg_arrivals;
+    if (nb == 1) {
+        hipLaunchKernelGGL(layout_main_kernel<true>, dim3(1), dim3(kBlock), 0, stream, topk_idx,
+                           s.T, s.E, s.R, s.k, epr, 1, (const int32_t*)nullptr,
+                           (const int32_t*)nullptr, num_tokens_per_rank, num_tokens_per_expert,
+                           rank_offset, expert_offset, w.msg_base, is_token_in_rank, send_slot,
+                           counters, w.counters_n, dev_status);
+    } else {
+        hipLaunchKernelGGL(layout_count_kernel, dim3(nb), dim3(kBlock), 0, stream, topk_idx, s.T,
+                           s.E, s.R, s.k, epr, w.blk_rank_cnt, w.blk_exp_cnt, counters,
+                           w.counters_n, dev_status);
+        hipLaunchKernelGGL(layout_main_kernel<false>, dim3(nb), dim3(kBlock), 0, stream, topk_idx,
+                           s.T, s.E, s.R, s.k, epr, nb, w.blk_rank_cnt, w.blk_exp_cnt,
+                           num_tokens_per_rank, num_tokens_per_expert, rank_offset, expert_offset,
+                           w.msg_base, is_token_in_rank, send_slot, counters, w.counters_n,
+                           dev_status);
+    }
+    EP_HIP_CHECK(hipGetLastError());
+    return EP_OK;
+}

@@ -1,0 +1,231 @@
+/*
+ * ep.h — C ABI of the MI355X (gfx950) MoE expert-parallel dispatch/combine
+ * library: one GPU's share of an EP group, with the destination EP ranks
+ * simulated as regions of the GPU's own HBM.
+ *
+ * Sources (page, section):
+ *   UCCL-EP article (peacm.com/news/835744):
+ *     s2.1  the GPU only writes a TransferCmd into a local FIFO and goes on
+ *           computing; CPU proxy threads do the transfers;
+ *     s2.2  FIFO ring {head, tail, slots, inflight_count}, lock-free head/tail
+ *           with atomics, batched enqueue of up to 8 commands, non-blocking
+ *           completion query, producer blocked at 256 commands in flight;
+ *     s2.3  proxy loop: dequeue, switch on the type, WRITE ->
+ *           PostRDMAWrite(dst_rank, src_offset, dst_offset, size);
+ *     s3.1  the message types (Write, Atomic, Drain, Barrier);
+ *     s3.2  an atomic carries an op and a value (4-bit op, 28-bit value);
+ *     s4.1  low-latency mode: small tokens packed into one message; the
+ *           dispatch kernel prepares the token data, synchronises, posts the
+ *           transfer and goes on;
+ *     s4.2  high-throughput mode: 8 independent FIFOs per GPU;
+ *     s5.1  AMD port: 64-lane wavefronts instead of 32-lane warps;
+ *     s5.2  tuning: FIFO depth 1024, 256 in flight, 8 channels, drain batch 32;
+ *     s5.3  pack small messages with batch size 8;
+ *     s6    EP32 dispatch and combine latencies.
+ *   NCCL GIN article (bjdmk.com.cn/news/2086017):
+ *     s2.2.1 caller-registered windows addressed by byte offsets;
+ *     s3.1.1 device-side routing: each token goes to the owner of its expert;
+ *     s4.2.1 error codes such as "window full".
+ *   GPU communication notes (blog.zhenwei.site), s5: reuse long-lived
+ *     buffers, keep explicit synchronisation boundaries; DeepEP dispatch and
+ *     combine for MoE.
+ *
+ * Conventions for every call below:
+ *   - Device pointers are HIP device allocations on the current device; the
+ *     caller owns them and the stream.  The library never allocates device
+ *     memory on the dispatch/combine path: scratch state comes in through
+ *     `workspace` (size from ep_workspace_bytes) and the ring owns its own
+ *     memory from ep_ring_create until ep_ring_destroy.
+ *   - Calls enqueue kernels on `stream` and return at once with the result of
+ *     host-side validation (EP_OK or EP_ERR_INVALID_ARG / EP_ERR_HIP).  Errors
+ *     found on the device (bad expert id, capacity, ring timeout) are written to
+ *     the device word `*dev_status` (int32, first error wins; the caller zeroes
+ *     it and reads it after synchronising the stream).
+ *   - Shapes: T tokens, H hidden size, E experts, R ranks, k experts per token.
+ *     Requirements: T >= 0; H >= 8 and H % 8 == 0 (bf16) or H % 512 == 0
+ *     (fp8); 1 <= R <= 64; E % R == 0; E <= 4096; 1 <= k <= min(E, 32);
+ *     T * R < 2^31; T * max(k, R) < 2^31.
+ *   - Expert e lives on rank e / (E / R).  A token goes once to every rank
+ *     that owns one of its experts (the (token, rank) pair is the unit of
+ *     dispatch).  Expert id -1 is a dropped choice and is skipped.
+ *   - Alignment: x, send_buf, y and out are 16-byte aligned.
+ */
+#ifndef EP_H
+#define EP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return value of every call and value of the device status word. */
+enum ep_status {
+    EP_OK = 0,
+    EP_ERR_INVALID_ARG = 1,   /* host-side validation failed; nothing enqueued */
+    EP_ERR_BAD_EXPERT = 2,    /* device: an expert id outside [-1, E) */
+    EP_ERR_CAPACITY = 3,      /* device: P > capacity_rows */
+    EP_ERR_RING_TIMEOUT = 4,  /* device: a producer waited longer than the ring's timeout */
+    EP_ERR_HIP = 5,           /* a HIP runtime call failed */
+    EP_ERR_BUSY = 6           /* ring call not allowed while its proxy threads run */
+};
+
+/* Row format of the send buffer. */
+enum ep_format {
+    EP_FMT_BF16 = 0,           /* a row is the token's H bf16 values: 2H bytes */
+    EP_FMT_FP8_E4M3_B128 = 1   /* H OCP e4m3 codes, then H/128 float scales */
+};
+
+/* TransferCmd types (UCCL-EP s3.1) and atomic ops (s3.2). */
+enum { EP_CMD_WRITE = 1, EP_CMD_ATOMIC = 2 };
+enum { EP_ATOMIC_ADD = 1 };
+
+typedef struct ep_shape {
+    int32_t T, H, E, R, k, fmt;
+} ep_shape_t;
+
+/* One FIFO slot, 32 bytes: the command a CPU proxy would execute
+ * (UCCL-EP s2.3 WRITE fields; s3.2 op/value).  Written by the GPU into host
+ * memory; `seq` is written last and equals the slot's ticket + 1.
+ *   WRITE : copy `size_or_value` bytes holding `num_tokens` (1..8) rows from
+ *           byte `src_offset` of the send buffer to byte `dst_offset` of rank
+ *           `dst_rank`'s receive region.
+ *   ATOMIC: add `size_or_value` (the rank's row count, < 2^28) to rank
+ *           `dst_rank`'s count word; follows all of that rank's WRITEs in
+ *           its channel. */
+typedef struct ep_transfer_cmd {
+    uint32_t seq;
+    uint8_t type;
+    uint8_t op;
+    uint16_t num_tokens;
+    uint32_t dst_rank;
+    uint32_t size_or_value;
+    uint64_t src_offset;
+    uint64_t dst_offset;
+} ep_transfer_cmd_t;
+
+typedef struct ep_ring ep_ring_t;
+
+/* Bytes of one send-buffer row: 2H for bf16, H + 4*(H/128) for fp8. */
+size_t ep_row_bytes(int32_t H, int32_t fmt);
+
+/* Bytes of device workspace that ep_dispatch_layout and ep_dispatch need for
+ * `shape` (per-block partial counts, per-message arrival counters).  One
+ * workspace serves a layout call and the dispatch calls that follow it on the
+ * same stream; its contents need no initialisation.  Returns 0 for an invalid
+ * shape. */
+size_t ep_workspace_bytes(const ep_shape_t* shape);
+
+/* Routing layout.  UCCL-EP s1 (token-level exchange with many
+ * peers), NCCL GIN s3.1.1 (each token is routed to the owner of its expert).
+ *   topk_idx              int32 [T,k]   expert ids, -1 = dropped
+ *   num_tokens_per_rank   int32 [R]     cnt_r = #tokens with >= 1 expert on r
+ *   num_tokens_per_expert int32 [E]     cnt_e = #(t,j) with topk_idx = e
+ *   rank_offset           int32 [R+1]   exclusive scan of cnt_r; P = rank_offset[R]
+ *   expert_offset         int32 [E+1]   exclusive scan of cnt_e
+ *   is_token_in_rank      uint8 [T,R]   1 if token t goes to rank r
+ *   send_slot             int32 [T,R]   row of (t,r) in the send buffer, or -1;
+ *                                       rank r's rows are [o_r, o_{r+1}) in
+ *                                       ascending token order
+ * Device error: EP_ERR_BAD_EXPERT (the offending entry is skipped). */
+int ep_dispatch_layout(const ep_shape_t* shape, const int32_t* topk_idx,
+                       int32_t* num_tokens_per_rank, int32_t* num_tokens_per_expert,
+                       int32_t* rank_offset, int32_t* expert_offset,
+                       uint8_t* is_token_in_rank, int32_t* send_slot,
+                       void* workspace, size_t workspace_bytes,
+                       int32_t* dev_status, hipStream_t stream);
+
+/* Pack and descriptor emission.  UCCL-EP s4.1 (prepare the
+ * token data, then post the transfer), s2.2 (FIFO), s4.2/s5.2 (channels).
+ * Must follow ep_dispatch_layout on the same stream with the same workspace.
+ *   x              bf16 [T,H]           token rows
+ *   topk_idx/_w    int32/float [T,k]    routing and gate weights
+ *   rank_offset, send_slot              from ep_dispatch_layout
+ *   send_buf       [capacity_rows, ep_row_bytes(H, fmt)]  rank-contiguous rows;
+ *                  for fp8 each row is quantised once per token: per 128-element
+ *                  block a = max(max|x|, 1e-4), codes e4m3(x * (448/a)) with
+ *                  round-to-nearest-even and saturation, scale a/448
+ *   slot_src       int32 [capacity_rows]    token of each row
+ *   slot_local_idx int32 [capacity_rows,k]  e_j - r*E/R if e_j is on the row's
+ *                                           rank r, else -1
+ *   slot_local_w   float [capacity_rows,k]  w_j if e_j is on r, else 0
+ *   ring           may be NULL (no descriptors).  Otherwise, per rank r, rows
+ *                  [o_r, o_{r+1}) are cut into messages of <= 8 rows, each a
+ *                  WRITE published on channel r % channels only after its rows
+ *                  are written (system-scope release), followed by one
+ *                  ATOMIC ADD of cnt_r (also for cnt_r = 0).
+ * Device errors: EP_ERR_CAPACITY (rows >= capacity_rows are not written and
+ * no descriptor is emitted), EP_ERR_RING_TIMEOUT (the ring stayed full for
+ * longer than its timeout; the ring must then be reset), EP_ERR_INVALID_ARG
+ * (send_slot and rank_offset do not come from the same layout). */
+int ep_dispatch(const ep_shape_t* shape, const void* x, const int32_t* topk_idx,
+                const float* topk_w, const int32_t* rank_offset, const int32_t* send_slot,
+                void* send_buf, int64_t capacity_rows,
+                int32_t* slot_src, int32_t* slot_local_idx, float* slot_local_w,
+                ep_ring_t* ring, void* workspace, size_t workspace_bytes,
+                int32_t* dev_status, hipStream_t stream);
+
+/* Combine.  UCCL-EP s6 (EP combine), GPU communication notes s5
+ * (DeepEP combine).  The returned expert outputs y sit in the dispatch
+ * layout: y row send_slot[t,r] is rank r's result for token t.
+ *   W[t,r]   = sum of w[t,j] (float adds, ascending j) over j with
+ *              e_j != -1 on rank r
+ *   out[t,:] = bf16_rne( sum over ranks r ascending with send_slot[t,r] >= 0
+ *              of W[t,r] * y[send_slot[t,r], :] ), accumulated with float fma
+ *   y   bf16 [y_rows,H] (y_rows >= P), out bf16 [T,H].  Tokens with no
+ *       destination get zeros.
+ * Device error: EP_ERR_CAPACITY if a slot is >= y_rows (that row is skipped). */
+int ep_combine(const ep_shape_t* shape, const void* y, int64_t y_rows,
+               const int32_t* topk_idx, const float* topk_w, const int32_t* send_slot,
+               void* out, int32_t* dev_status, hipStream_t stream);
+
+/* ---- TransferCmd ring (UCCL-EP s2.2, s2.3, s5.2) ---------------------------
+ * `channels` FIFOs of `depth` slots each; a producer blocks while
+ * `max_inflight` commands of its channel are published but not yet drained,
+ * and gives up with EP_ERR_RING_TIMEOUT after `timeout_ns`.  Slots and the
+ * consumer position live in host-pinned coherent memory (the consumer is a
+ * CPU proxy); the producer ticket counter and a cached copy of the consumer
+ * position live in device memory.  Allocated on the current device; returns
+ * NULL on invalid arguments (depth < 1, channels < 1 or > 64,
+ * max_inflight < 1 or > depth, timeout_ns < 1) or allocation failure.
+ * A ring serves one stream at a time. */
+ep_ring_t* ep_ring_create(int32_t depth, int32_t channels, int32_t max_inflight,
+                          int64_t timeout_ns);
+int ep_ring_destroy(ep_ring_t* ring);
+
+/* Host-only, while no kernel uses the ring and no proxy runs: clear slots,
+ * tickets and positions. */
+int ep_ring_reset(ep_ring_t* ring);
+
+/* Stand-in for one proxy dequeue: pop up to `max` published commands of
+ * `channel` in FIFO order into `out`, mark them completed and return their
+ * number in *n_out.  EP_ERR_BUSY while proxy threads run. */
+int ep_ring_drain(ep_ring_t* ring, int32_t channel, ep_transfer_cmd_t* out,
+                  int32_t max, int32_t* n_out);
+
+/* Proxy threads (UCCL-EP s2.3): `threads` host threads poll the channels
+ * (thread i serves channels i, i+threads, ...), pop commands in batches of
+ * up to 32, mark them completed and append them to a log of `log_capacity`
+ * entries (further commands are counted, not logged). */
+int ep_ring_proxy_start(ep_ring_t* ring, int32_t threads, int64_t log_capacity);
+
+/* Stop the proxy threads after they have drained every command published so
+ * far; copy up to `log_max` logged commands into `log_out` (may be NULL) and
+ * return the number logged and drained in *n_logged and *n_drained. */
+int ep_ring_proxy_stop(ep_ring_t* ring, ep_transfer_cmd_t* log_out, int64_t log_max,
+                       int64_t* n_logged, int64_t* n_drained);
+
+/* Commands drained so far by the proxy threads (a live counter). */
+int64_t ep_ring_proxy_drained(const ep_ring_t* ring);
+
+/* Text of a status code. */
+const char* ep_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EP_H */

@@ -93,7 +93,7 @@ class Oracle:
         return int(self.L.oracle_row_bytes(H, fmt))
 
     def layout(self, topk_idx: np.ndarray, E: int, R: int) -> dict:
-        """Rank membership, histograms, offsets and send slots (a1, a2)."""
+        """Rank membership, histograms, offsets and send slots."""
         idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
         T, k = idx.shape
         out = {
@@ -132,7 +132,7 @@ class Oracle:
              send_slot: np.ndarray, E: int, R: int, fmt: int,
              capacity_rows: int, poison: int = 0xA5) -> dict:
         """Pack rows into the rank-contiguous send buffer with per-slot
-        metadata (a3, a4).  Unwritten bytes keep the ``poison`` fill;
+        metadata.  Unwritten bytes keep the ``poison`` fill;
         unwritten metadata keeps -7 / -7 / NaN."""
         x = np.ascontiguousarray(x, dtype=np.uint16)
         idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
@@ -152,7 +152,7 @@ class Oracle:
 
     def descriptors(self, num_tokens_per_rank: np.ndarray, rank_offset: np.ndarray,
                     row_bytes_: int, channels: int) -> np.ndarray:
-        """Closed-form TransferCmd stream (a5), channel-major order."""
+        """Closed-form TransferCmd stream, channel-major order."""
         cnt = np.ascontiguousarray(num_tokens_per_rank, dtype=np.int32)
         off = np.ascontiguousarray(rank_offset, dtype=np.int32)
         R = cnt.size
@@ -165,7 +165,7 @@ class Oracle:
 
     def combine(self, y: np.ndarray, topk_idx: np.ndarray, topk_w: np.ndarray,
                 send_slot: np.ndarray, E: int, R: int, H: Optional[int] = None) -> np.ndarray:
-        """Gate-weighted gather-reduce of the returned rows (a6), float64."""
+        """Gate-weighted gather-reduce of the returned rows, float64."""
         y = np.ascontiguousarray(y, dtype=np.uint16)
         idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
         w = np.ascontiguousarray(topk_w, dtype=np.float32)

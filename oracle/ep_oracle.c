@@ -24,8 +24,8 @@
  *   [NOTES] GPU communication notes, blog.zhenwei.site, s5 optimisation list
  *           (DeepEP dispatch/combine, combine overlapped with the next layer).
  * The pages never print the dispatch/combine arithmetic.  Where they are
- * silent the plainest reading is used; each reading is stated, with an
- * R-number, at the place where it is applied.
+ * silent the plainest reading is used; each reading is stated at the place
+ * where it is applied.
  *
  * Parity status of each function:
  *   oracle_layout         pinned: brute-force set enumeration, invariants
@@ -80,19 +80,19 @@ static float bf16_to_float(uint16_t b) {
 
 int64_t oracle_row_bytes(int H, int fmt) {
     if (fmt == ORC_FMT_BF16) return 2LL * H;
-    /* R9: H code bytes followed by H/128 fp32 scales */
+    /* reading: H code bytes followed by H/128 fp32 scales, unpadded */
     return (int64_t)H + 4LL * (H / 128);
 }
 
-/* ------------------------------------------------------------ a1 + a2 layout
+/* ------------------------------------------------------------ routing layout
  * Rank membership, histograms, offsets and stable send slots.
- * R1: expert e lives on rank e / (E/R) (contiguous blocks of experts).
- * R2: the unit of dispatch is the (token, destination rank) pair: a token is
+ * Reading: expert e lives on rank e / (E/R) (contiguous blocks of experts).
+ * Reading: the unit of dispatch is the (token, destination rank) pair: a token is
  *     sent once to each rank that owns at least one of its top-k experts
  *     ([GIN] s3.1.1 sends each token to the owner of its expert; [UCCL] s1
  *     token-level exchange with dozens of peers).
- * R3: inside a rank's segment, rows are in ascending token order.
- * R4: expert id -1 is a dropped choice and is skipped; any other id outside
+ * Reading: inside a rank's segment, rows are in ascending token order.
+ * Reading: expert id -1 is a dropped choice and is skipped; any other id outside
  *     [0,E) is an error (ORC_ERR_BAD_EXPERT); outputs are then unspecified.
  */
 int oracle_layout(int T, int E, int R, int k, const int32_t* topk_idx,
@@ -142,13 +142,13 @@ int oracle_layout(int T, int E, int R, int k, const int32_t* topk_idx,
     return ORC_OK;
 }
 
-/* ------------------------------------------------------------ a4 fp8 e4m3
+/* ------------------------------------------------------------ fp8 e4m3
  * OCP 8-bit floating point, E4M3 ("FN": no infinities).  Written from the
  * format definition: sign bit, 4 exponent bits with bias 7, 3 mantissa bits;
  * exponent field 0 holds subnormals m * 2^-9; S.1111.111 is NaN, so the largest
  * finite magnitude is S.1111.110 = 1.75 * 2^8 = 448.  Conversion from float
  * rounds to nearest, ties to even, and saturates magnitudes beyond 448 to 448
- * (R7: OCP E4M3FN with saturation; the pages never name an fp8 format).
+ * (reading: OCP E4M3FN with saturation; the pages never name an fp8 format).
  * The sign bit is kept for zero and for values that round to zero.
  * NaN input gives 0x7F with the input's sign.
  */
@@ -188,8 +188,8 @@ float oracle_e4m3_decode(uint8_t c) {
     return (float)(s ? -v : v);
 }
 
-/* Quantise one bf16 row of H elements into the fp8 row format (R9):
- * H code bytes, then H/128 float32 scales.  Per 128-element block b (R8):
+/* Quantise one bf16 row of H elements into the fp8 row format (reading):
+ * H code bytes, then H/128 float32 scales.  Per 128-element block b (reading):
  *   amax = max |x_i|  (exact in float),  a = max(amax, 1e-4f),
  *   inv = 448 / a  (one IEEE float division),
  *   q_i = e4m3(x_i * inv)  (one IEEE float multiply, then the conversion),
@@ -217,10 +217,10 @@ void oracle_quantize_row(int H, const uint16_t* xrow, uint8_t* out_row) {
     }
 }
 
-/* ------------------------------------------------------------ a3 (+a4) pack
+/* ------------------------------------------------------------ pack
  * For every (t, r) with is_token_in_rank: row t (bf16 bytes, or its fp8 row)
  * goes to send_buf row send_slot[t,r] ([UCCL] s4.1 "prepare token data" before
- * posting the transfer).  Per-slot metadata (R6): slot_src[s] = t;
+ * posting the transfer).  Per-slot metadata (reading): slot_src[s] = t;
  * slot_local_idx[s,j] = e_j - r*epr if e_j lives on r else -1;
  * slot_local_w[s,j] = w[t,j] if e_j lives on r else 0.
  * Rows with s >= capacity are not written and ORC_ERR_CAPACITY is returned. */
@@ -261,17 +261,17 @@ int oracle_pack(int T, int H, int E, int R, int k, int fmt,
     return status;
 }
 
-/* ------------------------------------------------------------ a5 descriptors
+/* ------------------------------------------------------------ descriptors
  * Closed form of the command stream ([UCCL] s2.3 WRITE fields, s3.1 message
  * types, s4.1 token packing, s4.2/s5.2 channels, s5.3 batch of 8):
- *   R10: each rank's segment [o_r, o_{r+1}) is cut greedily into messages of
+ *   Reading: each rank's segment [o_r, o_{r+1}) is cut greedily into messages of
  *        at most 8 consecutive rows, starting at o_r;  message m of rank r is
  *        WRITE{dst_rank=r, src_offset=(o_r+8m)*row_bytes,
  *              dst_offset=8m*row_bytes, size=n*row_bytes, num_tokens=n}.
- *   R11: after its WRITEs, each rank gets ATOMIC{dst_rank=r, op=ADD,
+ *   Reading: after its WRITEs, each rank gets ATOMIC{dst_rank=r, op=ADD,
  *        value=cnt_r} (also when cnt_r = 0), so the receiver learns its count.
- *   R12: dst_offset is relative to the start of rank r's receive region.
- *   R13: rank r uses channel r mod C.
+ *   Reading: dst_offset is relative to the start of rank r's receive region.
+ *   Reading: rank r uses channel r mod C.
  * Records are emitted per channel c = 0..C-1, ranks ascending within the
  * channel, messages ascending, then the rank's ATOMIC.  Returns the number of
  * records (or -1 if max is too small). */
@@ -311,10 +311,10 @@ int64_t oracle_descriptors(int R, int C, const int32_t* num_tokens_per_rank,
     return n;
 }
 
-/* ------------------------------------------------------------ a6 combine
+/* ------------------------------------------------------------ combine
  * The returned expert outputs Y sit in the dispatch layout: row
  * send_slot[t,r] holds what rank r sends back for token t.  The combined
- * output is the gate-weighted sum over the token's destination ranks (R15):
+ * output is the gate-weighted sum over the token's destination ranks (reading):
  *   W[t,r]  = sum of w[t,j] over j with e_j != -1 and rank(e_j) = r
  *   out[t,h] = sum over r with send_slot[t,r] >= 0 of W[t,r] * Y[slot, h]
  * evaluated in double precision (the exact definition up to double rounding;

@@ -1,0 +1,108 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/*.h declares, and validates arguments on the host (no kernel is
+launched for an invalid call).  Also checks that the HIP library and the CPU
+oracle share no code."""
+
+import ctypes
+import glob
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"\b(ep_[a-z0-9_]+)\s*\(", text):
+            names.add(m.group(1))
+    return sorted(names)
+
+
+@pytest.fixture(scope="module")
+def ep():
+    import combine_topk_rank_amd as ep
+    return ep
+
+
+def test_exports_every_declared_symbol(ep):
+    names = declared_functions()
+    assert len(names) >= 13
+    lib = ctypes.CDLL(ep.LIB_PATH)
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_row_bytes(ep):
+    assert ep.ep_row_bytes(7168, ep.EP_FMT_BF16) == 14336
+    assert ep.ep_row_bytes(7168, ep.EP_FMT_FP8_E4M3_B128) == 7392
+    assert ep.ep_row_bytes(512, ep.EP_FMT_BF16) == 1024
+    assert ep.ep_row_bytes(7, ep.EP_FMT_BF16) == 0
+    assert ep.ep_row_bytes(7168, 9) == 0
+
+
+def test_workspace_bytes(ep):
+    assert ep.ep_workspace_bytes(ep.shape(4096, 7168, 256, 32, 8)) > 0
+    assert ep.ep_workspace_bytes(ep.shape(0, 64, 16, 4, 2)) > 0
+    for bad in [ep.shape(-1, 64, 16, 4, 2), ep.shape(16, 7, 16, 4, 2), ep.shape(16, 64, 15, 4, 2),
+                ep.shape(16, 64, 16, 65, 2), ep.shape(16, 64, 16, 4, 0), ep.shape(16, 64, 16, 4, 17),
+                ep.shape(16, 64, 8192, 4, 2), ep.shape(16, 7168 + 128, 256, 32, 8, 1),
+                ep.shape(16, 64, 16, 4, 2, 5), ep.shape(16, 64, 64, 4, 33)]:
+        assert ep.ep_workspace_bytes(bad) == 0
+
+
+def test_host_validation_rejects_without_launch(ep):
+    L = ep.lib
+    bad = ep.shape(16, 7, 16, 4, 2)
+    assert L.ep_dispatch_layout(ctypes.byref(bad), *([None] * 7), None, 0, None, None) == 1
+    good = ep.shape(16, 64, 16, 4, 2)
+    # null outputs / missing workspace
+    assert L.ep_dispatch_layout(ctypes.byref(good), *([None] * 7), None, 0, None, None) == 1
+    assert L.ep_dispatch(ctypes.byref(good), *([None] * 6), 0, None, None, None, None, None, 0,
+                         None, None) == 1
+    assert L.ep_combine(ctypes.byref(good), None, 0, None, None, None, None, None, None) == 1
+    # misaligned x
+    assert L.ep_dispatch(ctypes.byref(good), 8, 16, 16, 16, 16, 256, 10, 16, 16, 16, None, 256,
+                         1 << 20, 16, None) == 1
+    # T = 0 combine is a no-op
+    zero = ep.shape(0, 64, 16, 4, 2)
+    assert L.ep_combine(ctypes.byref(zero), None, 0, None, None, None, None, 16, None) == 0
+
+
+def test_ring_create_rejects_bad_arguments(ep):
+    L = ep.lib
+    for args in [(0, 1, 1, 1), (8, 0, 1, 1), (8, 65, 1, 1), (8, 1, 0, 1), (8, 1, 9, 1), (8, 1, 4, 0)]:
+        assert not L.ep_ring_create(*args)
+
+
+def test_status_strings(ep):
+    for st in range(7):
+        assert ep.status_str(st) != "unknown status"
+    assert ep.status_str(99) == "unknown status"
+
+
+def test_command_record_layout(ep):
+    import oracle
+    assert ep.CMD_DTYPE.itemsize == 32
+    assert ep.CMD_DTYPE == oracle.CMD_DTYPE
+    offs = {n: ep.CMD_DTYPE.fields[n][1] for n in ep.CMD_DTYPE.names}
+    assert offs == {"seq": 0, "type": 4, "op": 5, "num_tokens": 6, "dst_rank": 8,
+                    "size_or_value": 12, "src_offset": 16, "dst_offset": 24}
+
+
+def test_oracle_and_hip_path_share_nothing():
+    prod = glob.glob(os.path.join(ROOT, "combine_topk_rank_amd", "**", "*.*"), recursive=True)
+    prod += glob.glob(os.path.join(ROOT, "include", "*.h"))
+    for p in prod:
+        if p.endswith((".hip", ".h", ".py", ".cpp")):
+            text = open(p).read()
+            assert "oracle" not in text.lower(), p
+    orc = glob.glob(os.path.join(ROOT, "oracle", "*.c")) + glob.glob(os.path.join(ROOT, "oracle", "*.py"))
+    for p in orc:
+        text = open(p).read()
+        assert "combine_topk_rank_amd" not in text and "ep.h" not in text, p

@@ -1,0 +1,110 @@
+"""Device-side error reporting, forced from the host so that every kernel
+still ends normally: a bad expert id, a send buffer below capacity, a ring
+that nobody drains (a short timeout on the kernel's own bounded wait), and
+inconsistent layout arguments."""
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from gpu_helpers import assert_layout_equal, assert_pack_equal, log, run_hip
+
+pytestmark = pytest.mark.gpu
+
+
+def test_bad_expert_reported_and_skipped():
+    rng = np.random.default_rng(31)
+    inp = W.make_random_case(rng, 300, 64, 32, 8, 4)
+    idx = inp["topk_idx"].copy()
+    idx[7, 1] = 32          # == E
+    idx[200, 3] = -5
+    log("[errors] bad expert ids")
+    g = run_hip(300, 64, 32, 8, 4, 0, inp["x"], idx, inp["topk_w"], ring_cfg=None)
+    assert g["status"] == 2
+    # the bad entries are skipped: same layout as with them dropped
+    clean = idx.copy()
+    clean[7, 1] = -1
+    clean[200, 3] = -1
+    L = oracle.layout(clean, 32, 8)
+    assert_layout_equal(g, L)
+
+
+def test_capacity_exceeded():
+    rng = np.random.default_rng(32)
+    T, H, E, R, k = 200, 128, 32, 8, 4
+    inp = W.make_random_case(rng, T, H, E, R, k)
+    L = oracle.layout(inp["topk_idx"], E, R)
+    cap = L["P"] - 3
+    pk = oracle.pack(inp["x"], inp["topk_idx"], inp["topk_w"], L["send_slot"], E, R, 0,
+                     capacity_rows=cap)
+    assert pk["status"] == 3
+    log("[errors] capacity")
+    g = run_hip(T, H, E, R, k, 0, inp["x"], inp["topk_idx"], inp["topk_w"], capacity_rows=cap,
+                ring_cfg=(1024, 2, 256, 5_000_000_000))
+    assert g["status"] == 3
+    assert_pack_equal(g, pk, cap)
+    lg, nd = g["logs"][0]
+    assert nd == 0          # nothing is announced for a partial send
+
+
+def test_ring_timeout_without_consumer():
+    """No proxy runs and only 2 commands may be in flight: producers give up
+    after the ring's 2 ms timeout and report it."""
+    import combine_topk_rank_amd as ep
+    w = W.WORKLOADS["tiny"]
+    inp = W.make_inputs(w, 0)
+    log("[errors] ring timeout (no consumer, 2 ms)")
+    g = run_hip(w.T, w.H, w.E, w.R, w.k, w.fmt, inp["x"], inp["topk_idx"], inp["topk_w"],
+                ring_cfg=(8, 1, 2, 2_000_000), proxy_threads=0)
+    assert g["status"] == ep.EP_ERR_RING_TIMEOUT
+    ring = g["ring"]
+    first = ring.drain(0)
+    assert len(first) == 2           # the two commands that fit
+    ring.reset()
+    assert len(ring.drain(0)) == 0
+
+
+def test_manual_drain_api():
+    """Without proxy threads, ep_ring_drain pops what fits in flight."""
+    w = W.WORKLOADS["decode"]
+    inp = W.make_inputs(w, 0)
+    L = oracle.layout(inp["topk_idx"], w.E, w.R)
+    want = oracle.descriptors(L["num_tokens_per_rank"], L["rank_offset"],
+                              oracle.row_bytes(w.H, w.fmt), 1)
+    assert len(want) <= 256
+    log("[errors] manual drain, decode")
+    g = run_hip(w.T, w.H, w.E, w.R, w.k, w.fmt, inp["x"], inp["topk_idx"], inp["topk_w"],
+                ring_cfg=(1024, 1, 256, 5_000_000_000), proxy_threads=0)
+    assert g["status"] == 0
+    got = g["ring"].drain(0, 4096)
+    from gpu_helpers import assert_descriptors
+    assert_descriptors(got, want, 1, first_seq=1)
+    assert np.all(np.diff(got["seq"].astype(np.int64)) == 1)   # FIFO order
+
+
+def test_inconsistent_slots_rejected():
+    """send_slot from one layout with rank_offset of another: reported, no
+    descriptor escapes, nothing outside the buffers is touched."""
+    import combine_topk_rank_amd as ep
+    import torch
+    from gpu_helpers import dev, dev_bf16
+    rng = np.random.default_rng(33)
+    T, H, E, R, k = 64, 64, 16, 4, 2
+    inp = W.make_random_case(rng, T, H, E, R, k)
+    s = ep.shape(T, H, E, R, k)
+    b = ep.Buffers(s)
+    d_idx, d_w, d_x = dev(inp["topk_idx"]), dev(inp["topk_w"]), dev_bf16(inp["x"])
+    log("[errors] inconsistent rank_offset")
+    b.layout(d_idx)
+    torch.cuda.synchronize()
+    bad_off = torch.zeros_like(b.rank_offset)
+    bad_off[-1] = b.rank_offset[-1]           # every rank starts at 0
+    ring = ep.Ring(64, 1, 16, 1_000_000_000)
+    ring.proxy_start(1, 1024)
+    ep.ep_dispatch(s, d_x, d_idx, d_w, bad_off, b.send_slot, b.send_buf, b.slot_src,
+                   b.slot_local_idx, b.slot_local_w, ring, b.workspace, b.dev_status)
+    torch.cuda.synchronize()
+    lg, nd = ring.proxy_stop(1024)
+    assert int(b.dev_status.item()) == ep.EP_ERR_INVALID_ARG
+    assert all(d["type"] != 1 or d["dst_rank"] == 0 for d in lg)

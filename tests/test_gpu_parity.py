@@ -1,0 +1,179 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bit-exact: counts, offsets, membership, send slots, packed bytes (poisoned
+buffers, rows past P untouched), per-slot metadata, fp8 codes and scales, and
+the TransferCmd multiset (plus per-channel ticket order).  Combine: within
+|gpu - ref| <= 1e-2 * max(1, |ref|) of the oracle's float64 value."""
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle_pins as pins
+import workloads as W
+from gpu_helpers import (assert_descriptors, assert_layout_equal, assert_pack_equal,
+                         combine_tolerance_check, log, run_hip, run_hip_combine)
+
+pytestmark = pytest.mark.gpu
+
+RING_TIMEOUT_NS = 5_000_000_000
+
+
+def _full_case(name):
+    w = W.WORKLOADS[name]
+    log(f"[parity] workload {name}: T={w.T} H={w.H} E={w.E} R={w.R} k={w.k} fmt={w.fmt} "
+        f"channels={w.channels}")
+    inp = pins.workload_inputs(name)
+    L = oracle.layout(inp["topk_idx"], w.E, w.R)
+    P = L["P"]
+    cap = P + 8
+    pk = oracle.pack(inp["x"], inp["topk_idx"], inp["topk_w"], L["send_slot"], w.E, w.R, w.fmt,
+                     capacity_rows=cap)
+    rb = oracle.row_bytes(w.H, w.fmt)
+    want = oracle.descriptors(L["num_tokens_per_rank"], L["rank_offset"], rb, w.channels)
+    log(f"[parity] {name}: P={P}, {len(want)} descriptors; running HIP layout+dispatch")
+    g = run_hip(w.T, w.H, w.E, w.R, w.k, w.fmt, inp["x"], inp["topk_idx"], inp["topk_w"],
+                capacity_rows=cap, ring_cfg=(w.depth, w.channels, w.max_inflight, RING_TIMEOUT_NS))
+    return w, inp, L, pk, want, g
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "train", "fp8", "skewed"])
+def test_workload_parity(name):
+    w, inp, L, pk, want, g = _full_case(name)
+    assert g["status"] == 0, g["status"]
+    assert_layout_equal(g, L)
+    assert_pack_equal(g, pk, L["P"])
+    lg, n_drained = g["logs"][0]
+    assert n_drained == len(want) == len(lg)
+    assert_descriptors(lg, want, w.channels, first_seq=1)
+
+    # combine on synthetic expert outputs Y (N(0,1) bf16, [P, H])
+    y = W.make_expert_outputs(L["P"], w.H, 0)
+    ref = oracle.combine(y, inp["topk_idx"], inp["topk_w"], L["send_slot"], w.E, w.R)
+    log(f"[parity] {name}: HIP combine on synthetic Y")
+    got, st = run_hip_combine(g["buffers"], y, g["d_idx"], g["d_w"])
+    assert st == 0
+    emax, frac = combine_tolerance_check(got, ref, f"{name} combine")
+    log(f"[parity] {name}: combine max abs err {emax:.3g} ({frac:.3g} of the tolerance)")
+
+    # identity experts: Y = the packed rows (bf16) or their dequantised values
+    # (fp8), both built from the oracle's send buffer
+    P = L["P"]
+    if w.fmt == W.FMT_BF16:
+        yid = pk["send_buf"][:P].view(np.uint16).reshape(P, w.H)
+    else:
+        yid = dequant_rows(pk["send_buf"][:P], w.H)
+    ref_id = oracle.combine(yid, inp["topk_idx"], inp["topk_w"], L["send_slot"], w.E, w.R)
+    got_id, st = run_hip_combine(g["buffers"], np.ascontiguousarray(yid), g["d_idx"], g["d_w"])
+    assert st == 0
+    combine_tolerance_check(got_id, ref_id, f"{name} identity combine")
+    if w.routing != "softmax_top":
+        # gate weights sum to 1: identity combine returns the input
+        xf = W.bf16_bits_to_f32(inp["x"]).astype(np.float64)
+        combine_tolerance_check(got_id, xf if w.fmt == W.FMT_BF16 else ref_id, f"{name} x round trip")
+        if w.fmt == W.FMT_BF16:
+            same = np.mean(got_id == xf)
+            log(f"[parity] {name}: identity combine equals x on {100 * same:.3f}% of elements")
+            assert same > 0.999
+
+
+def dequant_rows(rows: np.ndarray, H: int) -> np.ndarray:
+    """bf16 bits of code * scale for fp8 rows (e4m3 values from the format
+    definition)."""
+    codes_t, vals = pins.e4m3_table()
+    lut = np.zeros(256, np.float64)
+    lut[codes_t] = vals
+    lut[codes_t | 0x80] = -vals
+    lut[0x7F] = lut[0xFF] = np.nan
+    codes = rows[:, :H]
+    scales = rows[:, H:].copy().view(np.float32).astype(np.float64)
+    v = lut[codes] * np.repeat(scales, 128, axis=1)
+    return W.f32_to_bf16_bits(v.astype(np.float32))
+
+
+def test_deterministic_repeat():
+    """Two runs on the same inputs give bit-identical outputs (slots come from
+    prefix sums, never from atomic order)."""
+    w = W.WORKLOADS["train"]
+    inp = pins.workload_inputs("train")
+    log("[parity] determinism: train, two runs")
+    a = run_hip(w.T, w.H, w.E, w.R, w.k, w.fmt, inp["x"], inp["topk_idx"], inp["topk_w"])
+    b = run_hip(w.T, w.H, w.E, w.R, w.k, w.fmt, inp["x"], inp["topk_idx"], inp["topk_w"])
+    for key in ("send_slot", "is_token_in_rank", "rank_offset", "send_buf", "slot_src",
+                "slot_local_idx"):
+        assert np.array_equal(a[key], b[key]), key
+
+
+# (T, H, E, R, k, fmt, drop_prob, channels, depth, max_inflight)
+CASES = [
+    (1, 8, 1, 1, 1, 0, 0.0, 1, 4, 1),
+    (0, 64, 16, 4, 2, 0, 0.0, 2, 8, 4),
+    (5, 16, 6, 3, 2, 0, 0.3, 2, 8, 2),
+    (1000, 200, 64, 8, 6, 0, 0.1, 3, 16, 4),
+    (700, 7168, 256, 32, 8, 0, 0.0, 8, 64, 16),
+    (300, 1024, 64, 64, 4, 0, 0.0, 64, 32, 8),
+    (2000, 512, 4096, 64, 32, 0, 0.05, 8, 1024, 256),
+    (513, 64, 16, 1, 2, 0, 0.0, 1, 32, 8),
+    (257, 512, 32, 16, 8, 1, 0.0, 4, 16, 4),
+    (130, 4096, 128, 8, 4, 1, 0.2, 8, 1024, 256),
+    (4099, 136, 32, 4, 3, 0, 0.5, 1, 1024, 256),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "T%d_H%d_E%d_R%d_k%d_f%d" % c[:6])
+def test_random_case_parity(case):
+    T, H, E, R, k, fmt, drop, C, depth, mif = case
+    rng = np.random.default_rng(1000 + CASES.index(case))
+    inp = W.make_random_case(rng, T, H, E, R, k, drop_prob=drop)
+    L = oracle.layout(inp["topk_idx"], E, R)
+    P = L["P"]
+    cap = P + 5
+    pk = oracle.pack(inp["x"], inp["topk_idx"], inp["topk_w"], L["send_slot"], E, R, fmt,
+                     capacity_rows=cap)
+    want = oracle.descriptors(L["num_tokens_per_rank"], L["rank_offset"], oracle.row_bytes(H, fmt), C)
+    log(f"[parity] case {case}: P={P}")
+    g = run_hip(T, H, E, R, k, fmt, inp["x"], inp["topk_idx"], inp["topk_w"], capacity_rows=cap,
+                ring_cfg=(depth, C, mif, RING_TIMEOUT_NS))
+    assert g["status"] == 0
+    assert_layout_equal(g, L)
+    assert_pack_equal(g, pk, P)
+    lg, nd = g["logs"][0]
+    assert nd == len(want)
+    assert_descriptors(lg, want, C, first_seq=1)
+    y = W.make_expert_outputs(P, H, 3)
+    ref = oracle.combine(y, inp["topk_idx"], inp["topk_w"], L["send_slot"], E, R, H=H)
+    got, st = run_hip_combine(g["buffers"], y, g["d_idx"], g["d_w"])
+    assert st == 0
+    combine_tolerance_check(got, ref, f"case {case}")
+
+
+def test_duplicate_experts_in_a_token():
+    """A token that names the same expert twice counts it twice per expert and
+    once per rank."""
+    idx = np.array([[3, 3], [0, 5], [5, 5], [-1, 3]], np.int32)
+    w = np.array([[0.25, 0.5], [0.5, 0.125], [1.0, 2.0], [3.0, 0.5]], np.float32)
+    x = W.f32_to_bf16_bits(np.arange(4 * 16, dtype=np.float32).reshape(4, 16))
+    E, R = 8, 4
+    L = oracle.layout(idx, E, R)
+    pk = oracle.pack(x, idx, w, L["send_slot"], E, R, 0, capacity_rows=L["P"] + 2)
+    log("[parity] duplicate experts")
+    g = run_hip(4, 16, E, R, 2, 0, x, idx, w, capacity_rows=L["P"] + 2, ring_cfg=(8, 2, 4, RING_TIMEOUT_NS))
+    assert g["status"] == 0
+    assert_layout_equal(g, L)
+    assert_pack_equal(g, pk, L["P"])
+    y = W.make_expert_outputs(L["P"], 16, 4)
+    ref = oracle.combine(y, idx, w, L["send_slot"], E, R)
+    got, _ = run_hip_combine(g["buffers"], y, g["d_idx"], g["d_w"])
+    combine_tolerance_check(got, ref, "duplicates")
+
+
+def test_layout_many_tiles():
+    """A long token axis: many 256-token tiles in the two-pass layout."""
+    T, E, R, k = 40000, 256, 64, 8
+    rng = np.random.default_rng(17)
+    inp = W.make_random_case(rng, T, 8, E, R, k, drop_prob=0.02)
+    L = oracle.layout(inp["topk_idx"], E, R)
+    log("[parity] layout T=40000 R=64")
+    g = run_hip(T, 8, E, R, k, 0, inp["x"], inp["topk_idx"], inp["topk_w"], ring_cfg=None)
+    assert g["status"] == 0
+    assert_layout_equal(g, L)

@@ -4,7 +4,7 @@ combine on one MI355X.
 Argument marshalling only.  Every step of the path runs in the HIP kernels of
 libep.so; torch supplies device memory and streams.  There is no fallback:
 importing this package fails loudly when libep.so has not been built
-(``python -m combine_topk_rank_amd.build``).
+(``python combine_topk_rank_amd/build.py``).
 
 The functions keep the C names:
 
@@ -59,7 +59,10 @@ CMD_DTYPE = np.dtype([
 class EpError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
-        super().__init__(f"{where}: {status_str(status)} ({status})")
+        detail = ""
+        if status == EP_ERR_HIP:
+            detail = " [" + lib.ep_last_error().decode() + "]"
+        super().__init__(f"{where}: {status_str(status)} ({status}){detail}")
 
 
 class ep_shape_t(ctypes.Structure):
@@ -68,8 +71,13 @@ class ep_shape_t(ctypes.Structure):
 
 
 def _load() -> ctypes.CDLL:
+    # torch ships its own HIP runtime (file libamdhip64.so, soname
+    # libamdhip64.so.7).  Loading torch first lets libep.so's dependency on
+    # libamdhip64.so.7 resolve to that same runtime; the other order puts two
+    # HIP runtimes in the process and the second one finds no device.
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m combine_topk_rank_amd.build` "
+        raise ImportError(f"{LIB_PATH} is not built; run `python combine_topk_rank_amd/build.py` "
                           "(there is no CPU fallback)")
     L = ctypes.CDLL(LIB_PATH)
     P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
@@ -100,6 +108,8 @@ def _load() -> ctypes.CDLL:
     L.ep_ring_proxy_drained.restype = i64
     L.ep_status_str.argtypes = [ctypes.c_int]
     L.ep_status_str.restype = ctypes.c_char_p
+    L.ep_last_error.argtypes = []
+    L.ep_last_error.restype = ctypes.c_char_p
     return L
 
 

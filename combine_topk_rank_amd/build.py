@@ -1,6 +1,6 @@
 """Build libep.so (the HIP library behind include/ep.h) for gfx950, in-tree.
 
-    python -m combine_topk_rank_amd.build
+    python combine_topk_rank_amd/build.py
 
 Each source is compiled to an object under ``_build/`` in parallel, then
 linked.  Flags: -O3, no fast-math (the fp8 scale divisions stay IEEE), and

@@ -1,9 +1,19 @@
 // ep_api.hip — host-side helpers of the C ABI: shape validation, row sizes,
 // workspace layout and status strings.
 
+#include <stdio.h>
+
 #include "ep_common.h"
 
 namespace ep {
+
+namespace {
+thread_local char g_last_error[256] = "";
+}
+
+void record_hip_error(hipError_t e, const char* what) {
+    snprintf(g_last_error, sizeof g_last_error, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
 
 size_t row_bytes(int32_t H, int32_t fmt) {
     if (fmt == EP_FMT_BF16) return (size_t)2 * H;
@@ -72,6 +82,8 @@ extern "C" size_t ep_workspace_bytes(const ep_shape_t* shape) {
     if (validate_shape(shape) != EP_OK) return 0;
     return workspace_bytes(*shape);
 }
+
+extern "C" const char* ep_last_error(void) { return g_last_error; }
 
 extern "C" const char* ep_status_str(int st) {
     switch (st) {

@@ -128,8 +128,10 @@ namespace {
 template <int VPL>
 int launch_combine(const CombineArgs& a, int64_t waves, hipStream_t stream) {
     const int64_t blocks = ceil_div(waves, kBlock / kWave);
+    clear_hip_error();
     hipLaunchKernelGGL(combine_kernel<VPL>, dim3((unsigned)blocks), dim3(kBlock), 0, stream, a);
-    return hipGetLastError() == hipSuccess ? EP_OK : EP_ERR_HIP;
+    EP_HIP_CHECK(hipGetLastError());
+    return EP_OK;
 }
 }  // namespace
 

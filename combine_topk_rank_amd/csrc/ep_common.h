@@ -60,11 +60,21 @@ Workspace carve_workspace(const ep_shape_t& s, void* base);
 int validate_shape(const ep_shape_t* s);
 size_t row_bytes(int32_t H, int32_t fmt);
 
-#define EP_HIP_CHECK(expr)                          \
-    do {                                            \
-        hipError_t e_ = (expr);                     \
-        if (e_ != hipSuccess) return EP_ERR_HIP;    \
+// Remember the last failing HIP call of this thread (ep_last_error).
+void record_hip_error(hipError_t e, const char* what);
+
+#define EP_HIP_CHECK(expr)                                  \
+    do {                                                    \
+        hipError_t e_ = (expr);                             \
+        if (e_ != hipSuccess) {                             \
+            ::ep::record_hip_error(e_, #expr);              \
+            return EP_ERR_HIP;                              \
+        }                                                   \
     } while (0)
+
+// Launch errors surface through hipGetLastError, which also returns errors
+// left by unrelated earlier calls of the thread: clear it before a launch.
+inline void clear_hip_error() { (void)hipGetLastError(); }
 
 // First error wins.
 __device__ inline void set_error(int32_t* st, int code) {

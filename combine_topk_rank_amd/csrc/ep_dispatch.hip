@@ -57,33 +57,6 @@ struct PackArgs {
 };
 
 // ------------------------------------------------------------------ ring
-__device__ inline unsigned long long realtime() { return __builtin_amdgcn_s_memrealtime(); }
-
-// Wait until `ticket` may be written on channel c: fewer than max_inflight
-// commands of the channel may be published but not yet drained.  Returns
-// false on timeout (status set) or when another producer already failed.
-__device__ bool ring_wait(const RingDev& g, int c, unsigned long long ticket, int32_t* st) {
-    unsigned long long* cache = g.tail_cache + (size_t)c * kPad;
-    const unsigned long long* htail = g.host_tail + (size_t)c * kPad;
-    const unsigned long long lim = (unsigned long long)g.max_inflight;
-    unsigned long long seen = __hip_atomic_load(cache, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (ticket < seen + lim) return true;
-    const unsigned long long t0 = realtime();
-    for (;;) {
-        unsigned long long h = __hip_atomic_load(htail, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-        if (h > seen) {
-            atomicMax(cache, h);
-            seen = h;
-        }
-        if (ticket < seen + lim) return true;
-        if (read_status(st) != 0) return false;
-        if (realtime() - t0 > g.timeout_ticks) {
-            set_error(st, EP_ERR_RING_TIMEOUT);
-            return false;
-        }
-        __builtin_amdgcn_s_sleep(16);
-    }
-}
 
 // Write one command into its slot: payload first, then seq with a
 // system-scope release, so a consumer that sees seq sees the payload.
@@ -111,58 +84,130 @@ __device__ inline unsigned long long ring_reserve(const RingDev& g, int c, unsig
     return atomicAdd(g.head + (size_t)c * kPad, (unsigned long long)n);
 }
 
-// ATOMIC{ADD, cnt} for ranks that receive no rows (nothing to order after).
-__device__ void publish_empty_ranks(const PackArgs& a) {
-    const int lane = lane_id();
-    if (lane < a.R) {
-        int32_t cnt = a.rank_off[lane + 1] - a.rank_off[lane];
-        if (cnt == 0) {
-            const int c = lane % a.ring.channels;
-            unsigned long long tk = ring_reserve(a.ring, c, 1);
-            if (ring_wait(a.ring, c, tk, a.st))
-                ring_write(a.ring, c, tk, EP_CMD_ATOMIC, EP_ATOMIC_ADD, 0, (uint32_t)lane, 0, 0, 0);
+// One command per lane (lanes with `have`): wait until the lane's ticket may
+// be written -- fewer than max_inflight commands of its channel published but
+// not yet drained -- and write it.  The wait and the write share one
+// wave-uniform loop, so a lane whose ticket is ready writes at once even while
+// other lanes of the wavefront still wait (their tickets may wait on it).
+// A lane gives up when the ring's timeout passes (status set) or when another
+// producer has already failed.
+__device__ void ring_publish(const RingDev& g, bool have, int c, unsigned long long ticket,
+                             uint32_t type, uint32_t op, uint32_t ntok, uint32_t dst_rank,
+                             uint32_t size_val, uint64_t src_off, uint64_t dst_off, int32_t* st) {
+    if (!__ballot(have)) return;
+    const unsigned long long lim = (unsigned long long)g.max_inflight;
+    unsigned long long* cache = g.tail_cache + (size_t)c * kPad;
+    const unsigned long long* htail = g.host_tail + (size_t)c * kPad;
+    unsigned long long seen = 0, t0 = 0;
+    bool pending = have;
+    bool polled = false;
+    if (pending) seen = __hip_atomic_load(cache, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    while (__ballot(pending)) {
+        bool progress = false;
+        if (pending) {
+            if (ticket >= seen + lim) {
+                // cached consumer position says full: read the real one (PCIe)
+                unsigned long long h =
+                    __hip_atomic_load(htail, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                if (h > seen) {
+                    atomicMax(cache, h);
+                    seen = h;
+                }
+            }
+            if (ticket < seen + lim) {
+                ring_write(g, c, ticket, type, op, ntok, dst_rank, size_val, src_off, dst_off);
+                pending = false;
+                progress = true;
+            } else if (read_status(st) != 0) {
+                pending = false;
+            } else {
+                const unsigned long long now = __builtin_amdgcn_s_memrealtime();
+                if (!polled) {
+                    polled = true;
+                    t0 = now;
+                } else if (now - t0 > g.timeout_ticks) {
+                    set_error(st, EP_ERR_RING_TIMEOUT);
+                    pending = false;
+                }
+            }
         }
+        if (!__ballot(progress) && __ballot(pending)) __builtin_amdgcn_s_sleep(16);
     }
 }
 
-// Called by lane r of a wavefront that wrote (one chunk of) the row in slot s
-// of rank r, after its release fence.  The last arrival of a message publishes
-// the WRITE, and the last WRITE of a rank is followed by its ATOMIC.
-__device__ void arrive_and_publish(const PackArgs& a, int r, int32_t s) {
-    const int32_t o = a.rank_off[r];
-    const int32_t cnt = a.rank_off[r + 1] - o;
-    const int32_t m = (s - o) / kMsgRows;
-    const int32_t nrows = min(kMsgRows, cnt - m * kMsgRows);
-    const int32_t gm = a.msg_base[r] + m;
-    if (s < o || s >= o + cnt || gm < 0 || gm >= a.max_msgs) {
-        // send_slot does not belong to rank_offset: not from the same layout
-        set_error(a.st, EP_ERR_INVALID_ARG);
-        return;
+// ATOMIC{ADD, cnt} for ranks that receive no rows (nothing to order after).
+__device__ void publish_empty_ranks(const PackArgs& a) {
+    const int lane = lane_id();
+    bool have = false;
+    int c = 0;
+    unsigned long long tk = 0;
+    if (lane < a.R && a.rank_off[lane + 1] == a.rank_off[lane]) {
+        have = true;
+        c = lane % a.ring.channels;
+        tk = ring_reserve(a.ring, c, 1);
     }
-    const int32_t need = nrows * a.nchunks;
-    int32_t old = atomicAdd(&a.msg_arrivals[gm], 1);
-    if (old != need - 1) return;
-    a.msg_arrivals[gm] = 0;   // every arrival is in: leave the counter clean
+    ring_publish(a.ring, have, c, tk, EP_CMD_ATOMIC, EP_ATOMIC_ADD, 0, (uint32_t)lane, 0, 0, 0,
+                 a.st);
+}
+
+// Lane r of a wavefront that wrote (one chunk of) the row in slot s of rank r
+// (`mine`), after the wavefront's release fence: count the row into its
+// message; the last arrival of a message publishes the WRITE, and the last
+// WRITE of a rank is followed by the rank's ATOMIC.  All lanes of the
+// wavefront call this together.
+__device__ void arrive_and_publish(const PackArgs& a, bool mine, int r, int32_t s) {
+    bool pub = false;
+    int32_t o = 0, cnt = 0, m = 0, nrows = 0;
+    if (mine) {
+        o = a.rank_off[r];
+        cnt = a.rank_off[r + 1] - o;
+        m = (s - o) / kMsgRows;
+        nrows = min(kMsgRows, cnt - m * kMsgRows);
+        const int32_t gm = a.msg_base[r] + m;
+        if (s < o || s >= o + cnt || gm < 0 || gm >= a.max_msgs) {
+            // send_slot does not belong to rank_offset: not from the same layout
+            set_error(a.st, EP_ERR_INVALID_ARG);
+        } else {
+            const int32_t old = atomicAdd(&a.msg_arrivals[gm], 1);
+            if (old == nrows * a.nchunks - 1) {
+                pub = true;
+                a.msg_arrivals[gm] = 0;   // every arrival is in: leave the counter clean
+            }
+        }
+    }
+    if (!__ballot(pub)) return;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     const int c = r % a.ring.channels;
-    const int32_t st0 = read_status(a.st);
-    unsigned long long tk = ring_reserve(a.ring, c, 1);
-    if (st0 == 0 && ring_wait(a.ring, c, tk, a.st)) {
-        const uint64_t rb = (uint64_t)a.row_bytes;
-        ring_write(a.ring, c, tk, EP_CMD_WRITE, 0, (uint32_t)nrows, (uint32_t)r,
-                   (uint32_t)(nrows * rb), (uint64_t)(o + m * kMsgRows) * rb,
-                   (uint64_t)(m * kMsgRows) * rb);
+    unsigned long long tk = 0;
+    bool ok = false;
+    if (pub) {
+        ok = read_status(a.st) == 0;
+        tk = ring_reserve(a.ring, c, 1);
     }
-    // count this message into its rank only after its WRITE ticket exists: the
+    const uint64_t rb = (uint64_t)a.row_bytes;
+    ring_publish(a.ring, pub && ok, c, tk, EP_CMD_WRITE, 0, (uint32_t)nrows, (uint32_t)r,
+                 (uint32_t)(nrows * rb), (uint64_t)(o + m * kMsgRows) * rb,
+                 (uint64_t)(m * kMsgRows) * rb, a.st);
+    // count the message into its rank only after its WRITE ticket exists: the
     // added value depends on the ticket, so the two atomics cannot reorder
-    const int32_t nmsgs = (cnt + kMsgRows - 1) / kMsgRows;
-    int32_t one = 1 + (int32_t)(tk >> 62);
-    int32_t done = atomicAdd(&a.rank_msgs_done[r], one);
-    if (done != nmsgs - 1) return;
-    a.rank_msgs_done[r] = 0;
-    unsigned long long tka = ring_reserve(a.ring, c, 1);
-    if (read_status(a.st) == 0 && ring_wait(a.ring, c, tka, a.st))
-        ring_write(a.ring, c, tka, EP_CMD_ATOMIC, EP_ATOMIC_ADD, 0, (uint32_t)r, (uint32_t)cnt, 0, 0);
+    bool pub_a = false;
+    if (pub) {
+        const int32_t nmsgs = (cnt + kMsgRows - 1) / kMsgRows;
+        const int32_t one = 1 + (int32_t)(tk >> 62);
+        const int32_t done = atomicAdd(&a.rank_msgs_done[r], one);
+        if (done == nmsgs - 1) {
+            pub_a = true;
+            a.rank_msgs_done[r] = 0;
+        }
+    }
+    unsigned long long tka = 0;
+    bool ok_a = false;
+    if (pub_a) {
+        ok_a = read_status(a.st) == 0;
+        tka = ring_reserve(a.ring, c, 1);
+    }
+    ring_publish(a.ring, pub_a && ok_a, c, tka, EP_CMD_ATOMIC, EP_ATOMIC_ADD, 0, (uint32_t)r,
+                 (uint32_t)cnt, 0, 0, a.st);
 }
 
 // ------------------------------------------------------------------ fp8
@@ -293,7 +338,7 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(PackArgs a) {
     if (a.has_ring && cap_ok) {
         // rows (and metadata) visible to the system before any descriptor
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");
-        if ((dmask >> lane) & 1ull) arrive_and_publish(a, lane, s_lane);
+        arrive_and_publish(a, ((dmask >> lane) & 1ull) != 0, lane, s_lane);
     }
 }
 
@@ -306,13 +351,15 @@ namespace {
 template <int VPL>
 int launch_pack(const PackArgs& a, int fmt, int64_t waves, hipStream_t stream) {
     const int64_t blocks = ceil_div(waves, kBlock / kWave);
+    clear_hip_error();
     if (fmt == EP_FMT_BF16)
         hipLaunchKernelGGL((pack_kernel<VPL, EP_FMT_BF16>), dim3((unsigned)blocks), dim3(kBlock), 0,
                            stream, a);
     else
         hipLaunchKernelGGL((pack_kernel<VPL, EP_FMT_FP8_E4M3_B128>), dim3((unsigned)blocks),
                            dim3(kBlock), 0, stream, a);
-    return hipGetLastError() == hipSuccess ? EP_OK : EP_ERR_HIP;
+    EP_HIP_CHECK(hipGetLastError());
+    return EP_OK;
 }
 
 }  // namespace

@@ -241,6 +241,7 @@ extern "C" int ep_dispatch_layout(const ep_shape_t* shape, const int32_t* topk_i
     const int epr = s.E / s.R;
     const int nb = w.layout_blocks;
     int32_t* counters = w.msg_arrivals;
+    clear_hip_error();
     if (nb == 1) {
         hipLaunchKernelGGL(layout_main_kernel<true>, dim3(1), dim3(kBlock), 0, stream, topk_idx,
                            s.T, s.E, s.R, s.k, epr, 1, (const int32_t*)nullptr,

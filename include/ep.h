@@ -224,6 +224,10 @@ int64_t ep_ring_proxy_drained(const ep_ring_t* ring);
 /* Text of a status code. */
 const char* ep_status_str(int status);
 
+/* Description of the last HIP runtime failure seen by this library on the
+ * calling thread (the call that returned EP_ERR_HIP), or "" if none. */
+const char* ep_last_error(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -19,12 +19,33 @@ constexpr int kMaxE = 4096;        // per-expert LDS histogram bound
 constexpr int kMaxK = 32;          // experts of a token sit in lanes 0..k-1
 constexpr int kPad = 8;            // 64-byte stride between per-channel counters
 
+// One FIFO slot as it sits in the ring: four 64-bit words, each
+//   bits  0..15  tag = low 16 bits of (ticket + 1)
+//   bits 16..63  48 bits of the command:
+//     w0: type (8) | op (8) | num_tokens (16) | 0 (16)
+//     w1: dst_rank (16) | size_or_value (32)
+//     w2: src_offset (48)
+//     w3: dst_offset (48)
+// The GPU writes the words with two plain 16-byte stores followed by a
+// system-scope release, in any order and with no flag write; a consumer that reads the four words (8-byte
+// loads are single-copy atomic) and finds the expected tag in all of them has
+// the whole command.  A stale slot holds the tag of ticket - depth + 1, which
+// differs as long as depth < 65536.  The consumer decodes slots into
+// ep_transfer_cmd_t.
+struct RingSlot {
+    uint64_t w[4];
+};
+static_assert(sizeof(RingSlot) == 32, "ring slot is 32 bytes");
+constexpr uint64_t kMaxRingOffset = (1ull << 48) - 1;
+constexpr int32_t kMaxRingDepth = 65535;
+
 // Device view of a TransferCmd ring.
 struct RingDev {
-    ep_transfer_cmd_t* slots;              // host-pinned, [channels][depth]
+    RingSlot* slots;                       // host-pinned, [channels][depth]
     const unsigned long long* host_tail;   // host-pinned, consumer position, stride kPad
     unsigned long long* head;              // device, ticket counter, stride kPad
     unsigned long long* tail_cache;        // device, last consumer position seen, stride kPad
+    unsigned long long* poll;              // device, 1 while a lane reads host_tail, stride kPad
     int32_t depth;
     int32_t channels;
     int32_t max_inflight;

@@ -31,6 +31,8 @@ RingDev ring_device_view(ep_ring_t* r);
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
+
 
 struct PackArgs {
     const u32x4* x;               // [T, H/8] 16-byte vectors
@@ -58,25 +60,24 @@ struct PackArgs {
 
 // ------------------------------------------------------------------ ring
 
-// Write one command into its slot: payload first, then seq with a
-// system-scope release, so a consumer that sees seq sees the payload.
+// Write one command into its slot: four tagged 8-byte words in two plain
+// 16-byte stores.  The caller makes them visible to the CPU with one
+// system-scope release per round of writes (see ring_publish); the tags make
+// the order in which the words land irrelevant.  The rows the command points
+// to were released at system scope before the command's ticket was taken.
 __device__ inline void ring_write(const RingDev& g, int c, unsigned long long ticket, uint32_t type,
                                   uint32_t op, uint32_t ntok, uint32_t dst_rank, uint32_t size_val,
                                   uint64_t src_off, uint64_t dst_off) {
-    ep_transfer_cmd_t* slot =
-        g.slots + (size_t)c * g.depth + (size_t)(ticket % (unsigned long long)g.depth);
-    uint32_t* wds = reinterpret_cast<uint32_t*>(slot);
-    wds[1] = type | (op << 8) | (ntok << 16);
-    wds[2] = dst_rank;
-    wds[3] = size_val;
-    u32x4 tail;
-    tail.x = (uint32_t)src_off;
-    tail.y = (uint32_t)(src_off >> 32);
-    tail.z = (uint32_t)dst_off;
-    tail.w = (uint32_t)(dst_off >> 32);
-    *reinterpret_cast<u32x4*>(wds + 4) = tail;
-    __hip_atomic_store(&slot->seq, (uint32_t)(ticket + 1), __ATOMIC_RELEASE,
-                       __HIP_MEMORY_SCOPE_SYSTEM);
+    RingSlot* slot = g.slots + (size_t)c * g.depth + (size_t)(ticket % (unsigned long long)g.depth);
+    const uint64_t tag = (uint64_t)((ticket + 1) & 0xFFFFull);
+    const uint64_t w0 = tag | ((uint64_t)(type & 0xFF) << 16) | ((uint64_t)(op & 0xFF) << 24) |
+                        ((uint64_t)(ntok & 0xFFFF) << 32);
+    const uint64_t w1 = tag | ((uint64_t)(dst_rank & 0xFFFF) << 16) | ((uint64_t)size_val << 32);
+    const uint64_t w2 = tag | ((src_off & kMaxRingOffset) << 16);
+    const uint64_t w3 = tag | ((dst_off & kMaxRingOffset) << 16);
+    u64x2* p = reinterpret_cast<u64x2*>(slot);
+    p[0] = u64x2{w0, w1};
+    p[1] = u64x2{w2, w3};
 }
 
 // Reserve n consecutive tickets on channel c (one atomic per reservation).
@@ -86,7 +87,7 @@ __device__ inline unsigned long long ring_reserve(const RingDev& g, int c, unsig
 
 // One command per lane (lanes with `have`): wait until the lane's ticket may
 // be written -- fewer than max_inflight commands of its channel published but
-// not yet drained -- and write it.  The wait and the write share one
+// not yet drained -- write it, and release it at system scope.  The wait and the write share one
 // wave-uniform loop, so a lane whose ticket is ready writes at once even while
 // other lanes of the wavefront still wait (their tickets may wait on it).
 // A lane gives up when the ring's timeout passes (status set) or when another
@@ -97,6 +98,7 @@ __device__ void ring_publish(const RingDev& g, bool have, int c, unsigned long l
     if (!__ballot(have)) return;
     const unsigned long long lim = (unsigned long long)g.max_inflight;
     unsigned long long* cache = g.tail_cache + (size_t)c * kPad;
+    unsigned long long* poll = g.poll + (size_t)c * kPad;
     const unsigned long long* htail = g.host_tail + (size_t)c * kPad;
     unsigned long long seen = 0, t0 = 0;
     bool pending = have;
@@ -106,13 +108,18 @@ __device__ void ring_publish(const RingDev& g, bool have, int c, unsigned long l
         bool progress = false;
         if (pending) {
             if (ticket >= seen + lim) {
-                // cached consumer position says full: read the real one (PCIe)
-                unsigned long long h =
-                    __hip_atomic_load(htail, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-                if (h > seen) {
+                // The cached consumer position says full.  One lane per
+                // channel at a time reads the real one over PCIe and
+                // refreshes the cache; the others read the cache.
+                if (atomicCAS(poll, 0ull, 1ull) == 0ull) {
+                    unsigned long long h =
+                        __hip_atomic_load(htail, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
                     atomicMax(cache, h);
-                    seen = h;
+                    atomicExch(poll, 0ull);
                 }
+                unsigned long long cv =
+                    __hip_atomic_load(cache, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (cv > seen) seen = cv;
             }
             if (ticket < seen + lim) {
                 ring_write(g, c, ticket, type, op, ntok, dst_rank, size_val, src_off, dst_off);
@@ -131,7 +138,13 @@ __device__ void ring_publish(const RingDev& g, bool have, int c, unsigned long l
                 }
             }
         }
-        if (!__ballot(progress) && __ballot(pending)) __builtin_amdgcn_s_sleep(16);
+        if (__ballot(progress)) {
+            // one system-scope release pushes this round's slots out of the
+            // L2 to host memory, where the proxy polls them
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");
+        } else if (__ballot(pending)) {
+            __builtin_amdgcn_s_sleep(16);
+        }
     }
 }
 
@@ -233,10 +246,22 @@ __device__ inline float group16_max(float v) {
 }
 
 // ------------------------------------------------------------------ kernel
+// Wavefronts per pack workgroup: they share one system-scope release for
+// their rows and one wavefront publishes their descriptors.
+constexpr int kPackWaves = 16;
+// Vectors per lane for rows of up to 896 vectors (H = 7168): 14 = one
+// wavefront per row, 7 = two.
+constexpr int kPackVplH7168 = 14;
+
 template <int VPL, int FMT>
-__global__ __launch_bounds__(kBlock) void pack_kernel(PackArgs a) {
+__global__ __launch_bounds__(kPackWaves * kWave) void pack_kernel(PackArgs a) {
+    constexpr int kWaves = kPackWaves;
+    __shared__ int32_t s_pair_slot[kWaves][kMaxR];
+    __shared__ int32_t s_pair_rank[kWaves][kMaxR];
+    __shared__ int32_t s_npairs[kWaves];
     const int lane = lane_id();
-    const int64_t gw = (int64_t)blockIdx.x * (kBlock / kWave) + (threadIdx.x / kWave);
+    const int wave = (int)(threadIdx.x / kWave);
+    const int64_t gw = (int64_t)blockIdx.x * kWaves + wave;
     const int64_t P = a.rank_off[a.R];
     const bool cap_ok = P <= a.cap;
     if (gw == 0) {
@@ -245,100 +270,131 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(PackArgs a) {
     }
     const int64_t t = gw / a.nchunks;
     const int chunk = (int)(gw - t * a.nchunks);
-    if (t >= a.T) return;
+    const bool active = t < a.T;   // wavefront-uniform
 
     int32_t s_lane = -1;
-    if (lane < a.R) s_lane = a.send_slot[t * a.R + lane];
-    const uint64_t dmask = __ballot(s_lane >= 0);
+    uint64_t dmask = 0;
+    if (active) {
+        if (lane < a.R) s_lane = a.send_slot[t * a.R + lane];
+        dmask = __ballot(s_lane >= 0);
 
-    // load this wavefront's chunk of the row: vectors v0 + lane + 64 i
-    const int v0 = chunk * VPL * kWave;
-    const u32x4* xr = a.x + t * a.nv;
-    u32x4 v[VPL];
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-        int vi = v0 + lane + i * kWave;
-        if (vi < a.nv) v[i] = xr[vi];
-        else v[i] = u32x4{0, 0, 0, 0};
-    }
-
-    if (FMT == EP_FMT_BF16) {
-        for (uint64_t m = dmask; m; m &= m - 1) {
-            const int r = __builtin_ctzll(m);
-            const int32_t s = bcast(s_lane, r);
-            if (s >= a.cap) continue;
-            u32x4* dst = reinterpret_cast<u32x4*>(a.send_buf + (int64_t)s * a.row_bytes);
-#pragma unroll
-            for (int i = 0; i < VPL; ++i) {
-                int vi = v0 + lane + i * kWave;
-                if (vi < a.nv) __builtin_nontemporal_store(v[i], dst + vi);
-            }
-        }
-    } else {
-        // quantise once: per 128-element block, a = max(amax, 1e-4),
-        // codes = e4m3(x * (448 / a)), scale = a / 448
-        u32x2 q[VPL];
-        float scale[VPL];
+        // load this wavefront's chunk of the row: vectors v0 + lane + 64 i
+        const int v0 = chunk * VPL * kWave;
+        const u32x4* xr = a.x + t * a.nv;
+        u32x4 v[VPL];
 #pragma unroll
         for (int i = 0; i < VPL; ++i) {
-            const u32x4 u = v[i];
-            float f0 = bf16lo(u.x), f1 = bf16hi(u.x), f2 = bf16lo(u.y), f3 = bf16hi(u.y);
-            float f4 = bf16lo(u.z), f5 = bf16hi(u.z), f6 = bf16lo(u.w), f7 = bf16hi(u.w);
-            float am = fmaxf(fmaxf(fmaxf(fabsf(f0), fabsf(f1)), fmaxf(fabsf(f2), fabsf(f3))),
-                             fmaxf(fmaxf(fabsf(f4), fabsf(f5)), fmaxf(fabsf(f6), fabsf(f7))));
-            am = group16_max(am);
-            const float av = fmaxf(am, 1e-4f);
-            const float inv = 448.0f / av;
-            scale[i] = av / 448.0f;
-            uint32_t lo = e4m3x2<false>(f0 * inv, f1 * inv, 0);
-            lo = e4m3x2<true>(f2 * inv, f3 * inv, lo);
-            uint32_t hi = e4m3x2<false>(f4 * inv, f5 * inv, 0);
-            hi = e4m3x2<true>(f6 * inv, f7 * inv, hi);
-            q[i] = u32x2{lo, hi};
+            int vi = v0 + lane + i * kWave;
+            if (vi < a.nv) v[i] = xr[vi];
+            else v[i] = u32x4{0, 0, 0, 0};
         }
-        for (uint64_t m = dmask; m; m &= m - 1) {
-            const int r = __builtin_ctzll(m);
-            const int32_t s = bcast(s_lane, r);
-            if (s >= a.cap) continue;
-            uint8_t* row = a.send_buf + (int64_t)s * a.row_bytes;
-            u32x2* codes = reinterpret_cast<u32x2*>(row);
-            float* scales = reinterpret_cast<float*>(row + a.H);
+
+        if (FMT == EP_FMT_BF16) {
+            for (uint64_t m = dmask; m; m &= m - 1) {
+                const int r = __builtin_ctzll(m);
+                const int32_t s = bcast(s_lane, r);
+                if (s >= a.cap) continue;
+                u32x4* dst = reinterpret_cast<u32x4*>(a.send_buf + (int64_t)s * a.row_bytes);
+#pragma unroll
+                for (int i = 0; i < VPL; ++i) {
+                    int vi = v0 + lane + i * kWave;
+                    if (vi < a.nv) __builtin_nontemporal_store(v[i], dst + vi);
+                }
+            }
+        } else {
+            // quantise once: per 128-element block, a = max(amax, 1e-4),
+            // codes = e4m3(x * (448 / a)), scale = a / 448
+            u32x2 q[VPL];
+            float scale[VPL];
 #pragma unroll
             for (int i = 0; i < VPL; ++i) {
-                int vi = v0 + lane + i * kWave;
-                if (vi < a.nv) {
-                    __builtin_nontemporal_store(q[i], codes + vi);
-                    if ((lane & 15) == 0) __builtin_nontemporal_store(scale[i], scales + vi / 16);
+                const u32x4 u = v[i];
+                float f0 = bf16lo(u.x), f1 = bf16hi(u.x), f2 = bf16lo(u.y), f3 = bf16hi(u.y);
+                float f4 = bf16lo(u.z), f5 = bf16hi(u.z), f6 = bf16lo(u.w), f7 = bf16hi(u.w);
+                float am = fmaxf(fmaxf(fmaxf(fabsf(f0), fabsf(f1)), fmaxf(fabsf(f2), fabsf(f3))),
+                                 fmaxf(fmaxf(fabsf(f4), fabsf(f5)), fmaxf(fabsf(f6), fabsf(f7))));
+                am = group16_max(am);
+                const float av = fmaxf(am, 1e-4f);
+                const float inv = 448.0f / av;
+                scale[i] = av / 448.0f;
+                uint32_t lo = e4m3x2<false>(f0 * inv, f1 * inv, 0);
+                lo = e4m3x2<true>(f2 * inv, f3 * inv, lo);
+                uint32_t hi = e4m3x2<false>(f4 * inv, f5 * inv, 0);
+                hi = e4m3x2<true>(f6 * inv, f7 * inv, hi);
+                q[i] = u32x2{lo, hi};
+            }
+            for (uint64_t m = dmask; m; m &= m - 1) {
+                const int r = __builtin_ctzll(m);
+                const int32_t s = bcast(s_lane, r);
+                if (s >= a.cap) continue;
+                uint8_t* row = a.send_buf + (int64_t)s * a.row_bytes;
+                u32x2* codes = reinterpret_cast<u32x2*>(row);
+                float* scales = reinterpret_cast<float*>(row + a.H);
+#pragma unroll
+                for (int i = 0; i < VPL; ++i) {
+                    int vi = v0 + lane + i * kWave;
+                    if (vi < a.nv) {
+                        __builtin_nontemporal_store(q[i], codes + vi);
+                        if ((lane & 15) == 0) __builtin_nontemporal_store(scale[i], scales + vi / 16);
+                    }
                 }
             }
         }
-    }
 
-    // per-slot metadata, written by the token's first chunk
-    if (chunk == 0) {
-        int e = -1;
-        float wt = 0.0f;
-        if (lane < a.k) {
-            e = a.idx[t * a.k + lane];
-            wt = a.w[t * a.k + lane];
-        }
-        for (uint64_t m = dmask; m; m &= m - 1) {
-            const int r = __builtin_ctzll(m);
-            const int32_t s = bcast(s_lane, r);
-            if (s >= a.cap) continue;
+        // per-slot metadata, written by the token's first chunk
+        if (chunk == 0) {
+            int e = -1;
+            float wt = 0.0f;
             if (lane < a.k) {
-                const bool local = e >= 0 && e < a.E && e / a.epr == r;
-                a.slot_local_idx[(int64_t)s * a.k + lane] = local ? e - r * a.epr : -1;
-                a.slot_local_w[(int64_t)s * a.k + lane] = local ? wt : 0.0f;
+                e = a.idx[t * a.k + lane];
+                wt = a.w[t * a.k + lane];
             }
-            if (lane == 0) a.slot_src[s] = (int32_t)t;
+            for (uint64_t m = dmask; m; m &= m - 1) {
+                const int r = __builtin_ctzll(m);
+                const int32_t s = bcast(s_lane, r);
+                if (s >= a.cap) continue;
+                if (lane < a.k) {
+                    const bool local = e >= 0 && e < a.E && e / a.epr == r;
+                    a.slot_local_idx[(int64_t)s * a.k + lane] = local ? e - r * a.epr : -1;
+                    a.slot_local_w[(int64_t)s * a.k + lane] = local ? wt : 0.0f;
+                }
+                if (lane == 0) a.slot_src[s] = (int32_t)t;
+            }
         }
     }
 
-    if (a.has_ring && cap_ok) {
-        // rows (and metadata) visible to the system before any descriptor
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");
-        arrive_and_publish(a, ((dmask >> lane) & 1ull) != 0, lane, s_lane);
+    if (!(a.has_ring && cap_ok)) return;   // uniform over the workgroup
+    // hand this wavefront's (slot, rank) pairs to wavefront 0
+    if ((dmask >> lane) & 1ull) {
+        const int j = lane_prefix(dmask);
+        s_pair_slot[wave][j] = s_lane;
+        s_pair_rank[wave][j] = lane;
+    }
+    if (lane == 0) s_npairs[wave] = (int32_t)__popcll(dmask);
+    __syncthreads();
+    if (wave != 0) return;
+    // One system-scope release for the rows and metadata of the whole
+    // workgroup (ordered after the other wavefronts' stores by the barrier),
+    // then the arrivals and the descriptors.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");
+    int total = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) total += s_npairs[w];
+    for (int base = 0; base < total; base += kWave) {
+        int p = base + lane;
+        const bool mine = p < total;
+        int r = 0;
+        int32_t s = 0;
+        if (mine) {
+            int w = 0;
+            while (p >= s_npairs[w]) {
+                p -= s_npairs[w];
+                ++w;
+            }
+            s = s_pair_slot[w][p];
+            r = s_pair_rank[w][p];
+        }
+        arrive_and_publish(a, mine, r, s);
     }
 }
 
@@ -350,14 +406,14 @@ namespace {
 
 template <int VPL>
 int launch_pack(const PackArgs& a, int fmt, int64_t waves, hipStream_t stream) {
-    const int64_t blocks = ceil_div(waves, kBlock / kWave);
+    const int64_t blocks = ceil_div(waves, kPackWaves);
     clear_hip_error();
     if (fmt == EP_FMT_BF16)
-        hipLaunchKernelGGL((pack_kernel<VPL, EP_FMT_BF16>), dim3((unsigned)blocks), dim3(kBlock), 0,
-                           stream, a);
+        hipLaunchKernelGGL((pack_kernel<VPL, EP_FMT_BF16>), dim3((unsigned)blocks),
+                           dim3(kPackWaves * kWave), 0, stream, a);
     else
         hipLaunchKernelGGL((pack_kernel<VPL, EP_FMT_FP8_E4M3_B128>), dim3((unsigned)blocks),
-                           dim3(kBlock), 0, stream, a);
+                           dim3(kPackWaves * kWave), 0, stream, a);
     EP_HIP_CHECK(hipGetLastError());
     return EP_OK;
 }
@@ -379,6 +435,8 @@ extern "C" int ep_dispatch(const ep_shape_t* shape, const void* x, const int32_t
         return EP_ERR_INVALID_ARG;
     if (((uintptr_t)x | (uintptr_t)send_buf) & 15) return EP_ERR_INVALID_ARG;
     if (ws_bytes < workspace_bytes(s)) return EP_ERR_INVALID_ARG;
+    if (ring && (uint64_t)capacity_rows * row_bytes(s.H, s.fmt) > kMaxRingOffset)
+        return EP_ERR_INVALID_ARG;   // descriptor offsets are 48-bit
     Workspace w = carve_workspace(s, workspace);
 
     PackArgs a{};
@@ -408,13 +466,15 @@ extern "C" int ep_dispatch(const ep_shape_t* shape, const void* x, const int32_t
     a.epr = s.E / s.R;
     a.nv = s.H / 8;
 
-    // vectors per lane: one pass over the row when it fits 16 per lane
+    // vectors per lane: one pass over the row when it fits (bf16: 16 per
+    // lane); fp8 also holds the codes and scales, so it takes at most 8
     int vpl;
     if (a.nv <= 64) vpl = 1;
     else if (a.nv <= 128) vpl = 2;
     else if (a.nv <= 256) vpl = 4;
     else if (a.nv <= 512) vpl = 8;
-    else if (a.nv <= 896) vpl = 14;
+    else if (s.fmt != EP_FMT_BF16) vpl = a.nv <= 896 ? 7 : 8;
+    else if (a.nv <= 896) vpl = kPackVplH7168;
     else vpl = 16;
     a.nchunks = (int32_t)ceil_div(a.nv, (int64_t)vpl * kWave);
     int64_t waves = (int64_t)s.T * a.nchunks;
@@ -427,6 +487,7 @@ extern "C" int ep_dispatch(const ep_shape_t* shape, const void* x, const int32_t
         case 2: return launch_pack<2>(a, s.fmt, waves, stream);
         case 4: return launch_pack<4>(a, s.fmt, waves, stream);
         case 8: return launch_pack<8>(a, s.fmt, waves, stream);
+        case 7: return launch_pack<7>(a, s.fmt, waves, stream);
         case 14: return launch_pack<14>(a, s.fmt, waves, stream);
         default: return launch_pack<16>(a, s.fmt, waves, stream);
     }

@@ -51,32 +51,71 @@ __device__ inline void wave_rank_counts(uint64_t mask, int R, int32_t* wcnt) {
 }
 
 // Exclusive scan of n (<= kMaxE) ints held in LDS `v`, written to `out`
-// (n+1 entries, out[n] = total).  All kBlock threads take part.
+// (n+1 entries, out[n] = total).  All kBlock threads take part: each thread
+// sums a contiguous run of `per` values, the 256 run sums are scanned with
+// wavefront shuffles and a 4-entry scan of the wavefront totals.
 __device__ inline void block_exclusive_scan_store(const int32_t* v, int n, int32_t* out,
-                                                  int32_t* s_part) {
+                                                  int32_t* s_wtot) {
     const int tid = threadIdx.x;
+    const int lane = lane_id();
+    const int wave = tid / kWave;
     const int per = (n + kBlock - 1) / kBlock;
     const int b0 = tid * per;
     int32_t sum = 0;
     for (int i = 0; i < per; ++i)
         if (b0 + i < n) sum += v[b0 + i];
-    s_part[tid] = sum;
-    __syncthreads();
-    if (tid == 0) {
-        int32_t run = 0;
-        for (int i = 0; i < kBlock; ++i) {
-            int32_t x = s_part[i];
-            s_part[i] = run;
-            run += x;
-        }
-        out[n] = run;
+    int32_t incl = sum;
+    for (int d = 1; d < kWave; d <<= 1) {
+        int32_t o = __shfl_up(incl, d);
+        if (lane >= d) incl += o;
     }
+    if (lane == kWave - 1) s_wtot[wave] = incl;
     __syncthreads();
-    int32_t run = s_part[tid];
+    int32_t run = incl - sum;
+    for (int w = 0; w < wave; ++w) run += s_wtot[w];
+    if (tid == kBlock - 1) out[n] = run + sum;
     for (int i = 0; i < per; ++i) {
         if (b0 + i < n) {
             out[b0 + i] = run;
             run += v[b0 + i];
+        }
+    }
+}
+
+// Sum the [nrows, ncols] int32 matrix m over its rows into LDS acc[ncols]
+// (zeroed by the caller); rows < split also go to acc_pre (may be null).
+// Flat and fully parallel: 16-byte loads when ncols % 4 == 0, LDS atomics.
+__device__ inline void column_sums(const int32_t* __restrict__ m, int nrows, int ncols, int split,
+                                   int32_t* acc, int32_t* acc_pre) {
+    const int64_t n = (int64_t)nrows * ncols;
+    if ((ncols & 3) == 0) {
+        const int4* m4 = reinterpret_cast<const int4*>(m);
+        const int64_t n4 = n >> 2;
+#pragma unroll 4
+        for (int64_t i = threadIdx.x; i < n4; i += kBlock) {
+            const int4 q = m4[i];
+            const int64_t e0 = i * 4;
+            const int row = (int)(e0 / ncols);
+            const int col = (int)(e0 - (int64_t)row * ncols);
+            atomicAdd(&acc[col], q.x);
+            atomicAdd(&acc[col + 1], q.y);
+            atomicAdd(&acc[col + 2], q.z);
+            atomicAdd(&acc[col + 3], q.w);
+            if (acc_pre && row < split) {
+                atomicAdd(&acc_pre[col], q.x);
+                atomicAdd(&acc_pre[col + 1], q.y);
+                atomicAdd(&acc_pre[col + 2], q.z);
+                atomicAdd(&acc_pre[col + 3], q.w);
+            }
+        }
+    } else {
+#pragma unroll 4
+        for (int64_t i = threadIdx.x; i < n; i += kBlock) {
+            const int32_t q = m[i];
+            const int row = (int)(i / ncols);
+            const int col = (int)(i - (int64_t)row * ncols);
+            atomicAdd(&acc[col], q);
+            if (acc_pre && row < split) atomicAdd(&acc_pre[col], q);
         }
     }
 }
@@ -140,19 +179,23 @@ __global__ __launch_bounds__(kBlock) void layout_main_kernel(
     __syncthreads();
 
     // rank totals and the prefix over earlier tiles
-    if (tid < R) {
-        int32_t pre = 0, tot = 0;
-        if (SINGLE) {
+    if (SINGLE) {
+        if (tid < R) {
+            int32_t tot = 0;
             for (int w = 0; w < kBlock / kWave; ++w) tot += s_wcnt[w][tid];
-        } else {
-            for (int bb = 0; bb < nblocks; ++bb) {
-                int32_t c = blk_rank_cnt[(int64_t)bb * R + tid];
-                if (bb < b) pre += c;
-                tot += c;
-            }
+            s_pre[tid] = 0;
+            s_tot[tid] = tot;
         }
-        s_pre[tid] = pre;
-        s_tot[tid] = tot;
+    } else {
+        if (tid < R) {
+            s_pre[tid] = 0;
+            s_tot[tid] = 0;
+        }
+        if (b == 0)
+            for (int e = tid; e < E; e += kBlock) s_exp[e] = 0;
+        __syncthreads();
+        column_sums(blk_rank_cnt, nblocks, R, b, s_tot, s_pre);
+        if (b == 0) column_sums(blk_exp_cnt, nblocks, E, 0, s_exp, nullptr);
     }
     __syncthreads();
     if (wave == 0) {
@@ -185,14 +228,8 @@ __global__ __launch_bounds__(kBlock) void layout_main_kernel(
     if (b == 0) {
         // per-expert totals and their exclusive scan
         for (int e = tid; e < E; e += kBlock) {
-            int32_t c = 0;
-            if (SINGLE) {
-                c = s_hist[e];
-            } else {
-                for (int bb = 0; bb < nblocks; ++bb) c += blk_exp_cnt[(int64_t)bb * E + e];
-            }
-            s_exp[e] = c;
-            cnt_exp[e] = c;
+            if (SINGLE) s_exp[e] = s_hist[e];
+            cnt_exp[e] = s_exp[e];
         }
         __syncthreads();
         block_exclusive_scan_store(s_exp, E, exp_off, s_part);

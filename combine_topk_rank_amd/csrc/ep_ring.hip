@@ -34,9 +34,9 @@ struct ep_ring {
     int32_t depth = 0, channels = 0, max_inflight = 0;
     int64_t timeout_ns = 0;
     int device = 0;
-    ep_transfer_cmd_t* slots = nullptr;        // host-pinned
+    ep::RingSlot* slots = nullptr;             // host-pinned
     unsigned long long* host_tail = nullptr;   // host-pinned, stride kPad
-    unsigned long long* dev_state = nullptr;   // device: head[c*kPad], tail_cache[(C + c)*kPad]
+    unsigned long long* dev_state = nullptr;   // device: head, tail_cache, poll; each [C*kPad]
     unsigned long long timeout_ticks = 0;
     std::vector<unsigned long long> pos;       // consumer position per channel
     std::mutex mu;                             // serialises host-side calls
@@ -59,6 +59,7 @@ RingDev ring_device_view(ep_ring_t* r) {
     d.host_tail = r->host_tail;
     d.head = r->dev_state;
     d.tail_cache = r->dev_state + (size_t)r->channels * kPad;
+    d.poll = r->dev_state + 2 * (size_t)r->channels * kPad;
     d.depth = r->depth;
     d.channels = r->channels;
     d.max_inflight = r->max_inflight;
@@ -72,19 +73,36 @@ using namespace ep;
 
 namespace {
 
-inline uint32_t load_seq(const ep_transfer_cmd_t* s) {
-    return __atomic_load_n(&s->seq, __ATOMIC_ACQUIRE);
+// Read one slot (four 8-byte loads) and decode it when every word carries
+// the tag of ticket `want - 1`.
+inline bool read_slot(const RingSlot* s, uint32_t want, ep_transfer_cmd_t* out) {
+    const uint64_t tag = want & 0xFFFFu;
+    uint64_t w[4];
+    for (int i = 0; i < 4; ++i) {
+        w[i] = __atomic_load_n(&s->w[i], __ATOMIC_ACQUIRE);
+        if ((w[i] & 0xFFFFu) != tag) return false;
+    }
+    if (out) {
+        out->seq = want;
+        out->type = (uint8_t)(w[0] >> 16);
+        out->op = (uint8_t)(w[0] >> 24);
+        out->num_tokens = (uint16_t)(w[0] >> 32);
+        out->dst_rank = (uint32_t)((w[1] >> 16) & 0xFFFFu);
+        out->size_or_value = (uint32_t)(w[1] >> 32);
+        out->src_offset = w[2] >> 16;
+        out->dst_offset = w[3] >> 16;
+    }
+    return true;
 }
 
 // Pop up to `max` published commands of channel c; returns the number popped.
 int64_t pop_channel(ep_ring_t* r, int c, ep_transfer_cmd_t* out, int64_t max, bool publish) {
     unsigned long long p = r->pos[c];
-    ep_transfer_cmd_t* base = r->slots + (size_t)c * r->depth;
+    const RingSlot* base = r->slots + (size_t)c * r->depth;
     int64_t n = 0;
     while (n < max) {
-        const ep_transfer_cmd_t* s = base + (p % (unsigned long long)r->depth);
-        if (load_seq(s) != (uint32_t)(p + 1)) break;
-        if (out) std::memcpy(&out[n], s, sizeof(ep_transfer_cmd_t));
+        const RingSlot* s = base + (p % (unsigned long long)r->depth);
+        if (!read_slot(s, (uint32_t)(p + 1), out ? &out[n] : nullptr)) break;
         ++p;
         ++n;
     }
@@ -129,8 +147,8 @@ void proxy_loop(ep_ring_t* r, int first, int stride) {
 
 extern "C" ep_ring_t* ep_ring_create(int32_t depth, int32_t channels, int32_t max_inflight,
                                      int64_t timeout_ns) {
-    if (depth < 1 || channels < 1 || channels > kMaxR || max_inflight < 1 ||
-        max_inflight > depth || timeout_ns < 1)
+    if (depth < 1 || depth > kMaxRingDepth || channels < 1 || channels > kMaxR ||
+        max_inflight < 1 || max_inflight > depth || timeout_ns < 1)
         return nullptr;
     ep_ring_t* r = new (std::nothrow) ep_ring_t();
     if (!r) return nullptr;
@@ -148,17 +166,17 @@ extern "C" ep_ring_t* ep_ring_create(int32_t depth, int32_t channels, int32_t ma
         long double ticks = (long double)timeout_ns * rate_khz / 1.0e6L;
         r->timeout_ticks = ticks < 1 ? 1ull : (unsigned long long)ticks;
     }
-    const size_t slot_bytes = (size_t)channels * depth * sizeof(ep_transfer_cmd_t);
+    const size_t slot_bytes = (size_t)channels * depth * sizeof(RingSlot);
     const size_t tail_bytes = (size_t)channels * kPad * sizeof(unsigned long long);
     ok = ok && hipHostMalloc((void**)&r->slots, slot_bytes,
                              hipHostMallocCoherent | hipHostMallocMapped) == hipSuccess;
     ok = ok && hipHostMalloc((void**)&r->host_tail, tail_bytes,
                              hipHostMallocCoherent | hipHostMallocMapped) == hipSuccess;
-    ok = ok && hipMalloc((void**)&r->dev_state, 2 * tail_bytes) == hipSuccess;
+    ok = ok && hipMalloc((void**)&r->dev_state, 3 * tail_bytes) == hipSuccess;
     if (ok) {
         std::memset(r->slots, 0, slot_bytes);
         std::memset(r->host_tail, 0, tail_bytes);
-        ok = hipMemset(r->dev_state, 0, 2 * tail_bytes) == hipSuccess &&
+        ok = hipMemset(r->dev_state, 0, 3 * tail_bytes) == hipSuccess &&
              hipDeviceSynchronize() == hipSuccess;
     }
     if (!ok) {
@@ -183,10 +201,10 @@ extern "C" int ep_ring_reset(ep_ring_t* r) {
     if (!r) return EP_ERR_INVALID_ARG;
     std::lock_guard<std::mutex> g(r->mu);
     if (r->running.load()) return EP_ERR_BUSY;
-    std::memset(r->slots, 0, (size_t)r->channels * r->depth * sizeof(ep_transfer_cmd_t));
+    std::memset(r->slots, 0, (size_t)r->channels * r->depth * sizeof(RingSlot));
     std::memset(r->host_tail, 0, (size_t)r->channels * kPad * sizeof(unsigned long long));
     std::fill(r->pos.begin(), r->pos.end(), 0ull);
-    EP_HIP_CHECK(hipMemset(r->dev_state, 0, 2 * (size_t)r->channels * kPad * sizeof(unsigned long long)));
+    EP_HIP_CHECK(hipMemset(r->dev_state, 0, 3 * (size_t)r->channels * kPad * sizeof(unsigned long long)));
     EP_HIP_CHECK(hipDeviceSynchronize());
     return EP_OK;
 }

@@ -87,9 +87,11 @@ typedef struct ep_shape {
     int32_t T, H, E, R, k, fmt;
 } ep_shape_t;
 
-/* One FIFO slot, 32 bytes: the command a CPU proxy would execute
- * (UCCL-EP s2.3 WRITE fields; s3.2 op/value).  Written by the GPU into host
- * memory; `seq` is written last and equals the slot's ticket + 1.
+/* One TransferCmd, 32 bytes: the command a CPU proxy would execute
+ * (UCCL-EP s2.3 WRITE fields; s3.2 op/value), as returned by the drain and
+ * proxy calls.  `seq` is the command's ticket in its channel + 1 (its FIFO
+ * position).  In the ring itself the GPU stores each command as four
+ * self-tagged 8-byte words, so it never writes a separate ready flag.
  *   WRITE : copy `size_or_value` bytes holding `num_tokens` (1..8) rows from
  *           byte `src_offset` of the send buffer to byte `dst_offset` of rank
  *           `dst_rank`'s receive region.
@@ -189,8 +191,9 @@ int ep_combine(const ep_shape_t* shape, const void* y, int64_t y_rows,
  * consumer position live in host-pinned coherent memory (the consumer is a
  * CPU proxy); the producer ticket counter and a cached copy of the consumer
  * position live in device memory.  Allocated on the current device; returns
- * NULL on invalid arguments (depth < 1, channels < 1 or > 64,
+ * NULL on invalid arguments (depth < 1 or > 65535, channels < 1 or > 64,
  * max_inflight < 1 or > depth, timeout_ns < 1) or allocation failure.
+ * Descriptor offsets must fit 48 bits (capacity_rows * row bytes < 2^48).
  * A ring serves one stream at a time. */
 ep_ring_t* ep_ring_create(int32_t depth, int32_t channels, int32_t max_inflight,
                           int64_t timeout_ns);

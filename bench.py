@@ -53,6 +53,38 @@ def algorithmic_bytes(w, P: int) -> dict:
             "total": layout_r + layout_w + pack_r + pack_w + comb_r + comb_w}
 
 
+KERNEL_SOURCES = ["combine_topk_rank_amd/csrc/ep_dispatch.hip",
+                  "combine_topk_rank_amd/csrc/ep_combine.hip",
+                  "combine_topk_rank_amd/csrc/ep_layout.hip",
+                  "combine_topk_rank_amd/csrc/ep_common.h"]
+
+
+def measured_traffic(kernel_prefix: str, workload: str):
+    """HBM bytes per launch of a kernel from the rocprofv3 counter summaries
+    under profiles/, or None when none matches the current kernel sources."""
+    import glob
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    sha = h.hexdigest()
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        text = open(path).read()
+        for m in re.finditer(r"```json\n(.*?)\n```", text, re.S):
+            try:
+                block = json.loads(m.group(1))
+            except ValueError:
+                continue
+            if block.get("source_sha256") != sha:
+                continue
+            for c in block.get("counters", []):
+                if kernel_prefix in c["kernel"] and c["workload"] == workload:
+                    return int(c["traffic_bytes"]), os.path.relpath(path, ROOT)
+    return None
+
+
 def cpu_baseline(w, inp, budget_s: float) -> dict:
     """The oracle as it stands, single thread, on whole passes of the same
     workload until about budget_s seconds of CPU work."""
@@ -97,7 +129,20 @@ def main() -> int:
                     help="seconds of oracle work for the CPU baseline (0: skip)")
     ap.add_argument("--cold-steps", type=int, default=20,
                     help="extra steps with the 256 MB last-level cache flushed before each")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MiB",
+                    help="only run 5 plain device-to-device copies of this many MiB (a known "
+                         "byte count for scaling hardware traffic counters) and exit")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        import torch
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "copies": 5}), flush=True)
+        return 0
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the EP ranks are "
               "simulated as regions of one GPU's HBM", file=sys.stderr)
@@ -199,10 +244,11 @@ def main() -> int:
     tokens_s = w.T * K / elapsed
     # dominant kernel: the longer of pack (inside ep_dispatch) and combine
     if t_disp >= t_comb:
-        dom, dom_ms, dom_bytes = "pack_kernel (ep_dispatch)", t_disp, ab["dispatch"]
+        dom, dom_ms, dom_bytes, prefix = "pack_kernel (ep_dispatch)", t_disp, ab["dispatch"], "pack_kernel"
     else:
-        dom, dom_ms, dom_bytes = "combine_kernel (ep_combine)", t_comb, ab["combine"]
+        dom, dom_ms, dom_bytes, prefix = "combine_kernel (ep_combine)", t_comb, ab["combine"], "combine_kernel"
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    traffic = measured_traffic(prefix, w.name)
 
     cpu = None
     if args.cpu_budget > 0:
@@ -235,7 +281,10 @@ def main() -> int:
         "descriptors_per_step": n_cmds,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None},
+                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "algorithmic_bytes": dom_bytes,
+                     "traffic": traffic[0] if traffic else None,
+                     "traffic_source": traffic[1] if traffic else None},
         "cold": cold,
         "cpu_baseline": cpu,
     }

@@ -56,6 +56,7 @@ struct PackArgs {
     int32_t nv;                   // 16-byte vectors per x row (H/8)
     int32_t nchunks;              // wavefronts per token
     int32_t has_ring;
+    int64_t ngroups;              // groups of kPackWaves wavefronts
 };
 
 // ------------------------------------------------------------------ ring
@@ -252,6 +253,11 @@ constexpr int kPackWaves = 16;
 // Vectors per lane for rows of up to 896 vectors (H = 7168): 14 = one
 // wavefront per row, 7 = two.
 constexpr int kPackVplH7168 = 14;
+// Pack workgroups per compute unit, at most: with fewer workgroups than
+// groups, each workgroup loops, so rows complete (and descriptors are
+// published) in several generations instead of all at the end of the kernel.
+// Half the compute units already saturate HBM with 16 wavefronts each.
+constexpr int kPackGridPerCuNum = 1, kPackGridPerCuDen = 2;
 
 template <int VPL, int FMT>
 __global__ __launch_bounds__(kPackWaves * kWave) void pack_kernel(PackArgs a) {
@@ -261,13 +267,16 @@ __global__ __launch_bounds__(kPackWaves * kWave) void pack_kernel(PackArgs a) {
     __shared__ int32_t s_npairs[kWaves];
     const int lane = lane_id();
     const int wave = (int)(threadIdx.x / kWave);
-    const int64_t gw = (int64_t)blockIdx.x * kWaves + wave;
     const int64_t P = a.rank_off[a.R];
     const bool cap_ok = P <= a.cap;
-    if (gw == 0) {
+    if (blockIdx.x == 0 && wave == 0) {
         if (!cap_ok && lane == 0) set_error(a.st, EP_ERR_CAPACITY);
         if (a.has_ring && cap_ok) publish_empty_ranks(a);
     }
+    // groups of kWaves wavefronts, taken in launch order; a workgroup that
+    // finishes a group (rows, then descriptors) moves on to the next one
+    for (int64_t grp = blockIdx.x; grp < a.ngroups; grp += gridDim.x) {
+    const int64_t gw = grp * kWaves + wave;
     const int64_t t = gw / a.nchunks;
     const int chunk = (int)(gw - t * a.nchunks);
     const bool active = t < a.T;   // wavefront-uniform
@@ -363,7 +372,7 @@ __global__ __launch_bounds__(kPackWaves * kWave) void pack_kernel(PackArgs a) {
         }
     }
 
-    if (!(a.has_ring && cap_ok)) return;   // uniform over the workgroup
+    if (!(a.has_ring && cap_ok)) continue;   // uniform over the workgroup
     // hand this wavefront's (slot, rank) pairs to wavefront 0
     if ((dmask >> lane) & 1ull) {
         const int j = lane_prefix(dmask);
@@ -372,29 +381,32 @@ __global__ __launch_bounds__(kPackWaves * kWave) void pack_kernel(PackArgs a) {
     }
     if (lane == 0) s_npairs[wave] = (int32_t)__popcll(dmask);
     __syncthreads();
-    if (wave != 0) return;
-    // One system-scope release for the rows and metadata of the whole
-    // workgroup (ordered after the other wavefronts' stores by the barrier),
-    // then the arrivals and the descriptors.
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");
-    int total = 0;
+    if (wave == 0) {
+        // One system-scope release for the rows and metadata of the whole
+        // group (ordered after the other wavefronts' stores by the barrier),
+        // then the arrivals and the descriptors.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");
+        int total = 0;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) total += s_npairs[w];
-    for (int base = 0; base < total; base += kWave) {
-        int p = base + lane;
-        const bool mine = p < total;
-        int r = 0;
-        int32_t s = 0;
-        if (mine) {
-            int w = 0;
-            while (p >= s_npairs[w]) {
-                p -= s_npairs[w];
-                ++w;
+        for (int w = 0; w < kWaves; ++w) total += s_npairs[w];
+        for (int base = 0; base < total; base += kWave) {
+            int p = base + lane;
+            const bool mine = p < total;
+            int r = 0;
+            int32_t s = 0;
+            if (mine) {
+                int w = 0;
+                while (p >= s_npairs[w]) {
+                    p -= s_npairs[w];
+                    ++w;
+                }
+                s = s_pair_slot[w][p];
+                r = s_pair_rank[w][p];
             }
-            s = s_pair_slot[w][p];
-            r = s_pair_rank[w][p];
+            arrive_and_publish(a, mine, r, s);
         }
-        arrive_and_publish(a, mine, r, s);
+    }
+    __syncthreads();   // the pair lists are reused by the next group
     }
 }
 
@@ -404,9 +416,25 @@ using namespace ep;
 
 namespace {
 
+int64_t pack_grid_cap() {
+    static int64_t cap = 0;   // per process; the library targets one GPU model
+    if (cap == 0) {
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            cus = 256;
+        cap = (int64_t)cus * kPackGridPerCuNum / kPackGridPerCuDen;
+        if (cap < 1) cap = 1;
+    }
+    return cap;
+}
+
 template <int VPL>
-int launch_pack(const PackArgs& a, int fmt, int64_t waves, hipStream_t stream) {
-    const int64_t blocks = ceil_div(waves, kPackWaves);
+int launch_pack(PackArgs a, int fmt, int64_t waves, hipStream_t stream) {
+    a.ngroups = ceil_div(waves, kPackWaves);
+    const int64_t cap = pack_grid_cap();
+    const int64_t blocks = a.ngroups < cap ? a.ngroups : cap;
     clear_hip_error();
     if (fmt == EP_FMT_BF16)
         hipLaunchKernelGGL((pack_kernel<VPL, EP_FMT_BF16>), dim3((unsigned)blocks),

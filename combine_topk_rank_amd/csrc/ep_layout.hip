@@ -27,10 +27,15 @@ __device__ inline uint64_t token_rank_mask(const int32_t* __restrict__ idx, int6
                                            int E, int k, int epr, int32_t* st, int32_t* hist) {
     uint64_t m = 0;
     if (t < T) {
+        // issue all k loads before using any (one memory latency, not k)
         const int32_t* row = idx + t * k;
-        for (int j = 0; j < k; ++j) {
-            int e = row[j];
-            if (e == -1) continue;
+        int32_t ids[kMaxK];
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j) ids[j] = j < k ? row[j] : -1;
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j) {
+            const int e = ids[j];
+            if (j >= k || e == -1) continue;
             if (e < -1 || e >= E) {
                 set_error(st, EP_ERR_BAD_EXPERT);
                 continue;
@@ -42,12 +47,24 @@ __device__ inline uint64_t token_rank_mask(const int32_t* __restrict__ idx, int6
     return m;
 }
 
-// Per-wave count of tokens routed to each rank -> wcnt[r].
-__device__ inline void wave_rank_counts(uint64_t mask, int R, int32_t* wcnt) {
+// Per-wave rank ballots: bit i of ball_r = the wave's token i goes to rank r.
+// Lane l ends up holding ball_{l mod R} (all lanes, so that every group of R
+// lanes has the full set); lanes < R write their count to wcnt[r] and, when
+// given, the ballot to ball[r].
+__device__ inline uint64_t wave_rank_counts(uint64_t mask, int R, int32_t* wcnt,
+                                            uint64_t* ball = nullptr) {
+    const int lane = lane_id();
+    const int my_r = lane % R;
+    uint64_t mine = 0;
     for (int r = 0; r < R; ++r) {
-        uint64_t b = __ballot((mask >> r) & 1ull);
-        if (lane_id() == 0) wcnt[r] = (int32_t)__popcll(b);
+        const uint64_t b = __ballot((mask >> r) & 1ull);
+        if (my_r == r) mine = b;
     }
+    if (lane < R) {
+        wcnt[lane] = (int32_t)__popcll(mine);
+        if (ball) ball[lane] = mine;
+    }
+    return mine;
 }
 
 // Exclusive scan of n (<= kMaxE) ints held in LDS `v`, written to `out`
@@ -94,9 +111,9 @@ __device__ inline void column_sums(const int32_t* __restrict__ m, int nrows, int
 #pragma unroll 4
         for (int64_t i = threadIdx.x; i < n4; i += kBlock) {
             const int4 q = m4[i];
-            const int64_t e0 = i * 4;
-            const int row = (int)(e0 / ncols);
-            const int col = (int)(e0 - (int64_t)row * ncols);
+            const int e0 = (int)(i * 4);
+            const int row = e0 / ncols;
+            const int col = e0 - row * ncols;
             atomicAdd(&acc[col], q.x);
             atomicAdd(&acc[col + 1], q.y);
             atomicAdd(&acc[col + 2], q.z);
@@ -112,8 +129,8 @@ __device__ inline void column_sums(const int32_t* __restrict__ m, int nrows, int
 #pragma unroll 4
         for (int64_t i = threadIdx.x; i < n; i += kBlock) {
             const int32_t q = m[i];
-            const int row = (int)(i / ncols);
-            const int col = (int)(i - (int64_t)row * ncols);
+            const int row = (int)i / ncols;
+            const int col = (int)i - row * ncols;
             atomicAdd(&acc[col], q);
             if (acc_pre && row < split) atomicAdd(&acc_pre[col], q);
         }
@@ -163,6 +180,8 @@ __global__ __launch_bounds__(kBlock) void layout_main_kernel(
     __shared__ int32_t s_tot[kMaxR];     // rows of rank r in all tiles
     __shared__ int32_t s_base[kMaxR];    // first slot of rank r in this tile
     __shared__ int32_t s_part[kBlock];
+    __shared__ uint64_t s_ball[kBlock / kWave][kMaxR];   // per-wave rank ballots
+    __shared__ int32_t s_wbase[kBlock / kWave][kMaxR];   // first slot of rank r in the wave
     const int tid = threadIdx.x;
     const int lane = lane_id();
     const int wave = tid / kWave;
@@ -175,7 +194,7 @@ __global__ __launch_bounds__(kBlock) void layout_main_kernel(
     const int64_t t_first = (int64_t)b * kLayoutTile;
     const int64_t t = t_first + tid;
     uint64_t mask = token_rank_mask(idx, t, T, E, k, epr, st, SINGLE ? s_hist : nullptr);
-    wave_rank_counts(mask, R, s_wcnt[wave]);
+    const uint64_t my_ball = wave_rank_counts(mask, R, s_wcnt[wave], s_ball[wave]);
     __syncthreads();
 
     // rank totals and the prefix over earlier tiles
@@ -236,23 +255,74 @@ __global__ __launch_bounds__(kBlock) void layout_main_kernel(
     }
     __syncthreads();
 
-    // slots: lane r < R walks this wave's 64 tokens in order
-    int32_t run = 0;
+    // slots in closed form: for the wave's token i and rank r,
+    //   slot = (first slot of r in this wave) + popcount(ball[r] below bit i)
+    // The wave's rows of send_slot / is_token_in_rank are one contiguous
+    // block of n*R entries, written with 16-byte stores by all lanes.
     if (lane < R) {
-        run = s_base[lane];
+        int32_t run = s_base[lane];
         for (int w = 0; w < wave; ++w) run += s_wcnt[w][lane];
+        s_wbase[wave][lane] = run;
     }
+    __syncthreads();
     const int64_t t_wave = t_first + (int64_t)wave * kWave;
-    for (int i = 0; i < kWave; ++i) {
-        const int64_t tt = t_wave + i;
-        if (tt >= T) break;
-        uint64_t m = bcast64(mask, i);
-        if (lane < R) {
-            int bit = (int)((m >> lane) & 1ull);
-            send_slot[tt * R + lane] = bit ? run : -1;
-            in_rank[tt * R + lane] = (uint8_t)bit;
-            run += bit;
+    const int n = (int)max((int64_t)0, min((int64_t)kWave, (int64_t)T - t_wave));   // tokens in this wave
+    const int64_t nel = (int64_t)n * R;
+    const uint64_t* ball = s_ball[wave];
+    const int32_t* wbase = s_wbase[wave];
+    int32_t* slot_out = send_slot + t_wave * R;
+    uint8_t* in_out = in_rank + t_wave * R;
+    if ((kWave % R) == 0) {
+        // R divides 64: lane l serves rank l % R of token (j * 64 + l) / R,
+        // so each store covers 64 consecutive entries; the ballot and base
+        // are already in the lane's registers.
+        const int G = kWave / R;
+        const int my_r = lane % R;
+        const int my_g = lane / R;
+        const int32_t my_base = s_wbase[wave][my_r];
+        for (int j = 0; j * G < n; ++j) {
+            const int i = j * G + my_g;
+            if (i < n) {
+                const int bit = (int)((my_ball >> i) & 1ull);
+                const int32_t sl =
+                    bit ? my_base + (int32_t)__popcll(my_ball & ((1ull << i) - 1ull)) : -1;
+                slot_out[j * kWave + lane] = sl;
+                in_out[j * kWave + lane] = (uint8_t)bit;
+            }
         }
+    } else {
+    // (t_wave * R) % 4 == 0 because kWave * R is a multiple of 4: 4-entry groups
+    for (int g = lane; g * 4 < (int)nel; g += kWave) {
+        int32_t v[4];
+        uint32_t bytes = 0;
+        int i = (g * 4) / R;            // token of the group's first entry
+        int r = g * 4 - i * R;          // its rank
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            int32_t sl = -1;
+            if (g * 4 + q < (int)nel) {
+                const uint64_t br = ball[r];
+                if ((br >> i) & 1ull) {
+                    sl = wbase[r] + (int32_t)__popcll(br & ((1ull << i) - 1ull));
+                    bytes |= 1u << (8 * q);
+                }
+            }
+            v[q] = sl;
+            if (++r == R) {
+                r = 0;
+                ++i;
+            }
+        }
+        if (g * 4 + 4 <= nel) {
+            *reinterpret_cast<int4*>(slot_out + g * 4) = int4{v[0], v[1], v[2], v[3]};
+            *reinterpret_cast<uint32_t*>(in_out + g * 4) = bytes;
+        } else {
+            for (int q = 0; q < 4 && g * 4 + q < nel; ++q) {
+                slot_out[g * 4 + q] = v[q];
+                in_out[g * 4 + q] = (uint8_t)((bytes >> (8 * q)) & 1u);
+            }
+        }
+    }
     }
     if (SINGLE) zero_counters(counters, counters_n, tid, kBlock);
 }
@@ -273,6 +343,7 @@ extern "C" int ep_dispatch_layout(const ep_shape_t* shape, const int32_t* topk_i
         !dev_status || !workspace)
         return EP_ERR_INVALID_ARG;
     if (s.T > 0 && (!topk_idx || !is_token_in_rank || !send_slot)) return EP_ERR_INVALID_ARG;
+    if (((uintptr_t)send_slot & 15) || ((uintptr_t)is_token_in_rank & 3)) return EP_ERR_INVALID_ARG;
     if (ws_bytes < workspace_bytes(s)) return EP_ERR_INVALID_ARG;
     Workspace w = carve_workspace(s, workspace);
     const int epr = s.E / s.R;

@@ -48,7 +48,8 @@
  *   - Expert e lives on rank e / (E / R).  A token goes once to every rank
  *     that owns one of its experts (the (token, rank) pair is the unit of
  *     dispatch).  Expert id -1 is a dropped choice and is skipped.
- *   - Alignment: x, send_buf, y and out are 16-byte aligned.
+ *   - Alignment: x, send_buf, y, out and send_slot are 16-byte aligned,
+ *     is_token_in_rank 4-byte aligned.
  */
 #ifndef EP_H
 #define EP_H

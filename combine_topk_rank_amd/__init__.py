@@ -42,6 +42,7 @@ EP_ERR_CAPACITY = 3
 EP_ERR_RING_TIMEOUT = 4
 EP_ERR_HIP = 5
 EP_ERR_BUSY = 6
+EP_ERR_TIMEOUT = 7
 EP_FMT_BF16 = 0
 EP_FMT_FP8_E4M3_B128 = 1
 EP_CMD_WRITE = 1
@@ -252,7 +253,8 @@ class Buffers:
         self.slot_src = torch.empty(cap, **i32)
         self.slot_local_idx = torch.empty((cap, k), **i32)
         self.slot_local_w = torch.empty((cap, k), dtype=torch.float32, device=device)
-        self.workspace = torch.empty(max(ep_workspace_bytes(s), 256), dtype=torch.uint8,
+        # zero-filled once; the library keeps it consistent afterwards
+        self.workspace = torch.zeros(max(ep_workspace_bytes(s), 256), dtype=torch.uint8,
                                      device=device)
         self.dev_status = torch.zeros(1, **i32)
         self.out = torch.empty((T, H), dtype=torch.bfloat16, device=device)

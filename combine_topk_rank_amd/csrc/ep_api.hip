@@ -41,7 +41,7 @@ inline size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 size_t workspace_bytes(const ep_shape_t& s) {
     const int64_t nb = layout_blocks(s.T);
-    size_t b = 0;
+    size_t b = 256;                            // grid barrier words
     b += align256((size_t)nb * s.R * 4);       // blk_rank_cnt
     b += align256((size_t)nb * s.E * 4);       // blk_exp_cnt
     b += align256((size_t)(s.R + 1) * 4);      // msg_base
@@ -54,6 +54,8 @@ Workspace carve_workspace(const ep_shape_t& s, void* base) {
     uint8_t* p = reinterpret_cast<uint8_t*>(base);
     const int64_t nb = layout_blocks(s.T);
     w.layout_blocks = (int32_t)nb;
+    w.barrier = reinterpret_cast<uint32_t*>(p);
+    p += 256;
     w.blk_rank_cnt = reinterpret_cast<int32_t*>(p);
     p += align256((size_t)nb * s.R * 4);
     w.blk_exp_cnt = reinterpret_cast<int32_t*>(p);
@@ -94,6 +96,7 @@ extern "C" const char* ep_status_str(int st) {
         case EP_ERR_RING_TIMEOUT: return "transfer ring full for longer than its timeout";
         case EP_ERR_HIP: return "HIP runtime error";
         case EP_ERR_BUSY: return "ring busy (proxy threads running)";
+        case EP_ERR_TIMEOUT: return "a device-side wait for other workgroups timed out";
         default: return "unknown status";
     }
 }

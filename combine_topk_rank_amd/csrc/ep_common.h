@@ -18,6 +18,8 @@ constexpr int kMaxR = 64;          // a rank set is one 64-bit mask
 constexpr int kMaxE = 4096;        // per-expert LDS histogram bound
 constexpr int kMaxK = 32;          // experts of a token sit in lanes 0..k-1
 constexpr int kPad = 8;            // 64-byte stride between per-channel counters
+// Bound on a grid-barrier wait, in s_memrealtime ticks (100 MHz): one second.
+constexpr unsigned long long kBarrierTimeoutTicks = 100000000ull;
 
 // One FIFO slot as it sits in the ring: four 64-bit words, each
 //   bits  0..15  tag = low 16 bits of (ticket + 1)
@@ -53,8 +55,9 @@ struct RingDev {
     unsigned long long timeout_ticks;      // in s_memrealtime ticks
 };
 
-// Carved workspace (all int32).
+// Carved workspace.
 struct Workspace {
+    uint32_t* barrier;        // [2] grid barrier: arrivals, generation (zero at first use)
     int32_t* blk_rank_cnt;    // [NB, R] per-layout-block rank counts
     int32_t* blk_exp_cnt;     // [NB, E] per-layout-block expert counts
     int32_t* msg_base;        // [R+1]   first message index of each rank

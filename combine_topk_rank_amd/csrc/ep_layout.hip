@@ -15,7 +15,9 @@
 //   layout_main_kernel  : per tile, prefix over the earlier tiles' counts,
 //                         then the slots of its tokens.  Tile 0 also writes
 //                         the counts, offsets and message bases.
-// One pass (layout_main_kernel<true>) when T fits one tile.
+// When every tile can be resident at once, both passes run in one kernel
+// (layout_main_kernel<2>) whose tiles meet at a grid barrier instead of a
+// kernel boundary; one workgroup does everything when T fits one tile.
 
 #include "ep_common.h"
 
@@ -165,15 +167,59 @@ __global__ __launch_bounds__(kBlock) void layout_count_kernel(
                   (int64_t)gridDim.x * kBlock);
 }
 
-template <bool SINGLE>
+// Grid-wide barrier for a grid whose workgroups are all resident: bar[0]
+// counts arrivals, bar[1] is a generation number.  Each workgroup reads the
+// generation before it arrives; the last arrival resets the count and bumps
+// the generation, which releases the others.  The words stay consistent from
+// one call to the next for any grid size (they start at zero).  The wait is
+// bounded by about a second of wall clock; on timeout the status is set and
+// false is returned.  Stores made before the barrier by any workgroup are
+// visible to loads made after it by every workgroup.
+__device__ bool grid_barrier(uint32_t* bar, uint32_t nblocks, int32_t* st) {
+    __shared__ int s_ok;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int ok = 1;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        const uint32_t gen = __hip_atomic_load(&bar[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t old = atomicAdd(&bar[0], 1u);
+        if (old == nblocks - 1) {
+            atomicExch(&bar[0], 0u);
+            __hip_atomic_store(&bar[1], gen + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+            while (__hip_atomic_load(&bar[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gen) {
+                if (__builtin_amdgcn_s_memrealtime() - t0 > kBarrierTimeoutTicks) {
+                    set_error(st, EP_ERR_TIMEOUT);
+                    ok = 0;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        s_ok = ok;
+    }
+    __syncthreads();
+    return s_ok != 0;
+}
+
+// MODE 0: one tile (the whole layout in one workgroup).
+// MODE 1: second pass after layout_count_kernel.
+// MODE 2: both passes in one kernel, the tiles meeting at a grid barrier
+//         (used only when every tile can be resident at once).
+template <int MODE>
 __global__ __launch_bounds__(kBlock) void layout_main_kernel(
     const int32_t* __restrict__ idx, int T, int E, int R, int k, int epr, int nblocks,
-    const int32_t* __restrict__ blk_rank_cnt, const int32_t* __restrict__ blk_exp_cnt,
+    int32_t* __restrict__ blk_rank_cnt, int32_t* __restrict__ blk_exp_cnt,
     int32_t* __restrict__ cnt_rank, int32_t* __restrict__ cnt_exp,
     int32_t* __restrict__ rank_off, int32_t* __restrict__ exp_off, int32_t* __restrict__ msg_base,
     uint8_t* __restrict__ in_rank, int32_t* __restrict__ send_slot,
-    int32_t* __restrict__ counters, int64_t counters_n, int32_t* st) {
-    __shared__ int32_t s_hist[SINGLE ? kMaxE : 1];
+    int32_t* __restrict__ counters, int64_t counters_n, uint32_t* __restrict__ bar,
+    int32_t* st) {
+    constexpr bool SINGLE = MODE == 0;
+    constexpr bool FUSED = MODE == 2;
+    __shared__ int32_t s_hist[(SINGLE || FUSED) ? kMaxE : 1];
     __shared__ int32_t s_exp[kMaxE];
     __shared__ int32_t s_wcnt[kBlock / kWave][kMaxR];
     __shared__ int32_t s_pre[kMaxR];     // rows of rank r in earlier tiles
@@ -187,15 +233,29 @@ __global__ __launch_bounds__(kBlock) void layout_main_kernel(
     const int wave = tid / kWave;
     const int b = blockIdx.x;
 
-    if (SINGLE) {
+    if (SINGLE || FUSED) {
         for (int e = tid; e < E; e += kBlock) s_hist[e] = 0;
         __syncthreads();
     }
     const int64_t t_first = (int64_t)b * kLayoutTile;
     const int64_t t = t_first + tid;
-    uint64_t mask = token_rank_mask(idx, t, T, E, k, epr, st, SINGLE ? s_hist : nullptr);
+    uint64_t mask =
+        token_rank_mask(idx, t, T, E, k, epr, st, (SINGLE || FUSED) ? s_hist : nullptr);
     const uint64_t my_ball = wave_rank_counts(mask, R, s_wcnt[wave], s_ball[wave]);
     __syncthreads();
+
+    if (FUSED) {
+        // first pass: this tile's counts for the others, then meet them
+        if (tid < R) {
+            int32_t c = 0;
+            for (int w = 0; w < kBlock / kWave; ++w) c += s_wcnt[w][tid];
+            blk_rank_cnt[(int64_t)b * R + tid] = c;
+        }
+        for (int e = tid; e < E; e += kBlock)
+            blk_exp_cnt[(int64_t)b * E + e] = s_hist[e];
+        zero_counters(counters, counters_n, (int64_t)b * kBlock + tid, (int64_t)gridDim.x * kBlock);
+        if (!grid_barrier(bar, (uint32_t)gridDim.x, st)) return;
+    }
 
     // rank totals and the prefix over earlier tiles
     if (SINGLE) {
@@ -247,7 +307,7 @@ __global__ __launch_bounds__(kBlock) void layout_main_kernel(
     if (b == 0) {
         // per-expert totals and their exclusive scan
         for (int e = tid; e < E; e += kBlock) {
-            if (SINGLE) s_exp[e] = s_hist[e];
+            if (SINGLE) s_exp[e] = s_hist[e];   // (FUSED reads the tiles' totals)
             cnt_exp[e] = s_exp[e];
         }
         __syncthreads();
@@ -327,6 +387,24 @@ __global__ __launch_bounds__(kBlock) void layout_main_kernel(
     if (SINGLE) zero_counters(counters, counters_n, tid, kBlock);
 }
 
+// Tiles of the one-kernel layout that can be resident at once on the current
+// device (workgroups per CU from the occupancy calculator x CUs), or 0.
+int64_t max_resident_layout_tiles() {
+    static int64_t cached = -1;   // per process; the library targets one GPU model
+    if (cached < 0) {
+        int dev = 0, cus = 0, per_cu = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &per_cu, reinterpret_cast<const void*>(layout_main_kernel<2>), kBlock, 0) ==
+                hipSuccess)
+            cached = (int64_t)cus * per_cu;
+        else
+            cached = 0;
+    }
+    return cached;
+}
+
 }  // namespace ep
 
 using namespace ep;
@@ -351,20 +429,26 @@ extern "C" int ep_dispatch_layout(const ep_shape_t* shape, const int32_t* topk_i
     int32_t* counters = w.msg_arrivals;
     clear_hip_error();
     if (nb == 1) {
-        hipLaunchKernelGGL(layout_main_kernel<true>, dim3(1), dim3(kBlock), 0, stream, topk_idx,
-                           s.T, s.E, s.R, s.k, epr, 1, (const int32_t*)nullptr,
-                           (const int32_t*)nullptr, num_tokens_per_rank, num_tokens_per_expert,
-                           rank_offset, expert_offset, w.msg_base, is_token_in_rank, send_slot,
-                           counters, w.counters_n, dev_status);
+        hipLaunchKernelGGL(layout_main_kernel<0>, dim3(1), dim3(kBlock), 0, stream, topk_idx, s.T,
+                           s.E, s.R, s.k, epr, 1, (int32_t*)nullptr, (int32_t*)nullptr,
+                           num_tokens_per_rank, num_tokens_per_expert, rank_offset, expert_offset,
+                           w.msg_base, is_token_in_rank, send_slot, counters, w.counters_n,
+                           w.barrier, dev_status);
+    } else if (nb <= max_resident_layout_tiles()) {
+        hipLaunchKernelGGL(layout_main_kernel<2>, dim3(nb), dim3(kBlock), 0, stream, topk_idx, s.T,
+                           s.E, s.R, s.k, epr, nb, w.blk_rank_cnt, w.blk_exp_cnt,
+                           num_tokens_per_rank, num_tokens_per_expert, rank_offset, expert_offset,
+                           w.msg_base, is_token_in_rank, send_slot, counters, w.counters_n,
+                           w.barrier, dev_status);
     } else {
         hipLaunchKernelGGL(layout_count_kernel, dim3(nb), dim3(kBlock), 0, stream, topk_idx, s.T,
                            s.E, s.R, s.k, epr, w.blk_rank_cnt, w.blk_exp_cnt, counters,
                            w.counters_n, dev_status);
-        hipLaunchKernelGGL(layout_main_kernel<false>, dim3(nb), dim3(kBlock), 0, stream, topk_idx,
-                           s.T, s.E, s.R, s.k, epr, nb, w.blk_rank_cnt, w.blk_exp_cnt,
+        hipLaunchKernelGGL(layout_main_kernel<1>, dim3(nb), dim3(kBlock), 0, stream, topk_idx, s.T,
+                           s.E, s.R, s.k, epr, nb, w.blk_rank_cnt, w.blk_exp_cnt,
                            num_tokens_per_rank, num_tokens_per_expert, rank_offset, expert_offset,
                            w.msg_base, is_token_in_rank, send_slot, counters, w.counters_n,
-                           dev_status);
+                           w.barrier, dev_status);
     }
     EP_HIP_CHECK(hipGetLastError());
     return EP_OK;

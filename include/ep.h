@@ -71,7 +71,8 @@ enum ep_status {
     EP_ERR_CAPACITY = 3,      /* device: P > capacity_rows */
     EP_ERR_RING_TIMEOUT = 4,  /* device: a producer waited longer than the ring's timeout */
     EP_ERR_HIP = 5,           /* a HIP runtime call failed */
-    EP_ERR_BUSY = 6           /* ring call not allowed while its proxy threads run */
+    EP_ERR_BUSY = 6,          /* ring call not allowed while its proxy threads run */
+    EP_ERR_TIMEOUT = 7        /* device: workgroups waited for each other too long */
 };
 
 /* Row format of the send buffer. */
@@ -116,10 +117,13 @@ typedef struct ep_ring ep_ring_t;
 size_t ep_row_bytes(int32_t H, int32_t fmt);
 
 /* Bytes of device workspace that ep_dispatch_layout and ep_dispatch need for
- * `shape` (per-block partial counts, per-message arrival counters).  One
- * workspace serves a layout call and the dispatch calls that follow it on the
- * same stream; its contents need no initialisation.  Returns 0 for an invalid
- * shape. */
+ * `shape` (a grid-barrier word pair, per-tile partial counts, per-message
+ * arrival counters).  One workspace serves a layout call and the dispatch
+ * calls that follow it on the same stream.  It must be zero-filled once
+ * before its first use (e.g. hipMemset); the library leaves it consistent
+ * after every call that completes.  A workspace sized for a shape also serves
+ * every smaller shape.  After a call fails with EP_ERR_TIMEOUT it must be
+ * zero-filled again.  Returns 0 for an invalid shape. */
 size_t ep_workspace_bytes(const ep_shape_t* shape);
 
 /* Routing layout.  UCCL-EP s1 (token-level exchange with many
@@ -133,7 +137,9 @@ size_t ep_workspace_bytes(const ep_shape_t* shape);
  *   send_slot             int32 [T,R]   row of (t,r) in the send buffer, or -1;
  *                                       rank r's rows are [o_r, o_{r+1}) in
  *                                       ascending token order
- * Device error: EP_ERR_BAD_EXPERT (the offending entry is skipped). */
+ * Device errors: EP_ERR_BAD_EXPERT (the offending entry is skipped),
+ * EP_ERR_TIMEOUT (the tiles of the one-kernel layout did not all become
+ * resident within a second; outputs are then unspecified). */
 int ep_dispatch_layout(const ep_shape_t* shape, const int32_t* topk_idx,
                        int32_t* num_tokens_per_rank, int32_t* num_tokens_per_expert,
                        int32_t* rank_offset, int32_t* expert_offset,

@@ -81,7 +81,7 @@ def test_ring_create_rejects_bad_arguments(ep):
 
 
 def test_status_strings(ep):
-    for st in range(7):
+    for st in range(8):
         assert ep.status_str(st) != "unknown status"
     assert ep.status_str(99) == "unknown status"
 

@@ -177,3 +177,20 @@ def test_layout_many_tiles():
     g = run_hip(T, 8, E, R, k, 0, inp["x"], inp["topk_idx"], inp["topk_w"], ring_cfg=None)
     assert g["status"] == 0
     assert_layout_equal(g, L)
+
+
+def test_layout_more_tiles_than_resident():
+    """300,000 tokens (1172 tiles) exceed what can be resident at once, so the
+    layout takes its two-kernel path; the result is the same."""
+    T, E, R, k = 300000, 64, 64, 4
+    rng = np.random.default_rng(18)
+    keys = rng.random((T, E), dtype=np.float32)
+    idx = np.ascontiguousarray(np.argpartition(-keys, k, axis=1)[:, :k].astype(np.int32))
+    del keys
+    L = oracle.layout(idx, E, R)
+    log("[parity] layout T=300000 R=64 (two-kernel path)")
+    x = np.zeros((T, 8), np.uint16)
+    w = np.ones((T, k), np.float32)
+    g = run_hip(T, 8, E, R, k, 0, x, idx, w, capacity_rows=1, ring_cfg=None)
+    assert g["status"] in (0, 3)   # capacity 1 row: the pack reports it, layout is intact
+    assert_layout_equal(g, L)

@@ -237,6 +237,16 @@ __device__ inline uint32_t e4m3x2(float a, float b, uint32_t old) {
 __device__ inline float bf16lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ inline float bf16hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
 
+// Largest magnitude among the four bf16 values of two words, as the bf16
+// bit pattern (finite values).
+__device__ inline uint32_t max_bf16_mag(uint32_t a, uint32_t b) {
+    const uint32_t a0 = a & 0x7FFFu, a1 = (a >> 16) & 0x7FFFu;
+    const uint32_t b0 = b & 0x7FFFu, b1 = (b >> 16) & 0x7FFFu;
+    const uint32_t x = a0 > a1 ? a0 : a1;
+    const uint32_t y = b0 > b1 ? b0 : b1;
+    return x > y ? x : y;
+}
+
 // max over the 16 lanes of a row group (a 128-element block is 16 lanes x 8)
 __device__ inline float group16_max(float v) {
     v = fmaxf(v, __shfl_xor(v, 1));
@@ -250,18 +260,20 @@ __device__ inline float group16_max(float v) {
 // Wavefronts per pack workgroup: they share one system-scope release for
 // their rows and one wavefront publishes their descriptors.
 constexpr int kPackWaves = 16;
+constexpr int kPackWavesFp8 = 8;
 // Vectors per lane for rows of up to 896 vectors (H = 7168): 14 = one
 // wavefront per row, 7 = two.
 constexpr int kPackVplH7168 = 14;
+constexpr int kPackVplFp8H7168 = 14;
 // Pack workgroups per compute unit, at most: with fewer workgroups than
 // groups, each workgroup loops, so rows complete (and descriptors are
 // published) in several generations instead of all at the end of the kernel.
 // Half the compute units already saturate HBM with 16 wavefronts each.
 constexpr int kPackGridPerCuNum = 1, kPackGridPerCuDen = 2;
 
-template <int VPL, int FMT>
-__global__ __launch_bounds__(kPackWaves * kWave) void pack_kernel(PackArgs a) {
-    constexpr int kWaves = kPackWaves;
+template <int VPL, int FMT, int WAVES>
+__global__ __launch_bounds__(WAVES * kWave) void pack_kernel(PackArgs a) {
+    constexpr int kWaves = WAVES;
     __shared__ int32_t s_pair_slot[kWaves][kMaxR];
     __shared__ int32_t s_pair_rank[kWaves][kMaxR];
     __shared__ int32_t s_npairs[kWaves];
@@ -312,24 +324,26 @@ __global__ __launch_bounds__(kPackWaves * kWave) void pack_kernel(PackArgs a) {
             }
         } else {
             // quantise once: per 128-element block, a = max(amax, 1e-4),
-            // codes = e4m3(x * (448 / a)), scale = a / 448
+            // codes = e4m3(x * (448 / a)), scale = a / 448.  The block max is
+            // taken on the bf16 bits: magnitudes of finite values order like
+            // unsigned integers, so no float copy of the row stays live.
             u32x2 q[VPL];
             float scale[VPL];
 #pragma unroll
             for (int i = 0; i < VPL; ++i) {
                 const u32x4 u = v[i];
-                float f0 = bf16lo(u.x), f1 = bf16hi(u.x), f2 = bf16lo(u.y), f3 = bf16hi(u.y);
-                float f4 = bf16lo(u.z), f5 = bf16hi(u.z), f6 = bf16lo(u.w), f7 = bf16hi(u.w);
-                float am = fmaxf(fmaxf(fmaxf(fabsf(f0), fabsf(f1)), fmaxf(fabsf(f2), fabsf(f3))),
-                                 fmaxf(fmaxf(fabsf(f4), fabsf(f5)), fmaxf(fabsf(f6), fabsf(f7))));
+                const uint32_t m01 = max_bf16_mag(u.x, u.y);
+                const uint32_t m23 = max_bf16_mag(u.z, u.w);
+                const uint32_t mw = m01 > m23 ? m01 : m23;
+                float am = __uint_as_float(mw << 16);
                 am = group16_max(am);
                 const float av = fmaxf(am, 1e-4f);
                 const float inv = 448.0f / av;
                 scale[i] = av / 448.0f;
-                uint32_t lo = e4m3x2<false>(f0 * inv, f1 * inv, 0);
-                lo = e4m3x2<true>(f2 * inv, f3 * inv, lo);
-                uint32_t hi = e4m3x2<false>(f4 * inv, f5 * inv, 0);
-                hi = e4m3x2<true>(f6 * inv, f7 * inv, hi);
+                uint32_t lo = e4m3x2<false>(bf16lo(u.x) * inv, bf16hi(u.x) * inv, 0);
+                lo = e4m3x2<true>(bf16lo(u.y) * inv, bf16hi(u.y) * inv, lo);
+                uint32_t hi = e4m3x2<false>(bf16lo(u.z) * inv, bf16hi(u.z) * inv, 0);
+                hi = e4m3x2<true>(bf16lo(u.w) * inv, bf16hi(u.w) * inv, hi);
                 q[i] = u32x2{lo, hi};
             }
             for (uint64_t m = dmask; m; m &= m - 1) {
@@ -432,16 +446,19 @@ int64_t pack_grid_cap() {
 
 template <int VPL>
 int launch_pack(PackArgs a, int fmt, int64_t waves, hipStream_t stream) {
-    a.ngroups = ceil_div(waves, kPackWaves);
-    const int64_t cap = pack_grid_cap();
+    // fp8 holds the codes and scales too: half the wavefronts per workgroup
+    // keep its registers (a 1024-thread workgroup caps a lane at 128)
+    const int wg_waves = fmt == EP_FMT_BF16 ? kPackWaves : kPackWavesFp8;
+    a.ngroups = ceil_div(waves, wg_waves);
+    const int64_t cap = pack_grid_cap() * (kPackWaves / wg_waves);
     const int64_t blocks = a.ngroups < cap ? a.ngroups : cap;
     clear_hip_error();
     if (fmt == EP_FMT_BF16)
-        hipLaunchKernelGGL((pack_kernel<VPL, EP_FMT_BF16>), dim3((unsigned)blocks),
+        hipLaunchKernelGGL((pack_kernel<VPL, EP_FMT_BF16, kPackWaves>), dim3((unsigned)blocks),
                            dim3(kPackWaves * kWave), 0, stream, a);
     else
-        hipLaunchKernelGGL((pack_kernel<VPL, EP_FMT_FP8_E4M3_B128>), dim3((unsigned)blocks),
-                           dim3(kPackWaves * kWave), 0, stream, a);
+        hipLaunchKernelGGL((pack_kernel<VPL, EP_FMT_FP8_E4M3_B128, kPackWavesFp8>),
+                           dim3((unsigned)blocks), dim3(kPackWavesFp8 * kWave), 0, stream, a);
     EP_HIP_CHECK(hipGetLastError());
     return EP_OK;
 }
@@ -501,7 +518,7 @@ extern "C" int ep_dispatch(const ep_shape_t* shape, const void* x, const int32_t
     else if (a.nv <= 128) vpl = 2;
     else if (a.nv <= 256) vpl = 4;
     else if (a.nv <= 512) vpl = 8;
-    else if (s.fmt != EP_FMT_BF16) vpl = a.nv <= 896 ? 7 : 8;
+    else if (s.fmt != EP_FMT_BF16) vpl = a.nv <= 896 ? kPackVplFp8H7168 : 8;
     else if (a.nv <= 896) vpl = kPackVplH7168;
     else vpl = 16;
     a.nchunks = (int32_t)ceil_div(a.nv, (int64_t)vpl * kWave);

@@ -41,7 +41,7 @@ inline size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 size_t workspace_bytes(const ep_shape_t& s) {
     const int64_t nb = layout_blocks(s.T);
-    size_t b = 256;                            // grid barrier words
+    size_t b = kWsHeader;                      // barrier words, channel ticket bases
     b += align256((size_t)nb * s.R * 4);       // blk_rank_cnt
     b += align256((size_t)nb * s.E * 4);       // blk_exp_cnt
     b += align256((size_t)(s.R + 1) * 4);      // msg_base
@@ -55,7 +55,8 @@ Workspace carve_workspace(const ep_shape_t& s, void* base) {
     const int64_t nb = layout_blocks(s.T);
     w.layout_blocks = (int32_t)nb;
     w.barrier = reinterpret_cast<uint32_t*>(p);
-    p += 256;
+    w.arrive = reinterpret_cast<uint32_t*>(p + 256);
+    p += kWsHeader;
     w.blk_rank_cnt = reinterpret_cast<int32_t*>(p);
     p += align256((size_t)nb * s.R * 4);
     w.blk_exp_cnt = reinterpret_cast<int32_t*>(p);

@@ -19,6 +19,10 @@ namespace ep {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Below this many wavefronts in the default layout, combine switches to
+// short chunks with eight rows in flight per wavefront.
+constexpr int64_t kCombineSmallWaves = 2048;
+
 struct CombineArgs {
     const u32x4* y;            // [P, H/8]
     const int32_t* idx;        // [T, k]
@@ -43,7 +47,9 @@ __device__ inline uint32_t pack2(float lo, float hi) {
     return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
 }
 
-template <int VPL>
+// B destination rows are loaded before any of them is accumulated (memory
+// parallelism within a wavefront); accumulation stays in ascending rank order.
+template <int VPL, int B>
 __global__ __launch_bounds__(kBlock) void combine_kernel(CombineArgs a) {
     const int lane = lane_id();
     const int64_t gw = (int64_t)blockIdx.x * (kBlock / kWave) + (threadIdx.x / kWave);
@@ -80,28 +86,49 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(CombineArgs a) {
 #pragma unroll
         for (int q = 0; q < 8; ++q) acc[i][q] = 0.0f;
 
-    for (uint64_t m = dmask; m; m &= m - 1) {
-        const int r = __builtin_ctzll(m);
-        const int32_t s = bcast(s_lane, r);
-        const float Wr = bcastf(W, r);
-        const u32x4* yr = a.y + (int64_t)s * a.nv;
-        u32x4 v[VPL];
+    for (uint64_t m = dmask; m;) {
+        int32_t ss[B];
+        float ww[B];
+        int nb = 0;
 #pragma unroll
-        for (int i = 0; i < VPL; ++i) {
-            int vi = v0 + lane + i * kWave;
-            v[i] = vi < a.nv ? __builtin_nontemporal_load(yr + vi) : u32x4{0, 0, 0, 0};
+        for (int b = 0; b < B; ++b) {
+            ss[b] = 0;
+            ww[b] = 0.0f;
+            if (m) {
+                const int r = __builtin_ctzll(m);
+                m &= m - 1;
+                ss[b] = bcast(s_lane, r);
+                ww[b] = bcastf(W, r);
+                nb = b + 1;
+            }
+        }
+        u32x4 v[B][VPL];
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            const u32x4* yr = a.y + (int64_t)ss[b] * a.nv;
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) {
+                const int vi = v0 + lane + i * kWave;
+                v[b][i] = (b < nb && vi < a.nv) ? __builtin_nontemporal_load(yr + vi)
+                                                : u32x4{0, 0, 0, 0};
+            }
         }
 #pragma unroll
-        for (int i = 0; i < VPL; ++i) {
-            const u32x4 u = v[i];
-            acc[i][0] = fmaf(Wr, __uint_as_float(u.x << 16), acc[i][0]);
-            acc[i][1] = fmaf(Wr, __uint_as_float(u.x & 0xFFFF0000u), acc[i][1]);
-            acc[i][2] = fmaf(Wr, __uint_as_float(u.y << 16), acc[i][2]);
-            acc[i][3] = fmaf(Wr, __uint_as_float(u.y & 0xFFFF0000u), acc[i][3]);
-            acc[i][4] = fmaf(Wr, __uint_as_float(u.z << 16), acc[i][4]);
-            acc[i][5] = fmaf(Wr, __uint_as_float(u.z & 0xFFFF0000u), acc[i][5]);
-            acc[i][6] = fmaf(Wr, __uint_as_float(u.w << 16), acc[i][6]);
-            acc[i][7] = fmaf(Wr, __uint_as_float(u.w & 0xFFFF0000u), acc[i][7]);
+        for (int b = 0; b < B; ++b) {
+            if (b >= nb) break;
+            const float Wr = ww[b];
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) {
+                const u32x4 u = v[b][i];
+                acc[i][0] = fmaf(Wr, __uint_as_float(u.x << 16), acc[i][0]);
+                acc[i][1] = fmaf(Wr, __uint_as_float(u.x & 0xFFFF0000u), acc[i][1]);
+                acc[i][2] = fmaf(Wr, __uint_as_float(u.y << 16), acc[i][2]);
+                acc[i][3] = fmaf(Wr, __uint_as_float(u.y & 0xFFFF0000u), acc[i][3]);
+                acc[i][4] = fmaf(Wr, __uint_as_float(u.z << 16), acc[i][4]);
+                acc[i][5] = fmaf(Wr, __uint_as_float(u.z & 0xFFFF0000u), acc[i][5]);
+                acc[i][6] = fmaf(Wr, __uint_as_float(u.w << 16), acc[i][6]);
+                acc[i][7] = fmaf(Wr, __uint_as_float(u.w & 0xFFFF0000u), acc[i][7]);
+            }
         }
     }
 
@@ -125,11 +152,12 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(CombineArgs a) {
 using namespace ep;
 
 namespace {
-template <int VPL>
+template <int VPL, int B>
 int launch_combine(const CombineArgs& a, int64_t waves, hipStream_t stream) {
     const int64_t blocks = ceil_div(waves, kBlock / kWave);
     clear_hip_error();
-    hipLaunchKernelGGL(combine_kernel<VPL>, dim3((unsigned)blocks), dim3(kBlock), 0, stream, a);
+    hipLaunchKernelGGL((combine_kernel<VPL, B>), dim3((unsigned)blocks), dim3(kBlock), 0, stream,
+                       a);
     EP_HIP_CHECK(hipGetLastError());
     return EP_OK;
 }
@@ -160,19 +188,27 @@ extern "C" int ep_combine(const ep_shape_t* shape, const void* y, int64_t y_rows
     a.k = s.k;
     a.epr = s.E / s.R;
     a.nv = s.H / 8;
-    int vpl;
-    if (a.nv <= 64) vpl = 1;
-    else if (a.nv <= 128) vpl = 2;
-    else if (a.nv <= 256) vpl = 4;
-    else if (a.nv <= 512) vpl = 8;
-    else vpl = 7;   // H = 7168: two wavefronts of 7 vectors per lane
-    a.nchunks = (int32_t)ceil_div(a.nv, (int64_t)vpl * kWave);
+    // Large batches: 7 vectors per lane (two wavefronts per 7168-wide row),
+    // one row in flight per wavefront (occupancy hides the latency; a second
+    // row's registers would halve it).  Small batches (few wavefronts): 1-2
+    // vectors per lane and eight rows in flight, so each wavefront does not
+    // wait on its token's rows one after another.
+    const int vpl_big = a.nv <= 64 ? 1 : a.nv <= 128 ? 2 : a.nv <= 256 ? 4 : a.nv <= 512 ? 8 : 7;
+    const int64_t waves_big = (int64_t)s.T * ceil_div(a.nv, (int64_t)vpl_big * kWave);
+    if (waves_big < kCombineSmallWaves) {
+        const int vpl = a.nv <= 64 ? 1 : 2;
+        a.nchunks = (int32_t)ceil_div(a.nv, (int64_t)vpl * kWave);
+        const int64_t waves = (int64_t)s.T * a.nchunks;
+        return vpl == 1 ? launch_combine<1, 8>(a, waves, stream)
+                        : launch_combine<2, 8>(a, waves, stream);
+    }
+    a.nchunks = (int32_t)ceil_div(a.nv, (int64_t)vpl_big * kWave);
     const int64_t waves = (int64_t)s.T * a.nchunks;
-    switch (vpl) {
-        case 1: return launch_combine<1>(a, waves, stream);
-        case 2: return launch_combine<2>(a, waves, stream);
-        case 4: return launch_combine<4>(a, waves, stream);
-        case 8: return launch_combine<8>(a, waves, stream);
-        default: return launch_combine<7>(a, waves, stream);
+    switch (vpl_big) {
+        case 1: return launch_combine<1, 4>(a, waves, stream);
+        case 2: return launch_combine<2, 4>(a, waves, stream);
+        case 4: return launch_combine<4, 2>(a, waves, stream);
+        case 8: return launch_combine<8, 1>(a, waves, stream);
+        default: return launch_combine<7, 1>(a, waves, stream);
     }
 }

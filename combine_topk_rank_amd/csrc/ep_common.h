@@ -56,8 +56,15 @@ struct RingDev {
 };
 
 // Carved workspace.
+// Workspace header: grid barrier words (256 B), then arrival counters, one
+// per 128-byte line (a top counter and 8 group counters).
+constexpr size_t kArriveStride = 32;   // words
+constexpr size_t kWsHeader = 256 + 16 * kArriveStride * 4;
+static_assert(kWsHeader % 256 == 0, "workspace sections stay 256-byte aligned");
+
 struct Workspace {
     uint32_t* barrier;        // [2] grid barrier: arrivals, generation (zero at first use)
+    uint32_t* arrive;         // [9 lines] dispatch arrival counters (zero between calls)
     int32_t* blk_rank_cnt;    // [NB, R] per-layout-block rank counts
     int32_t* blk_exp_cnt;     // [NB, E] per-layout-block expert counts
     int32_t* msg_base;        // [R+1]   first message index of each rank
@@ -126,6 +133,56 @@ __device__ inline float bcastf(float v, int l) {
 __device__ inline int lane_prefix(uint64_t m) {
     return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
                                           __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Wait until this wavefront's outstanding vector memory operations, stores
+// included, have completed (s_waitcnt vmcnt(0); gfx9 encoding with expcnt
+// and lgkmcnt left at their maxima).  A workgroup barrier does not wait for
+// stores, so a release fence executed by one wavefront after the barrier
+// covers another wavefront's stores only if that wavefront waited first.
+__device__ inline void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Grid-wide barrier for a grid whose workgroups are all resident: bar[0]
+// counts arrivals, bar[1] is a generation number.  Each workgroup reads the
+// generation before it arrives; the last arrival resets the count and bumps
+// the generation, which releases the others.  The words stay consistent from
+// one call to the next for any grid size (they start at zero).  The wait is
+// bounded by about a second of wall clock; on timeout the status is set and
+// false is returned.  Stores made before the barrier by any workgroup are
+// visible to loads made after it by every workgroup; with SYSTEM they are
+// also released at system scope (visible to other agents, e.g. a CPU or NIC).
+template <bool SYSTEM>
+__device__ bool grid_barrier(uint32_t* bar, uint32_t nblocks, int32_t* st) {
+    __shared__ int s_ok;
+    wait_vm();   // this workgroup's stores complete before thread 0 releases them
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int ok = 1;
+        if (SYSTEM)
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");
+        else
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        const uint32_t gen = __hip_atomic_load(&bar[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t old = atomicAdd(&bar[0], 1u);
+        if (old == nblocks - 1) {
+            atomicExch(&bar[0], 0u);
+            __hip_atomic_store(&bar[1], gen + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+            while (__hip_atomic_load(&bar[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gen) {
+                if (__builtin_amdgcn_s_memrealtime() - t0 > kBarrierTimeoutTicks) {
+                    set_error(st, EP_ERR_TIMEOUT);
+                    ok = 0;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        s_ok = ok;
+    }
+    __syncthreads();
+    return s_ok != 0;
 }
 
 }  // namespace ep

@@ -56,7 +56,8 @@ struct PackArgs {
     int32_t nv;                   // 16-byte vectors per x row (H/8)
     int32_t nchunks;              // wavefronts per token
     int32_t has_ring;
-    int64_t ngroups;              // groups of kPackWaves wavefronts
+    int64_t ngroups;              // groups of a workgroup's wavefronts (one per pass)
+    uint32_t* arrive;             // arrival counters (workspace, zero between calls)
 };
 
 // ------------------------------------------------------------------ ring
@@ -86,29 +87,40 @@ __device__ inline unsigned long long ring_reserve(const RingDev& g, int c, unsig
     return atomicAdd(g.head + (size_t)c * kPad, (unsigned long long)n);
 }
 
-// One command per lane (lanes with `have`): wait until the lane's ticket may
-// be written -- fewer than max_inflight commands of its channel published but
-// not yet drained -- write it, and release it at system scope.  The wait and the write share one
-// wave-uniform loop, so a lane whose ticket is ready writes at once even while
-// other lanes of the wavefront still wait (their tickets may wait on it).
-// A lane gives up when the ring's timeout passes (status set) or when another
-// producer has already failed.
-__device__ void ring_publish(const RingDev& g, bool have, int c, unsigned long long ticket,
-                             uint32_t type, uint32_t op, uint32_t ntok, uint32_t dst_rank,
-                             uint32_t size_val, uint64_t src_off, uint64_t dst_off, int32_t* st) {
-    if (!__ballot(have)) return;
+struct RingCmd {
+    uint32_t type, op, ntok, dst_rank, size_val;
+    uint64_t src_off, dst_off;
+};
+
+// Up to N commands per lane, all on the lane's channel c (the first n of
+// them, n <= N): wait until each ticket may be written -- fewer than
+// max_inflight commands of the channel published but not yet drained --
+// write it, and release it at system scope.  The waits and the writes share
+// one wave-uniform loop, so a command whose ticket is ready is written at once
+// even while other commands of the wavefront still wait (they may wait on
+// it).  A command is given up when the ring's timeout passes (status set) or
+// when another producer has already failed.
+template <int N>
+__device__ void ring_publish_n(const RingDev& g, int n, int c, const unsigned long long* ticket,
+                               const RingCmd* cmd, int32_t* st) {
+    if (!__ballot(n > 0)) return;
     const unsigned long long lim = (unsigned long long)g.max_inflight;
     unsigned long long* cache = g.tail_cache + (size_t)c * kPad;
     unsigned long long* poll = g.poll + (size_t)c * kPad;
     const unsigned long long* htail = g.host_tail + (size_t)c * kPad;
     unsigned long long seen = 0, t0 = 0;
-    bool pending = have;
+    uint32_t pending = (1u << n) - 1u;
     bool polled = false;
     if (pending) seen = __hip_atomic_load(cache, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    while (__ballot(pending)) {
+    while (__ballot(pending != 0)) {
         bool progress = false;
         if (pending) {
-            if (ticket >= seen + lim) {
+            // the lowest pending ticket decides whether the cache is refreshed
+            unsigned long long lo = ~0ull;
+#pragma unroll
+            for (int i = 0; i < N; ++i)
+                if (((pending >> i) & 1u) && ticket[i] < lo) lo = ticket[i];
+            if (lo >= seen + lim) {
                 // The cached consumer position says full.  One lane per
                 // channel at a time reads the real one over PCIe and
                 // refreshes the cache; the others read the cache.
@@ -122,20 +134,27 @@ __device__ void ring_publish(const RingDev& g, bool have, int c, unsigned long l
                     __hip_atomic_load(cache, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 if (cv > seen) seen = cv;
             }
-            if (ticket < seen + lim) {
-                ring_write(g, c, ticket, type, op, ntok, dst_rank, size_val, src_off, dst_off);
-                pending = false;
-                progress = true;
-            } else if (read_status(st) != 0) {
-                pending = false;
-            } else {
-                const unsigned long long now = __builtin_amdgcn_s_memrealtime();
-                if (!polled) {
-                    polled = true;
-                    t0 = now;
-                } else if (now - t0 > g.timeout_ticks) {
-                    set_error(st, EP_ERR_RING_TIMEOUT);
-                    pending = false;
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+                if (((pending >> i) & 1u) && ticket[i] < seen + lim) {
+                    ring_write(g, c, ticket[i], cmd[i].type, cmd[i].op, cmd[i].ntok,
+                               cmd[i].dst_rank, cmd[i].size_val, cmd[i].src_off, cmd[i].dst_off);
+                    pending &= ~(1u << i);
+                    progress = true;
+                }
+            }
+            if (pending && !progress) {
+                if (read_status(st) != 0) {
+                    pending = 0;
+                } else {
+                    const unsigned long long now = __builtin_amdgcn_s_memrealtime();
+                    if (!polled) {
+                        polled = true;
+                        t0 = now;
+                    } else if (now - t0 > g.timeout_ticks) {
+                        set_error(st, EP_ERR_RING_TIMEOUT);
+                        pending = 0;
+                    }
                 }
             }
         }
@@ -143,10 +162,19 @@ __device__ void ring_publish(const RingDev& g, bool have, int c, unsigned long l
             // one system-scope release pushes this round's slots out of the
             // L2 to host memory, where the proxy polls them
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");
-        } else if (__ballot(pending)) {
+        } else if (__ballot(pending != 0)) {
             __builtin_amdgcn_s_sleep(16);
         }
     }
+}
+
+// One command per lane (lanes with `have`).
+__device__ inline void ring_publish(const RingDev& g, bool have, int c, unsigned long long ticket,
+                                    uint32_t type, uint32_t op, uint32_t ntok, uint32_t dst_rank,
+                                    uint32_t size_val, uint64_t src_off, uint64_t dst_off,
+                                    int32_t* st) {
+    const RingCmd cmd{type, op, ntok, dst_rank, size_val, src_off, dst_off};
+    ring_publish_n<1>(g, have ? 1 : 0, c, &ticket, &cmd, st);
 }
 
 // ATOMIC{ADD, cnt} for ranks that receive no rows (nothing to order after).
@@ -192,36 +220,154 @@ __device__ void arrive_and_publish(const PackArgs& a, bool mine, int r, int32_t 
     if (!__ballot(pub)) return;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     const int c = r % a.ring.channels;
-    unsigned long long tk = 0;
-    bool ok = false;
-    if (pub) {
-        ok = read_status(a.st) == 0;
-        tk = ring_reserve(a.ring, c, 1);
-    }
-    const uint64_t rb = (uint64_t)a.row_bytes;
-    ring_publish(a.ring, pub && ok, c, tk, EP_CMD_WRITE, 0, (uint32_t)nrows, (uint32_t)r,
-                 (uint32_t)(nrows * rb), (uint64_t)(o + m * kMsgRows) * rb,
-                 (uint64_t)(m * kMsgRows) * rb, a.st);
-    // count the message into its rank only after its WRITE ticket exists: the
-    // added value depends on the ticket, so the two atomics cannot reorder
-    bool pub_a = false;
-    if (pub) {
+    unsigned long long tk[2] = {0, 0};
+    int ncmd = 0;
+    if (pub && read_status(a.st) == 0) {
+        tk[0] = ring_reserve(a.ring, c, 1);
+        ncmd = 1;
+        // Count the message into its rank once its WRITE ticket exists (the
+        // added value depends on the ticket, so the two atomics cannot
+        // reorder); the rank's last message reserves the ATOMIC's ticket,
+        // which then follows every WRITE ticket of the rank.
         const int32_t nmsgs = (cnt + kMsgRows - 1) / kMsgRows;
-        const int32_t one = 1 + (int32_t)(tk >> 62);
+        const int32_t one = 1 + (int32_t)(tk[0] >> 62);
         const int32_t done = atomicAdd(&a.rank_msgs_done[r], one);
         if (done == nmsgs - 1) {
-            pub_a = true;
             a.rank_msgs_done[r] = 0;
+            tk[1] = ring_reserve(a.ring, c, 1);
+            ncmd = 2;
         }
     }
-    unsigned long long tka = 0;
-    bool ok_a = false;
-    if (pub_a) {
-        ok_a = read_status(a.st) == 0;
-        tka = ring_reserve(a.ring, c, 1);
+    const uint64_t rb = (uint64_t)a.row_bytes;
+    const RingCmd cmd[2] = {
+        {EP_CMD_WRITE, 0, (uint32_t)nrows, (uint32_t)r, (uint32_t)(nrows * rb),
+         (uint64_t)(o + m * kMsgRows) * rb, (uint64_t)(m * kMsgRows) * rb},
+        {EP_CMD_ATOMIC, EP_ATOMIC_ADD, 0, (uint32_t)r, (uint32_t)cnt, 0, 0}};
+    ring_publish_n<2>(a.ring, ncmd, c, tk, cmd, a.st);
+}
+
+// Closed-form command stream (every row written and released first).  Per
+// channel c, its ranks r = c, c + C, ... ascending; per rank, the WRITEs of
+// its messages 0, 1, ..., then its ATOMIC (also for a rank with no rows).
+// The streams are concatenated channel-major; lane l of a wavefront takes
+// the l-th rank of that order (R <= 64).
+struct ClosedOrder {
+    int32_t r;        // rank at this lane's position (lanes < R)
+    int32_t c;        // its channel
+    int32_t o, cnt;   // its rows in the send buffer
+    int32_t items;    // its commands: ceil(cnt / 8) WRITEs + 1 ATOMIC
+    int32_t start;    // its first command in the concatenated order
+    int32_t cstart;   // first command of its channel
+    int32_t total;    // all commands (wave-uniform)
+};
+
+__device__ inline ClosedOrder closed_order(const PackArgs& a) {
+    const int lane = lane_id();
+    const int C = a.ring.channels, R = a.R;
+    const int q = R / C, rem = R % C;   // channels < rem hold q + 1 ranks
+    ClosedOrder z{};
+    int i = 0;
+    if (lane < R) {
+        if (lane < rem * (q + 1)) {
+            z.c = lane / (q + 1);
+            i = lane % (q + 1);
+        } else {
+            const int l2 = lane - rem * (q + 1);
+            z.c = rem + l2 / q;
+            i = l2 % q;
+        }
+        z.r = z.c + i * C;
+        z.o = a.rank_off[z.r];
+        z.cnt = a.rank_off[z.r + 1] - z.o;
+        z.items = (z.cnt + kMsgRows - 1) / kMsgRows + 1;
     }
-    ring_publish(a.ring, pub_a && ok_a, c, tka, EP_CMD_ATOMIC, EP_ATOMIC_ADD, 0, (uint32_t)r,
-                 (uint32_t)cnt, 0, 0, a.st);
+    int32_t incl = z.items;
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int32_t v = __shfl_up(incl, d);
+        if (lane >= d) incl += v;
+    }
+    z.start = incl - z.items;
+    z.cstart = __shfl(z.start, lane - i);   // the channel's first rank sits i lanes back
+    z.total = bcast(incl, kWave - 1);
+    return z;
+}
+
+// Publish commands [g0, g0 + 64) of the concatenated closed-form order;
+// base[c] is the first ticket of channel c.
+__device__ void closed_publish(const PackArgs& a, const ClosedOrder& z,
+                               const unsigned long long* base, int32_t g0) {
+    const int lane = lane_id();
+    const int32_t g = g0 + lane;
+    const bool have = g < z.total;
+    int j = 0;   // position holding command g
+    for (int p = 1; p < a.R; ++p)
+        if (bcast(z.start, p) <= g) j = p;
+    const int32_t local = g - __shfl(z.start, j);
+    const int32_t c = __shfl(z.c, j), r = __shfl(z.r, j);
+    const int32_t o = __shfl(z.o, j), cnt = __shfl(z.cnt, j);
+    const int32_t nmsg = __shfl(z.items, j) - 1;
+    const int32_t cstart = __shfl(z.cstart, j);
+    const unsigned long long ticket = have ? base[c] + (unsigned long long)(g - cstart) : 0;
+    const bool write = local < nmsg;
+    const int32_t rows = write ? min(kMsgRows, cnt - local * kMsgRows) : 0;
+    const uint64_t rb = (uint64_t)a.row_bytes;
+    ring_publish(a.ring, have, c, ticket, write ? EP_CMD_WRITE : EP_CMD_ATOMIC,
+                 write ? 0 : EP_ATOMIC_ADD, (uint32_t)rows, (uint32_t)r,
+                 write ? (uint32_t)(rows * rb) : (uint32_t)cnt,
+                 write ? (uint64_t)(o + local * kMsgRows) * rb : 0,
+                 write ? (uint64_t)(local * kMsgRows) * rb : 0, a.st);
+}
+
+// One ticket reservation per channel for all of its commands (wavefront-wide;
+// lane of a channel's first rank reserves), bases stored to base[c].
+__device__ void closed_reserve(const PackArgs& a, const ClosedOrder& z, unsigned long long* base) {
+    const int lane = lane_id();
+    const int C = a.ring.channels, R = a.R;
+    const int q = R / C, rem = R % C;
+    const int nr = z.c < rem ? q + 1 : q;   // ranks of this lane's channel
+    const int nxt = lane + nr;              // the next channel's first rank, if any
+    const int32_t nxt_start = __shfl(z.start, nxt < kWave ? nxt : kWave - 1);
+    if (lane < R && z.start == z.cstart) {   // lane of a channel's first rank
+        const int32_t n = (nxt < R ? nxt_start : z.total) - z.cstart;
+        base[z.c] = ring_reserve(a.ring, z.c, (unsigned)n);
+    }
+}
+
+// Count this workgroup out after its rows were released at system scope;
+// true in the last workgroup to finish.  Two levels spread the contention:
+// workgroups b = g (mod kArriveGroups) share counter g (consecutive
+// workgroups go to different XCDs, so a group tends to sit on one), and the
+// last of each group counts into the top counter.  Every counter is reset by
+// the arrival that completes it, so the words are zero between calls.
+constexpr int kArriveGroups = 8;
+__device__ bool arrive_last(uint32_t* ctr) {
+    const uint32_t nb = gridDim.x;
+    const uint32_t g = blockIdx.x % kArriveGroups;
+    const uint32_t ng = nb < kArriveGroups ? nb : kArriveGroups;   // groups in use
+    const uint32_t in_g = (nb - g + kArriveGroups - 1) / kArriveGroups;
+    uint32_t* cg = ctr + (size_t)(1 + g) * kArriveStride;
+    if (__hip_atomic_fetch_add(cg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != in_g - 1)
+        return false;
+    __hip_atomic_store(cg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // what the group's workgroups released is carried on to the top counter
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");
+    if (__hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != ng - 1)
+        return false;
+    __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    return true;
+}
+
+// Refresh the producers' cached consumer positions from host memory (one
+// PCIe read per channel), so that publication later in the kernel does not
+// find a stale "full" and wait for a read then.
+__device__ void refresh_tail_cache(const PackArgs& a) {
+    const int c = lane_id();
+    if (c < a.ring.channels) {
+        const unsigned long long h = __hip_atomic_load(a.ring.host_tail + (size_t)c * kPad,
+                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        atomicMax(a.ring.tail_cache + (size_t)c * kPad, h);
+    }
 }
 
 // ------------------------------------------------------------------ fp8
@@ -261,6 +407,10 @@ __device__ inline float group16_max(float v) {
 // their rows and one wavefront publishes their descriptors.
 constexpr int kPackWaves = 16;
 constexpr int kPackWavesFp8 = 8;
+// Below this many whole-chunk wavefronts, pack uses 2-vector chunks in
+// workgroups of kPackWavesSmall wavefronts.
+constexpr int64_t kPackSmallWaves = 1024;
+constexpr int kPackWavesSmall = 4;
 // Vectors per lane for rows of up to 896 vectors (H = 7168): 14 = one
 // wavefront per row, 7 = two.
 constexpr int kPackVplH7168 = 14;
@@ -271,7 +421,21 @@ constexpr int kPackVplFp8H7168 = 14;
 // Half the compute units already saturate HBM with 16 wavefronts each.
 constexpr int kPackGridPerCuNum = 1, kPackGridPerCuDen = 2;
 
-template <int VPL, int FMT, int WAVES>
+// How a pack kernel publishes descriptors.
+//   kPubNone:   no ring.
+//   kPubStream: as messages complete, overlapping the copy.  After each
+//     group, the workgroup's wavefronts hand their (slot, rank) pairs to
+//     wavefront 0 through LDS; it releases the group's rows at system scope,
+//     counts them into their messages' arrival counters, and the last
+//     arrival of a message publishes the WRITE (the last of a rank, also the
+//     rank's ATOMIC).
+//   kPubClosed (small batches): every workgroup writes and releases its
+//     rows and counts itself out; the last one to finish reserves each
+//     channel's tickets at once and publishes the whole command stream in
+//     closed form from the counts.  No per-message counters, no waiting.
+enum { kPubNone = 0, kPubStream = 1, kPubClosed = 2 };
+
+template <int VPL, int FMT, int WAVES, int PUB>
 __global__ __launch_bounds__(WAVES * kWave) void pack_kernel(PackArgs a) {
     constexpr int kWaves = WAVES;
     __shared__ int32_t s_pair_slot[kWaves][kMaxR];
@@ -283,8 +447,11 @@ __global__ __launch_bounds__(WAVES * kWave) void pack_kernel(PackArgs a) {
     const bool cap_ok = P <= a.cap;
     if (blockIdx.x == 0 && wave == 0) {
         if (!cap_ok && lane == 0) set_error(a.st, EP_ERR_CAPACITY);
-        if (a.has_ring && cap_ok) publish_empty_ranks(a);
+        if (PUB == kPubClosed) refresh_tail_cache(a);
     }
+    // stream publication runs when the ring exists and the rows fit
+    const bool streaming = PUB == kPubStream && cap_ok;
+    if (streaming && blockIdx.x == 0 && wave == 0) publish_empty_ranks(a);
     // groups of kWaves wavefronts, taken in launch order; a workgroup that
     // finishes a group (rows, then descriptors) moves on to the next one
     for (int64_t grp = blockIdx.x; grp < a.ngroups; grp += gridDim.x) {
@@ -298,6 +465,8 @@ __global__ __launch_bounds__(WAVES * kWave) void pack_kernel(PackArgs a) {
     if (active) {
         if (lane < a.R) s_lane = a.send_slot[t * a.R + lane];
         dmask = __ballot(s_lane >= 0);
+        if (PUB == kPubClosed && s_lane >= 0 && (s_lane < a.rank_off[lane] || s_lane >= a.rank_off[lane + 1]))
+            set_error(a.st, EP_ERR_INVALID_ARG);   // send_slot not from this rank_offset
 
         // load this wavefront's chunk of the row: vectors v0 + lane + 64 i
         const int v0 = chunk * VPL * kWave;
@@ -386,7 +555,7 @@ __global__ __launch_bounds__(WAVES * kWave) void pack_kernel(PackArgs a) {
         }
     }
 
-    if (!(a.has_ring && cap_ok)) continue;   // uniform over the workgroup
+    if (!streaming) continue;   // uniform over the workgroup
     // hand this wavefront's (slot, rank) pairs to wavefront 0
     if ((dmask >> lane) & 1ull) {
         const int j = lane_prefix(dmask);
@@ -394,11 +563,11 @@ __global__ __launch_bounds__(WAVES * kWave) void pack_kernel(PackArgs a) {
         s_pair_rank[wave][j] = lane;
     }
     if (lane == 0) s_npairs[wave] = (int32_t)__popcll(dmask);
+    wait_vm();   // the rows are complete before wavefront 0 releases them
     __syncthreads();
     if (wave == 0) {
         // One system-scope release for the rows and metadata of the whole
-        // group (ordered after the other wavefronts' stores by the barrier),
-        // then the arrivals and the descriptors.
+        // group, then the arrivals and the descriptors.
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");
         int total = 0;
 #pragma unroll
@@ -407,20 +576,41 @@ __global__ __launch_bounds__(WAVES * kWave) void pack_kernel(PackArgs a) {
             int p = base + lane;
             const bool mine = p < total;
             int r = 0;
-            int32_t s = 0;
+            int32_t sl = 0;
             if (mine) {
                 int w = 0;
                 while (p >= s_npairs[w]) {
                     p -= s_npairs[w];
                     ++w;
                 }
-                s = s_pair_slot[w][p];
+                sl = s_pair_slot[w][p];
                 r = s_pair_rank[w][p];
             }
-            arrive_and_publish(a, mine, r, s);
+            arrive_and_publish(a, mine, r, sl);
         }
     }
     __syncthreads();   // the pair lists are reused by the next group
+    }
+
+    if (PUB == kPubClosed) {
+        // The workgroup's rows go out at system scope; the last workgroup to
+        // finish then publishes every command.
+        __shared__ int s_last;
+        __shared__ unsigned long long s_base[kMaxR];
+        const ClosedOrder z = closed_order(a);   // loads issued before the wait
+        wait_vm();   // this wavefront's rows are complete
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");
+            // publish only if no error was raised: then no ticket is taken
+            s_last = arrive_last(a.arrive) && cap_ok && read_status(a.st) == 0;
+        }
+        __syncthreads();
+        if (!s_last) return;
+        if (wave == 0) closed_reserve(a, z, s_base);
+        __syncthreads();
+        for (int32_t g0 = wave * kWave; g0 < z.total; g0 += kWaves * kWave)
+            closed_publish(a, z, s_base, g0);
     }
 }
 
@@ -444,23 +634,51 @@ int64_t pack_grid_cap() {
     return cap;
 }
 
-template <int VPL>
-int launch_pack(PackArgs a, int fmt, int64_t waves, hipStream_t stream) {
-    // fp8 holds the codes and scales too: half the wavefronts per workgroup
-    // keep its registers (a 1024-thread workgroup caps a lane at 128)
-    const int wg_waves = fmt == EP_FMT_BF16 ? kPackWaves : kPackWavesFp8;
-    a.ngroups = ceil_div(waves, wg_waves);
-    const int64_t cap = pack_grid_cap() * (kPackWaves / wg_waves);
-    const int64_t blocks = a.ngroups < cap ? a.ngroups : cap;
+// SMALL: the small-batch configuration (closed-form publication).
+template <int VPL, int FMT, int WAVES, bool SMALL>
+int launch_pack_fmt(PackArgs a, int64_t waves, hipStream_t stream) {
+    const int pub = !a.has_ring ? kPubNone : SMALL ? kPubClosed : kPubStream;
+    a.ngroups = ceil_div(waves, WAVES);
+    // keep about the same number of wavefronts resident whatever WAVES is,
+    // and give every workgroup the same number of passes (+-1 group), so no
+    // few workgroups run a last pass alone
+    const int64_t cap = pack_grid_cap() * kPackWaves / WAVES;
+    const int64_t passes = ceil_div(a.ngroups, cap);
+    const int64_t blocks = ceil_div(a.ngroups, passes);
+    const dim3 grid((unsigned)blocks), block(WAVES * kWave);
     clear_hip_error();
-    if (fmt == EP_FMT_BF16)
-        hipLaunchKernelGGL((pack_kernel<VPL, EP_FMT_BF16, kPackWaves>), dim3((unsigned)blocks),
-                           dim3(kPackWaves * kWave), 0, stream, a);
+    if (pub == kPubNone)
+        hipLaunchKernelGGL((pack_kernel<VPL, FMT, WAVES, kPubNone>), grid, block, 0, stream, a);
+    else if (pub == kPubClosed)
+        hipLaunchKernelGGL((pack_kernel<VPL, FMT, WAVES, kPubClosed>), grid, block, 0, stream, a);
     else
-        hipLaunchKernelGGL((pack_kernel<VPL, EP_FMT_FP8_E4M3_B128, kPackWavesFp8>),
-                           dim3((unsigned)blocks), dim3(kPackWavesFp8 * kWave), 0, stream, a);
+        hipLaunchKernelGGL((pack_kernel<VPL, FMT, WAVES, kPubStream>), grid, block, 0, stream, a);
     EP_HIP_CHECK(hipGetLastError());
     return EP_OK;
+}
+
+template <int VPL, int WAVES, bool SMALL>
+int launch_pack_wg(const PackArgs& a, int fmt, int64_t waves, hipStream_t stream) {
+    if (fmt == EP_FMT_BF16)
+        return launch_pack_fmt<VPL, EP_FMT_BF16, WAVES, SMALL>(a, waves, stream);
+    return launch_pack_fmt<VPL, EP_FMT_FP8_E4M3_B128, WAVES, SMALL>(a, waves, stream);
+}
+
+template <int VPL>
+int launch_pack(const PackArgs& a, int fmt, int64_t waves, hipStream_t stream) {
+    // fp8 holds the codes and scales too: half the wavefronts per workgroup
+    // keep its registers (a 1024-thread workgroup caps a lane at 128)
+    if (fmt == EP_FMT_BF16) return launch_pack_wg<VPL, kPackWaves, false>(a, fmt, waves, stream);
+    return launch_pack_wg<VPL, kPackWavesFp8, false>(a, fmt, waves, stream);
+}
+
+// Small batches: short chunks and small workgroups spread the rows over the
+// chip (a large workgroup of whole-row wavefronts would sit on a few CUs),
+// and the descriptors go out in closed form at the end: with few rows, the
+// copy is short and the publication latency is what remains.
+template <int VPL>
+int launch_pack_small(const PackArgs& a, int fmt, int64_t waves, hipStream_t stream) {
+    return launch_pack_wg<VPL, kPackWavesSmall, true>(a, fmt, waves, stream);
 }
 
 }  // namespace
@@ -498,6 +716,7 @@ extern "C" int ep_dispatch(const ep_shape_t* shape, const void* x, const int32_t
     a.msg_arrivals = w.msg_arrivals;
     a.rank_msgs_done = w.rank_msgs_done;
     a.max_msgs = w.max_msgs;
+    a.arrive = w.arrive;
     a.st = dev_status;
     a.ring = ring_device_view(ring);
     a.has_ring = ring != nullptr;
@@ -523,9 +742,16 @@ extern "C" int ep_dispatch(const ep_shape_t* shape, const void* x, const int32_t
     else vpl = 16;
     a.nchunks = (int32_t)ceil_div(a.nv, (int64_t)vpl * kWave);
     int64_t waves = (int64_t)s.T * a.nchunks;
-    if (waves == 0) {
-        if (!a.has_ring) return EP_OK;
-        waves = 1;   // the zero-count ATOMICs still go out
+    if (waves < kPackSmallWaves) {
+        vpl = a.nv <= 64 ? 1 : 2;
+        a.nchunks = (int32_t)ceil_div(a.nv, (int64_t)vpl * kWave);
+        waves = (int64_t)s.T * a.nchunks;
+        if (waves == 0) {
+            if (!a.has_ring) return EP_OK;
+            waves = 1;   // the zero-count ATOMICs still go out
+        }
+        return vpl == 1 ? launch_pack_small<1>(a, s.fmt, waves, stream)
+                        : launch_pack_small<2>(a, s.fmt, waves, stream);
     }
     switch (vpl) {
         case 1: return launch_pack<1>(a, s.fmt, waves, stream);

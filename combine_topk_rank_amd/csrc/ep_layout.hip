@@ -167,43 +167,6 @@ __global__ __launch_bounds__(kBlock) void layout_count_kernel(
                   (int64_t)gridDim.x * kBlock);
 }
 
-// Grid-wide barrier for a grid whose workgroups are all resident: bar[0]
-// counts arrivals, bar[1] is a generation number.  Each workgroup reads the
-// generation before it arrives; the last arrival resets the count and bumps
-// the generation, which releases the others.  The words stay consistent from
-// one call to the next for any grid size (they start at zero).  The wait is
-// bounded by about a second of wall clock; on timeout the status is set and
-// false is returned.  Stores made before the barrier by any workgroup are
-// visible to loads made after it by every workgroup.
-__device__ bool grid_barrier(uint32_t* bar, uint32_t nblocks, int32_t* st) {
-    __shared__ int s_ok;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        int ok = 1;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        const uint32_t gen = __hip_atomic_load(&bar[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const uint32_t old = atomicAdd(&bar[0], 1u);
-        if (old == nblocks - 1) {
-            atomicExch(&bar[0], 0u);
-            __hip_atomic_store(&bar[1], gen + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        } else {
-            const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
-            while (__hip_atomic_load(&bar[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gen) {
-                if (__builtin_amdgcn_s_memrealtime() - t0 > kBarrierTimeoutTicks) {
-                    set_error(st, EP_ERR_TIMEOUT);
-                    ok = 0;
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(2);
-            }
-        }
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        s_ok = ok;
-    }
-    __syncthreads();
-    return s_ok != 0;
-}
-
 // MODE 0: one tile (the whole layout in one workgroup).
 // MODE 1: second pass after layout_count_kernel.
 // MODE 2: both passes in one kernel, the tiles meeting at a grid barrier
@@ -254,7 +217,7 @@ __global__ __launch_bounds__(kBlock) void layout_main_kernel(
         for (int e = tid; e < E; e += kBlock)
             blk_exp_cnt[(int64_t)b * E + e] = s_hist[e];
         zero_counters(counters, counters_n, (int64_t)b * kBlock + tid, (int64_t)gridDim.x * kBlock);
-        if (!grid_barrier(bar, (uint32_t)gridDim.x, st)) return;
+        if (!grid_barrier<false>(bar, (uint32_t)gridDim.x, st)) return;
     }
 
     // rank totals and the prefix over earlier tiles

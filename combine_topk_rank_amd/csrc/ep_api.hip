@@ -24,7 +24,7 @@ size_t row_bytes(int32_t H, int32_t fmt) {
 int validate_shape(const ep_shape_t* p) {
     if (!p) return EP_ERR_INVALID_ARG;
     const ep_shape_t& s = *p;
-    if (s.T < 0 || s.H < 8 || s.H % 8 != 0) return EP_ERR_INVALID_ARG;
+    if (s.T < 0 || s.H < 8 || s.H % 8 != 0 || s.H > kMaxH) return EP_ERR_INVALID_ARG;
     if (s.fmt != EP_FMT_BF16 && s.fmt != EP_FMT_FP8_E4M3_B128) return EP_ERR_INVALID_ARG;
     if (s.fmt == EP_FMT_FP8_E4M3_B128 && s.H % 512 != 0) return EP_ERR_INVALID_ARG;
     if (s.R < 1 || s.R > kMaxR || s.E < 1 || s.E > kMaxE || s.E % s.R != 0) return EP_ERR_INVALID_ARG;

@@ -16,7 +16,8 @@ constexpr int kLayoutTile = 256;   // tokens per layout workgroup
 constexpr int kMsgRows = 8;        // rows per WRITE message (UCCL-EP s4.1 packing, s5.3 batch 8)
 constexpr int kMaxR = 64;          // a rank set is one 64-bit mask
 constexpr int kMaxE = 4096;        // per-expert LDS histogram bound
-constexpr int kMaxK = 32;          // experts of a token sit in lanes 0..k-1
+constexpr int kMaxK = 32;
+constexpr int kMaxH = 1 << 24;        // rows stay far below 2^31 bytes (buffer records)          // experts of a token sit in lanes 0..k-1
 constexpr int kPad = 8;            // 64-byte stride between per-channel counters
 // Bound on a grid-barrier wait, in s_memrealtime ticks (100 MHz): one second.
 constexpr unsigned long long kBarrierTimeoutTicks = 100000000ull;
@@ -134,6 +135,20 @@ __device__ inline int lane_prefix(uint64_t m) {
     return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
                                           __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
+
+// Raw buffer resource over `bytes` bytes at p (the untyped-access word 3 of
+// CDNA3/CDNA4 buffer descriptors).  Buffer instructions drop accesses whose
+// offset falls outside [0, bytes).
+__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(void* p, int32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(p, 0, bytes, 0x00020000);
+}
+// Cache-policy bits of gfx94x/gfx950 buffer instructions.  A store with
+// sc0 sc1 has system scope: it is written through the L2 to memory and is
+// complete (vmcnt) only once it is coherent for every agent, so a completed
+// system-scope store needs no L2 write-back before another agent (a CPU, a
+// NIC reading over PCIe) may be told about it.  nt marks it streaming.
+constexpr int kCacheSc0 = 1, kCacheNt = 2, kCacheSc1 = 16;
+constexpr int kStoreSystem = kCacheSc0 | kCacheSc1;
 
 // Wait until this wavefront's outstanding vector memory operations, stores
 // included, have completed (s_waitcnt vmcnt(0); gfx9 encoding with expcnt

@@ -13,16 +13,23 @@
 //   s4.2 one FIFO per channel.
 //
 // Work decomposition (token-major): wavefront g handles chunk g % nchunks of
-// token g / nchunks.  It reads its chunk of x once (16-byte loads), and stores
+// token g / nchunks.  It reads its chunk of x once (16-byte loads) and stores
 // it to every destination slot of the token (16-byte stores; 8-byte stores of
-// codes for fp8), so x is read once and the packed rows written once.  A
-// message is the <= 8 consecutive rows [o_r + 8m, ...) of rank r; those rows
-// come from different tokens, hence different wavefronts.  Each wavefront
-// makes its stores visible system-wide (release fence) and then counts itself
-// into the message's arrival counter; the last arrival publishes the WRITE.
-// The last WRITE of a rank is followed by that rank's ATOMIC (its row count),
-// reserved after every WRITE ticket of the rank, so the proxy, which pops in
-// ticket order, sees the count after the rows.
+// codes for fp8), so x is read once and the packed rows written once.  Rows
+// are stored with system-scope stores, which are written through to memory:
+// once a wavefront's stores are complete, another agent (the NIC a proxy
+// drives, here the CPU) may read them.  A message is the <= 8 consecutive
+// rows [o_r + 8m, ...) of rank r; those rows come from different tokens.
+//
+// Large batches publish as messages complete.  Workgroups loop over groups
+// of consecutive wavefronts; after each group, wavefront 0 counts the group's
+// rows into their messages' arrival counters (one atomic per message and
+// group) and the last arrival of a message publishes its WRITE; the last
+// WRITE of a rank also publishes the rank's ATOMIC (its row count), whose
+// ticket is taken after every WRITE ticket of the rank, so the proxy, which
+// pops in ticket order, sees the count after the rows.  Small batches publish
+// in closed form: the last workgroup to finish emits every command from the
+// per-rank counts.
 
 #include "ep_common.h"
 
@@ -246,6 +253,100 @@ __device__ void arrive_and_publish(const PackArgs& a, bool mine, int r, int32_t 
     ring_publish_n<2>(a.ring, ncmd, c, tk, cmd, a.st);
 }
 
+// Wavefront 0 of a workgroup, after the rows of its current group (kWaves
+// consecutive wavefronts, hence consecutive tokens) are released: lane r
+// takes rank r.  slot[w][r] is the slot of rank r written by wavefront w of
+// the group (-1 for none).  The group's slots of rank r ascend with w and
+// are consecutive, so they fall into at most three consecutive messages;
+// each message gets one arrival atomic carrying the group's row count (x
+// chunks).  A message whose count completes is published (WRITE); the
+// rank's last message also publishes the rank's ATOMIC.  One publish round
+// (one release) per group.
+template <int W>
+__device__ void publish_group(const PackArgs& a, const int32_t (*slot)[kMaxR]) {
+    const int lane = lane_id();
+    const bool has = lane < a.R;
+    int32_t o = 0, cnt = 0, mbase = 0;
+    if (has) {
+        o = a.rank_off[lane];
+        cnt = a.rank_off[lane + 1] - o;
+        mbase = a.msg_base[lane];
+    }
+    int32_t done_m[3];
+    int ndone = 0;
+    bool bad = false;
+    int32_t cur = -1, run = 0;
+    auto flush = [&]() {
+        const int32_t gm = mbase + cur;
+        if (cur < 0 || gm >= a.max_msgs) {
+            bad = true;
+            return;
+        }
+        const int32_t nrows = min(kMsgRows, cnt - cur * kMsgRows);
+        const int32_t old = atomicAdd(&a.msg_arrivals[gm], run);
+        if (old + run == nrows * a.nchunks) {
+            a.msg_arrivals[gm] = 0;   // every arrival is in: leave the counter clean
+            if (ndone < 3) done_m[ndone++] = cur;
+            else bad = true;
+        }
+    };
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+        const int32_t sl = has ? slot[w][lane] : -1;
+        if (sl >= 0) {
+            if (sl < o || sl >= o + cnt) {
+                bad = true;   // send_slot does not belong to rank_offset
+            } else {
+                const int32_t m = (sl - o) / kMsgRows;
+                if (m != cur) {
+                    if (run) flush();
+                    cur = m;
+                    run = 0;
+                }
+                ++run;
+            }
+        }
+    }
+    if (run) flush();
+    if (bad) set_error(a.st, EP_ERR_INVALID_ARG);
+    if (!__ballot(ndone > 0)) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    const int c = lane % a.ring.channels;
+    unsigned long long tk[4] = {0, 0, 0, 0};
+    int ncmd = 0;
+    if (ndone > 0 && read_status(a.st) == 0) {
+        const unsigned long long t0 = ring_reserve(a.ring, c, (unsigned)ndone);
+        for (int i = 0; i < ndone; ++i) tk[i] = t0 + i;
+        ncmd = ndone;
+        // Count the messages into the rank once their WRITE tickets exist (the
+        // added value depends on the ticket); the rank's last messages
+        // reserve the ATOMIC's ticket, which then follows every WRITE ticket
+        // of the rank.
+        const int32_t nmsgs = (cnt + kMsgRows - 1) / kMsgRows;
+        const int32_t add = ndone + (int32_t)(t0 >> 62);
+        const int32_t done = atomicAdd(&a.rank_msgs_done[lane], add);
+        if (done + ndone == nmsgs) {
+            a.rank_msgs_done[lane] = 0;
+            tk[ncmd++] = ring_reserve(a.ring, c, 1);
+        }
+    }
+    const uint64_t rb = (uint64_t)a.row_bytes;
+    RingCmd cmd[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (i < ndone) {
+            const int32_t m = done_m[i < 3 ? i : 0];
+            const int32_t nrows = min(kMsgRows, cnt - m * kMsgRows);
+            cmd[i] = RingCmd{EP_CMD_WRITE, 0, (uint32_t)nrows, (uint32_t)lane,
+                             (uint32_t)(nrows * rb), (uint64_t)(o + m * kMsgRows) * rb,
+                             (uint64_t)(m * kMsgRows) * rb};
+        } else {
+            cmd[i] = RingCmd{EP_CMD_ATOMIC, EP_ATOMIC_ADD, 0, (uint32_t)lane, (uint32_t)cnt, 0, 0};
+        }
+    }
+    ring_publish_n<4>(a.ring, ncmd, c, tk, cmd, a.st);
+}
+
 // Closed-form command stream (every row written and released first).  Per
 // channel c, its ranks r = c, c + C, ... ascending; per rank, the WRITEs of
 // its messages 0, 1, ..., then its ATOMIC (also for a rank with no rows).
@@ -438,9 +539,8 @@ enum { kPubNone = 0, kPubStream = 1, kPubClosed = 2 };
 template <int VPL, int FMT, int WAVES, int PUB>
 __global__ __launch_bounds__(WAVES * kWave) void pack_kernel(PackArgs a) {
     constexpr int kWaves = WAVES;
-    __shared__ int32_t s_pair_slot[kWaves][kMaxR];
-    __shared__ int32_t s_pair_rank[kWaves][kMaxR];
-    __shared__ int32_t s_npairs[kWaves];
+    // group's slot of rank r per wavefront, two buffers by pass parity
+    __shared__ int32_t s_slot[2][kWaves][kMaxR];
     const int lane = lane_id();
     const int wave = (int)(threadIdx.x / kWave);
     const int64_t P = a.rank_off[a.R];
@@ -454,7 +554,8 @@ __global__ __launch_bounds__(WAVES * kWave) void pack_kernel(PackArgs a) {
     if (streaming && blockIdx.x == 0 && wave == 0) publish_empty_ranks(a);
     // groups of kWaves wavefronts, taken in launch order; a workgroup that
     // finishes a group (rows, then descriptors) moves on to the next one
-    for (int64_t grp = blockIdx.x; grp < a.ngroups; grp += gridDim.x) {
+    int pass = 0;
+    for (int64_t grp = blockIdx.x; grp < a.ngroups; grp += gridDim.x, pass ^= 1) {
     const int64_t gw = grp * kWaves + wave;
     const int64_t t = gw / a.nchunks;
     const int chunk = (int)(gw - t * a.nchunks);
@@ -484,11 +585,14 @@ __global__ __launch_bounds__(WAVES * kWave) void pack_kernel(PackArgs a) {
                 const int r = __builtin_ctzll(m);
                 const int32_t s = bcast(s_lane, r);
                 if (s >= a.cap) continue;
-                u32x4* dst = reinterpret_cast<u32x4*>(a.send_buf + (int64_t)s * a.row_bytes);
+                const __amdgpu_buffer_rsrc_t dst =
+                    buffer_rsrc(a.send_buf + (int64_t)s * a.row_bytes, (int32_t)a.row_bytes);
 #pragma unroll
                 for (int i = 0; i < VPL; ++i) {
                     int vi = v0 + lane + i * kWave;
-                    if (vi < a.nv) __builtin_nontemporal_store(v[i], dst + vi);
+                    if (vi < a.nv)
+                        __builtin_amdgcn_raw_buffer_store_b128(v[i], dst, vi * 16, 0,
+                                                               kStoreSystem | kCacheNt);
                 }
             }
         } else {
@@ -519,15 +623,17 @@ __global__ __launch_bounds__(WAVES * kWave) void pack_kernel(PackArgs a) {
                 const int r = __builtin_ctzll(m);
                 const int32_t s = bcast(s_lane, r);
                 if (s >= a.cap) continue;
-                uint8_t* row = a.send_buf + (int64_t)s * a.row_bytes;
-                u32x2* codes = reinterpret_cast<u32x2*>(row);
-                float* scales = reinterpret_cast<float*>(row + a.H);
+                // codes at [0, H), scales at [H, H + H/32)
+                const __amdgpu_buffer_rsrc_t row =
+                    buffer_rsrc(a.send_buf + (int64_t)s * a.row_bytes, (int32_t)a.row_bytes);
 #pragma unroll
                 for (int i = 0; i < VPL; ++i) {
                     int vi = v0 + lane + i * kWave;
                     if (vi < a.nv) {
-                        __builtin_nontemporal_store(q[i], codes + vi);
-                        if ((lane & 15) == 0) __builtin_nontemporal_store(scale[i], scales + vi / 16);
+                        __builtin_amdgcn_raw_buffer_store_b64(q[i], row, vi * 8, 0, kStoreSystem);
+                        if ((lane & 15) == 0)
+                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(scale[i]), row,
+                                                                  a.H + vi / 16 * 4, 0, kStoreSystem);
                     }
                 }
             }
@@ -556,52 +662,31 @@ __global__ __launch_bounds__(WAVES * kWave) void pack_kernel(PackArgs a) {
     }
 
     if (!streaming) continue;   // uniform over the workgroup
-    // hand this wavefront's (slot, rank) pairs to wavefront 0
-    if ((dmask >> lane) & 1ull) {
-        const int j = lane_prefix(dmask);
-        s_pair_slot[wave][j] = s_lane;
-        s_pair_rank[wave][j] = lane;
-    }
-    if (lane == 0) s_npairs[wave] = (int32_t)__popcll(dmask);
-    wait_vm();   // the rows are complete before wavefront 0 releases them
+    // hand this wavefront's slots (rank r on lane r) to wavefront 0
+    if (lane < a.R) s_slot[pass][wave][lane] = s_lane;
+    // The rows went out with system-scope stores: once complete they are
+    // visible to every agent, so no write-back precedes the arrivals.
+    wait_vm();
     __syncthreads();
     if (wave == 0) {
-        // One system-scope release for the rows and metadata of the whole
-        // group, then the arrivals and the descriptors.
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");
-        int total = 0;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) total += s_npairs[w];
-        for (int base = 0; base < total; base += kWave) {
-            int p = base + lane;
-            const bool mine = p < total;
-            int r = 0;
-            int32_t sl = 0;
-            if (mine) {
-                int w = 0;
-                while (p >= s_npairs[w]) {
-                    p -= s_npairs[w];
-                    ++w;
-                }
-                sl = s_pair_slot[w][p];
-                r = s_pair_rank[w][p];
-            }
-            arrive_and_publish(a, mine, r, sl);
-        }
+        // The arrivals and the descriptors of the group.  Meanwhile the
+        // other wavefronts go on with the next group, whose slots go to the
+        // other buffer; this one is written again only after the next
+        // barrier, which wavefront 0 reaches once it is done here.
+        publish_group<kWaves>(a, s_slot[pass]);
     }
-    __syncthreads();   // the pair lists are reused by the next group
     }
 
     if (PUB == kPubClosed) {
-        // The workgroup's rows go out at system scope; the last workgroup to
-        // finish then publishes every command.
+        // Once its system-scope row stores are complete, the workgroup
+        // counts itself out; the last workgroup to finish then publishes
+        // every command.
         __shared__ int s_last;
         __shared__ unsigned long long s_base[kMaxR];
         const ClosedOrder z = closed_order(a);   // loads issued before the wait
         wait_vm();   // this wavefront's rows are complete
         __syncthreads();
         if (threadIdx.x == 0) {
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");
             // publish only if no error was raised: then no ticket is taken
             s_last = arrive_last(a.arrive) && cap_ok && read_status(a.st) == 0;
         }

@@ -11,7 +11,7 @@ import pytest
 import oracle
 import oracle_pins as pins
 import workloads as W
-from gpu_helpers import (assert_descriptors, assert_layout_equal, assert_pack_equal,
+from gpu_helpers import (assert_descriptors, cmd_key, assert_layout_equal, assert_pack_equal,
                          combine_tolerance_check, log, run_hip, run_hip_combine)
 
 pytestmark = pytest.mark.gpu
@@ -194,3 +194,51 @@ def test_layout_more_tiles_than_resident():
     g = run_hip(T, 8, E, R, k, 0, x, idx, w, capacity_rows=1, ring_cfg=None)
     assert g["status"] in (0, 3)   # capacity 1 row: the pack reports it, layout is intact
     assert_layout_equal(g, L)
+
+
+def _channel_streams(log_, channels):
+    """Per channel, the logged commands in ticket order."""
+    by_ch = {}
+    for d in sorted(log_, key=lambda d: int(d["seq"])):
+        by_ch.setdefault(int(d["dst_rank"]) % channels, []).append(d)
+    return by_ch
+
+
+# (T, H, E, R, k, channels, depth, max_inflight, small): a small batch (100
+# one-wavefront rows), published in closed form after the copy, and a large
+# one (4096 rows), published as messages complete
+REPEAT_CASES = [
+    (100, 512, 64, 16, 4, 5, 16, 4, True),
+    (4096, 512, 64, 16, 4, 5, 64, 16, False),
+]
+
+
+@pytest.mark.parametrize("case", REPEAT_CASES, ids=lambda c: "T%d_C%d_inflight%d" % (c[0], c[5], c[7]))
+def test_repeated_dispatch_on_one_ring(case):
+    """Three layout + dispatch calls on one ring with a small in-flight window:
+    every call's commands arrive, tickets stay consecutive across calls, and
+    every call's ATOMIC of a rank follows that call's WRITEs.  The small
+    batch's stream matches the closed form command for command, in order."""
+    T, H, E, R, k, C, depth, mif, small = case
+    rng = np.random.default_rng(77 + T)
+    inp = W.make_random_case(rng, T, H, E, R, k, drop_prob=0.1)
+    L = oracle.layout(inp["topk_idx"], E, R)
+    want = oracle.descriptors(L["num_tokens_per_rank"], L["rank_offset"], oracle.row_bytes(H, 0), C)
+    log(f"[parity] repeated dispatch {case}")
+    g = run_hip(T, H, E, R, k, 0, inp["x"], inp["topk_idx"], inp["topk_w"],
+                capacity_rows=L["P"], ring_cfg=(depth, C, mif, RING_TIMEOUT_NS), repeat=3)
+    assert g["status"] == 0
+    lg, nd = g["logs"][0]
+    assert nd == 3 * len(want)
+    streams = _channel_streams(lg, C)
+    for c in range(C):
+        got_c = streams.get(c, [])
+        exp_c = [d for d in want if int(d["dst_rank"]) % C == c]
+        n = len(exp_c)
+        assert len(got_c) == 3 * n
+        assert [int(d["seq"]) for d in got_c] == list(range(1, 3 * n + 1))
+        for call in range(3):
+            part = got_c[call * n:(call + 1) * n]
+            assert_descriptors(part, exp_c, C)
+            if small:   # closed form: exact order
+                assert [cmd_key(d) for d in part] == [cmd_key(d) for d in exp_c]

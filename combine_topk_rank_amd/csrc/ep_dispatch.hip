@@ -69,11 +69,13 @@ struct PackArgs {
 
 // ------------------------------------------------------------------ ring
 
-// Write one command into its slot: four tagged 8-byte words in two plain
-// 16-byte stores.  The caller makes them visible to the CPU with one
-// system-scope release per round of writes (see ring_publish); the tags make
-// the order in which the words land irrelevant.  The rows the command points
-// to were released at system scope before the command's ticket was taken.
+// Write one command into its slot: four tagged 8-byte words in two 16-byte
+// stores; the tags make the order in which the words land irrelevant.  With
+// SYS the stores have system scope and go through to host memory by
+// themselves; otherwise they are cached and the caller releases each round
+// of writes at system scope (see ring_publish_n).  The rows the command
+// points to were complete at system scope before its ticket was taken.
+template <bool SYS>
 __device__ inline void ring_write(const RingDev& g, int c, unsigned long long ticket, uint32_t type,
                                   uint32_t op, uint32_t ntok, uint32_t dst_rank, uint32_t size_val,
                                   uint64_t src_off, uint64_t dst_off) {
@@ -84,9 +86,17 @@ __device__ inline void ring_write(const RingDev& g, int c, unsigned long long ti
     const uint64_t w1 = tag | ((uint64_t)(dst_rank & 0xFFFF) << 16) | ((uint64_t)size_val << 32);
     const uint64_t w2 = tag | ((src_off & kMaxRingOffset) << 16);
     const uint64_t w3 = tag | ((dst_off & kMaxRingOffset) << 16);
-    u64x2* p = reinterpret_cast<u64x2*>(slot);
-    p[0] = u64x2{w0, w1};
-    p[1] = u64x2{w2, w3};
+    if (SYS) {
+        const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(slot, (int32_t)sizeof(RingSlot));
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, (u64x2{w0, w1})), rs, 0,
+                                               0, kStoreSystem);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, (u64x2{w2, w3})), rs, 16,
+                                               0, kStoreSystem);
+    } else {
+        u64x2* p = reinterpret_cast<u64x2*>(slot);
+        p[0] = u64x2{w0, w1};
+        p[1] = u64x2{w2, w3};
+    }
 }
 
 // Reserve n consecutive tickets on channel c (one atomic per reservation).
@@ -102,12 +112,15 @@ struct RingCmd {
 // Up to N commands per lane, all on the lane's channel c (the first n of
 // them, n <= N): wait until each ticket may be written -- fewer than
 // max_inflight commands of the channel published but not yet drained --
-// write it, and release it at system scope.  The waits and the writes share
+// write it, and make it visible to the CPU.  The waits and the writes share
 // one wave-uniform loop, so a command whose ticket is ready is written at once
 // even while other commands of the wavefront still wait (they may wait on
 // it).  A command is given up when the ring's timeout passes (status set) or
-// when another producer has already failed.
-template <int N>
+// when another producer has already failed.  SYS: system-scope slot stores
+// (best for a few commands per wavefront: each lane's 16-byte stores travel
+// on their own); otherwise cached stores and one system-scope release per
+// round (best for runs of consecutive slots, which leave the L2 as lines).
+template <int N, bool SYS>
 __device__ void ring_publish_n(const RingDev& g, int n, int c, const unsigned long long* ticket,
                                const RingCmd* cmd, int32_t* st) {
     if (!__ballot(n > 0)) return;
@@ -144,8 +157,9 @@ __device__ void ring_publish_n(const RingDev& g, int n, int c, const unsigned lo
 #pragma unroll
             for (int i = 0; i < N; ++i) {
                 if (((pending >> i) & 1u) && ticket[i] < seen + lim) {
-                    ring_write(g, c, ticket[i], cmd[i].type, cmd[i].op, cmd[i].ntok,
-                               cmd[i].dst_rank, cmd[i].size_val, cmd[i].src_off, cmd[i].dst_off);
+                    ring_write<SYS>(g, c, ticket[i], cmd[i].type, cmd[i].op, cmd[i].ntok,
+                                    cmd[i].dst_rank, cmd[i].size_val, cmd[i].src_off,
+                                    cmd[i].dst_off);
                     pending &= ~(1u << i);
                     progress = true;
                 }
@@ -168,7 +182,7 @@ __device__ void ring_publish_n(const RingDev& g, int n, int c, const unsigned lo
         if (__ballot(progress)) {
             // one system-scope release pushes this round's slots out of the
             // L2 to host memory, where the proxy polls them
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");
+            if (!SYS) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");
         } else if (__ballot(pending != 0)) {
             __builtin_amdgcn_s_sleep(16);
         }
@@ -176,12 +190,13 @@ __device__ void ring_publish_n(const RingDev& g, int n, int c, const unsigned lo
 }
 
 // One command per lane (lanes with `have`).
+template <bool SYS>
 __device__ inline void ring_publish(const RingDev& g, bool have, int c, unsigned long long ticket,
                                     uint32_t type, uint32_t op, uint32_t ntok, uint32_t dst_rank,
                                     uint32_t size_val, uint64_t src_off, uint64_t dst_off,
                                     int32_t* st) {
     const RingCmd cmd{type, op, ntok, dst_rank, size_val, src_off, dst_off};
-    ring_publish_n<1>(g, have ? 1 : 0, c, &ticket, &cmd, st);
+    ring_publish_n<1, SYS>(g, have ? 1 : 0, c, &ticket, &cmd, st);
 }
 
 // ATOMIC{ADD, cnt} for ranks that receive no rows (nothing to order after).
@@ -195,62 +210,8 @@ __device__ void publish_empty_ranks(const PackArgs& a) {
         c = lane % a.ring.channels;
         tk = ring_reserve(a.ring, c, 1);
     }
-    ring_publish(a.ring, have, c, tk, EP_CMD_ATOMIC, EP_ATOMIC_ADD, 0, (uint32_t)lane, 0, 0, 0,
-                 a.st);
-}
-
-// Lane r of a wavefront that wrote (one chunk of) the row in slot s of rank r
-// (`mine`), after the wavefront's release fence: count the row into its
-// message; the last arrival of a message publishes the WRITE, and the last
-// WRITE of a rank is followed by the rank's ATOMIC.  All lanes of the
-// wavefront call this together.
-__device__ void arrive_and_publish(const PackArgs& a, bool mine, int r, int32_t s) {
-    bool pub = false;
-    int32_t o = 0, cnt = 0, m = 0, nrows = 0;
-    if (mine) {
-        o = a.rank_off[r];
-        cnt = a.rank_off[r + 1] - o;
-        m = (s - o) / kMsgRows;
-        nrows = min(kMsgRows, cnt - m * kMsgRows);
-        const int32_t gm = a.msg_base[r] + m;
-        if (s < o || s >= o + cnt || gm < 0 || gm >= a.max_msgs) {
-            // send_slot does not belong to rank_offset: not from the same layout
-            set_error(a.st, EP_ERR_INVALID_ARG);
-        } else {
-            const int32_t old = atomicAdd(&a.msg_arrivals[gm], 1);
-            if (old == nrows * a.nchunks - 1) {
-                pub = true;
-                a.msg_arrivals[gm] = 0;   // every arrival is in: leave the counter clean
-            }
-        }
-    }
-    if (!__ballot(pub)) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    const int c = r % a.ring.channels;
-    unsigned long long tk[2] = {0, 0};
-    int ncmd = 0;
-    if (pub && read_status(a.st) == 0) {
-        tk[0] = ring_reserve(a.ring, c, 1);
-        ncmd = 1;
-        // Count the message into its rank once its WRITE ticket exists (the
-        // added value depends on the ticket, so the two atomics cannot
-        // reorder); the rank's last message reserves the ATOMIC's ticket,
-        // which then follows every WRITE ticket of the rank.
-        const int32_t nmsgs = (cnt + kMsgRows - 1) / kMsgRows;
-        const int32_t one = 1 + (int32_t)(tk[0] >> 62);
-        const int32_t done = atomicAdd(&a.rank_msgs_done[r], one);
-        if (done == nmsgs - 1) {
-            a.rank_msgs_done[r] = 0;
-            tk[1] = ring_reserve(a.ring, c, 1);
-            ncmd = 2;
-        }
-    }
-    const uint64_t rb = (uint64_t)a.row_bytes;
-    const RingCmd cmd[2] = {
-        {EP_CMD_WRITE, 0, (uint32_t)nrows, (uint32_t)r, (uint32_t)(nrows * rb),
-         (uint64_t)(o + m * kMsgRows) * rb, (uint64_t)(m * kMsgRows) * rb},
-        {EP_CMD_ATOMIC, EP_ATOMIC_ADD, 0, (uint32_t)r, (uint32_t)cnt, 0, 0}};
-    ring_publish_n<2>(a.ring, ncmd, c, tk, cmd, a.st);
+    ring_publish<true>(a.ring, have, c, tk, EP_CMD_ATOMIC, EP_ATOMIC_ADD, 0, (uint32_t)lane, 0, 0,
+                       0, a.st);
 }
 
 // Wavefront 0 of a workgroup, after the rows of its current group (kWaves
@@ -272,24 +233,9 @@ __device__ void publish_group(const PackArgs& a, const int32_t (*slot)[kMaxR]) {
         cnt = a.rank_off[lane + 1] - o;
         mbase = a.msg_base[lane];
     }
-    int32_t done_m[3];
-    int ndone = 0;
+    // rows per message, relative to the first message m0 the group touches
+    int32_t m0 = -1, cnt3[3] = {0, 0, 0};
     bool bad = false;
-    int32_t cur = -1, run = 0;
-    auto flush = [&]() {
-        const int32_t gm = mbase + cur;
-        if (cur < 0 || gm >= a.max_msgs) {
-            bad = true;
-            return;
-        }
-        const int32_t nrows = min(kMsgRows, cnt - cur * kMsgRows);
-        const int32_t old = atomicAdd(&a.msg_arrivals[gm], run);
-        if (old + run == nrows * a.nchunks) {
-            a.msg_arrivals[gm] = 0;   // every arrival is in: leave the counter clean
-            if (ndone < 3) done_m[ndone++] = cur;
-            else bad = true;
-        }
-    };
 #pragma unroll
     for (int w = 0; w < W; ++w) {
         const int32_t sl = has ? slot[w][lane] : -1;
@@ -298,16 +244,39 @@ __device__ void publish_group(const PackArgs& a, const int32_t (*slot)[kMaxR]) {
                 bad = true;   // send_slot does not belong to rank_offset
             } else {
                 const int32_t m = (sl - o) / kMsgRows;
-                if (m != cur) {
-                    if (run) flush();
-                    cur = m;
-                    run = 0;
-                }
-                ++run;
+                if (m0 < 0) m0 = m;
+                const int32_t d = m - m0;
+                if (d == 0) ++cnt3[0];
+                else if (d == 1) ++cnt3[1];
+                else if (d == 2) ++cnt3[2];
+                else bad = true;   // slots of a rank not ascending through the group
             }
         }
     }
-    if (run) flush();
+    // the (at most three) arrival atomics go out together: one latency
+    int32_t old3[3] = {0, 0, 0};
+    bool hit[3];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        hit[i] = m0 >= 0 && cnt3[i] > 0;
+        if (hit[i] && mbase + m0 + i >= a.max_msgs) {
+            hit[i] = false;   // message table too small: not from this layout
+            bad = true;
+        }
+        if (hit[i]) old3[i] = atomicAdd(&a.msg_arrivals[mbase + m0 + i], cnt3[i]);
+    }
+    int32_t done_m[3];
+    int ndone = 0;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        if (!hit[i]) continue;
+        const int32_t m = m0 + i;
+        const int32_t nrows = min(kMsgRows, cnt - m * kMsgRows);
+        if (old3[i] + cnt3[i] == nrows * a.nchunks) {
+            a.msg_arrivals[mbase + m] = 0;   // every arrival is in: leave the counter clean
+            done_m[ndone++] = m;
+        }
+    }
     if (bad) set_error(a.st, EP_ERR_INVALID_ARG);
     if (!__ballot(ndone > 0)) return;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
@@ -344,7 +313,7 @@ __device__ void publish_group(const PackArgs& a, const int32_t (*slot)[kMaxR]) {
             cmd[i] = RingCmd{EP_CMD_ATOMIC, EP_ATOMIC_ADD, 0, (uint32_t)lane, (uint32_t)cnt, 0, 0};
         }
     }
-    ring_publish_n<4>(a.ring, ncmd, c, tk, cmd, a.st);
+    ring_publish_n<4, true>(a.ring, ncmd, c, tk, cmd, a.st);
 }
 
 // Closed-form command stream (every row written and released first).  Per
@@ -412,11 +381,11 @@ __device__ void closed_publish(const PackArgs& a, const ClosedOrder& z,
     const bool write = local < nmsg;
     const int32_t rows = write ? min(kMsgRows, cnt - local * kMsgRows) : 0;
     const uint64_t rb = (uint64_t)a.row_bytes;
-    ring_publish(a.ring, have, c, ticket, write ? EP_CMD_WRITE : EP_CMD_ATOMIC,
-                 write ? 0 : EP_ATOMIC_ADD, (uint32_t)rows, (uint32_t)r,
-                 write ? (uint32_t)(rows * rb) : (uint32_t)cnt,
-                 write ? (uint64_t)(o + local * kMsgRows) * rb : 0,
-                 write ? (uint64_t)(local * kMsgRows) * rb : 0, a.st);
+    ring_publish<false>(a.ring, have, c, ticket, write ? EP_CMD_WRITE : EP_CMD_ATOMIC,
+                        write ? 0 : EP_ATOMIC_ADD, (uint32_t)rows, (uint32_t)r,
+                        write ? (uint32_t)(rows * rb) : (uint32_t)cnt,
+                        write ? (uint64_t)(o + local * kMsgRows) * rb : 0,
+                        write ? (uint64_t)(local * kMsgRows) * rb : 0, a.st);
 }
 
 // One ticket reservation per channel for all of its commands (wavefront-wide;

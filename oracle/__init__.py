@@ -86,6 +86,14 @@ class Oracle:
         L.oracle_descriptors.restype = i64
         L.oracle_combine.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P]
         L.oracle_combine.restype = None
+        L.oracle_ll_layout.argtypes = [i32, i32, i32, P, P, P, P]
+        L.oracle_ll_layout.restype = i32
+        L.oracle_ll_pack.argtypes = [i32, i32, i32, i32, P, P, P, P, i64, P, P]
+        L.oracle_ll_pack.restype = i32
+        L.oracle_ll_descriptors.argtypes = [i32, i32, i32, P, P, i64, P, i64]
+        L.oracle_ll_descriptors.restype = i64
+        L.oracle_ll_combine.argtypes = [i32, i32, i32, P, P, P, P, P]
+        L.oracle_ll_combine.restype = None
         self.L = L
         self.path = path
 
@@ -178,6 +186,68 @@ class Oracle:
             self.L.oracle_combine(T, H, E, R, k, _p(y), _p(idx), _p(w), _p(ss), _p(out))
         return out
 
+    # ---------------------------------------------------------- per-expert mode
+    def ll_layout(self, topk_idx: np.ndarray, E: int) -> dict:
+        """Per-expert counts, offsets and the row of every kept choice."""
+        idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+        T, k = idx.shape
+        out = {
+            "num_tokens_per_expert": np.zeros(E, np.int32),
+            "expert_offset": np.zeros(E + 1, np.int32),
+            "expert_slot": np.zeros((T, k), np.int32),
+        }
+        st = self.L.oracle_ll_layout(T, E, k, _p(idx), _p(out["num_tokens_per_expert"]),
+                                     _p(out["expert_offset"]), _p(out["expert_slot"]))
+        out["status"] = int(st)
+        out["Q"] = int(out["expert_offset"][E])
+        return out
+
+    def ll_pack(self, x: np.ndarray, topk_w: np.ndarray, expert_slot: np.ndarray, fmt: int,
+                capacity_rows: int, poison: int = 0xA5) -> dict:
+        """Pack one row per kept choice into the per-expert send buffer, with
+        slot_src / slot_w metadata (unwritten: poison bytes, -7, NaN)."""
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+        w = np.ascontiguousarray(topk_w, dtype=np.float32)
+        es = np.ascontiguousarray(expert_slot, dtype=np.int32)
+        T, H = x.shape
+        k = es.shape[1]
+        rb = self.row_bytes(H, fmt)
+        buf = np.full((capacity_rows, rb), poison, np.uint8)
+        slot_src = np.full(capacity_rows, -7, np.int32)
+        slot_w = np.full(capacity_rows, np.nan, np.float32)
+        st = self.L.oracle_ll_pack(T, H, k, fmt, _p(x), _p(w), _p(es), _p(buf), capacity_rows,
+                                   _p(slot_src), _p(slot_w))
+        return {"status": int(st), "send_buf": buf, "slot_src": slot_src, "slot_w": slot_w}
+
+    def ll_descriptors(self, num_tokens_per_expert: np.ndarray, expert_offset: np.ndarray,
+                       R: int, row_bytes_: int, channels: int) -> np.ndarray:
+        """Closed-form per-expert TransferCmd stream, channel-major order."""
+        cnt = np.ascontiguousarray(num_tokens_per_expert, dtype=np.int32)
+        off = np.ascontiguousarray(expert_offset, dtype=np.int32)
+        E = cnt.size
+        cap = int(sum((int(c) + 7) // 8 for c in cnt)) + E + 16
+        out = np.zeros(cap, CMD_DTYPE)
+        n = self.L.oracle_ll_descriptors(E, R, channels, _p(cnt), _p(off), row_bytes_, _p(out),
+                                         cap)
+        if n < 0:
+            raise RuntimeError("descriptor buffer too small or E % R != 0")
+        return out[:n]
+
+    def ll_combine(self, y: np.ndarray, topk_idx: np.ndarray, topk_w: np.ndarray,
+                   expert_slot: np.ndarray, H: Optional[int] = None) -> np.ndarray:
+        """Gate-weighted sum of the per-expert rows of each token, float64."""
+        y = np.ascontiguousarray(y, dtype=np.uint16)
+        idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+        w = np.ascontiguousarray(topk_w, dtype=np.float32)
+        es = np.ascontiguousarray(expert_slot, dtype=np.int32)
+        T, k = idx.shape
+        if H is None:
+            H = y.shape[1]
+        out = np.zeros((T, H), np.float64)
+        if T and H:
+            self.L.oracle_ll_combine(T, H, k, _p(y), _p(idx), _p(w), _p(es), _p(out))
+        return out
+
 
 _default: Optional[Oracle] = None
 
@@ -221,3 +291,19 @@ def descriptors(*a, **kw):
 
 def combine(*a, **kw):
     return default().combine(*a, **kw)
+
+
+def ll_layout(*a, **kw):
+    return default().ll_layout(*a, **kw)
+
+
+def ll_pack(*a, **kw):
+    return default().ll_pack(*a, **kw)
+
+
+def ll_descriptors(*a, **kw):
+    return default().ll_descriptors(*a, **kw)
+
+
+def ll_combine(*a, **kw):
+    return default().ll_combine(*a, **kw)

@@ -35,6 +35,11 @@
  *   oracle_quantize_row   pinned: max code per block, error bound, round trip
  *   oracle_descriptors    pinned: tiling invariants, counts
  *   oracle_combine        pinned: per-expert brute force, identity, scaling
+ *   oracle_ll_layout      pinned: brute-force per-expert enumeration, invariants
+ *   oracle_ll_pack        pinned: byte equality with x rows per (t, j)
+ *   oracle_ll_descriptors pinned: tiling invariants, counts, brute-force grouping
+ *   oracle_ll_combine     pinned: per-choice brute force, identity, agreement
+ *                         with oracle_combine on identity experts
  *   end-to-end values vs the pages: parity unpinned (no printed example)
  */
 
@@ -338,6 +343,149 @@ void oracle_combine(int T, int H, int E, int R, int k, const uint16_t* y,
             if (s < 0) continue;
             const uint16_t* yrow = y + (int64_t)s * H;
             for (int h = 0; h < H; h++) o[h] += W[r] * (double)bf16_to_float(yrow[h]);
+        }
+    }
+}
+
+/* ------------------------------------------------------------ per-expert mode
+ * The low-latency mode of [UCCL] s4.1 exchanges tokens per expert rather than
+ * per rank: every kept choice (t, j) goes to the owner of expert e_j, into
+ * that expert's receive rows ([GIN] s3.1.1: a token is sent to the owner of
+ * its expert).  The pages give no layout; the readings are:
+ *   Reading: no deduplication by rank; every (t, j) with e_j != -1 is one row,
+ *        so a token that names an expert twice sends two rows.
+ *   Reading: expert e's rows are [expert_offset[e], expert_offset[e+1]) of the
+ *        send buffer, in ascending (t, j) order; expert_offset is the exclusive
+ *        scan of num_tokens_per_expert (the same arrays as oracle_layout's).
+ *   Reading: expert_slot[t, j] is the row of choice (t, j), or -1 if dropped. */
+int oracle_ll_layout(int T, int E, int k, const int32_t* topk_idx,
+                     int32_t* num_tokens_per_expert, int32_t* expert_offset,
+                     int32_t* expert_slot) {
+    if (T < 0 || E < 1 || E > 4096 || k < 1) return ORC_ERR_INVALID_ARG;
+    int status = ORC_OK;
+    for (int e = 0; e < E; e++) num_tokens_per_expert[e] = 0;
+    for (int64_t i = 0; i < (int64_t)T * k; i++) {
+        int e = topk_idx[i];
+        if (e == -1) continue;
+        if (e < -1 || e >= E) { status = ORC_ERR_BAD_EXPERT; continue; }
+        num_tokens_per_expert[e]++;
+    }
+    int32_t acc = 0;   /* exclusive scan */
+    for (int e = 0; e < E; e++) {
+        expert_offset[e] = acc;
+        acc += num_tokens_per_expert[e];
+    }
+    expert_offset[E] = acc;
+    /* second pass: a running count per expert hands out the rows in order */
+    int32_t run[4096];
+    for (int e = 0; e < E; e++) run[e] = 0;
+    for (int64_t i = 0; i < (int64_t)T * k; i++) {
+        int e = topk_idx[i];
+        if (e < 0 || e >= E) { expert_slot[i] = -1; continue; }
+        expert_slot[i] = expert_offset[e] + run[e]++;
+    }
+    return status;
+}
+
+/* Row t (bf16, or its fp8 row) goes to send_buf row expert_slot[t, j] for
+ * every kept choice.  Per-row metadata (reading): slot_src[s] = t and
+ * slot_w[s] = w[t, j], the gate of that choice.  Rows at or beyond the
+ * capacity are not written and ORC_ERR_CAPACITY is returned. */
+int oracle_ll_pack(int T, int H, int k, int fmt, const uint16_t* x, const float* topk_w,
+                   const int32_t* expert_slot, uint8_t* send_buf, int64_t capacity_rows,
+                   int32_t* slot_src, float* slot_w) {
+    if (fmt == ORC_FMT_FP8 && H % 128 != 0) return ORC_ERR_INVALID_ARG;
+    int64_t rb = oracle_row_bytes(H, fmt);
+    int status = ORC_OK;
+    uint8_t qbuf[1 << 16];
+    if (fmt == ORC_FMT_FP8 && rb > (int64_t)sizeof(qbuf)) return ORC_ERR_INVALID_ARG;
+    for (int t = 0; t < T; t++) {
+        const uint16_t* xrow = x + (int64_t)t * H;
+        if (fmt == ORC_FMT_FP8) oracle_quantize_row(H, xrow, qbuf);
+        for (int j = 0; j < k; j++) {
+            int32_t s = expert_slot[(int64_t)t * k + j];
+            if (s < 0) continue;
+            if (s >= capacity_rows) { status = ORC_ERR_CAPACITY; continue; }
+            uint8_t* dst = send_buf + (int64_t)s * rb;
+            if (fmt == ORC_FMT_BF16) memcpy(dst, xrow, (size_t)rb);
+            else memcpy(dst, qbuf, (size_t)rb);
+            slot_src[s] = t;
+            slot_w[s] = topk_w[(int64_t)t * k + j];
+        }
+    }
+    return status;
+}
+
+/* Closed form of the per-expert command stream:
+ *   Reading: each expert's rows are cut greedily into messages of at most 8
+ *        consecutive rows ([UCCL] s4.1, s5.3); message m of expert e (on rank
+ *        r = e / epr) is WRITE{dst_rank=r, src_offset=(eo_e+8m)*row_bytes,
+ *        dst_offset=(eo_e - eo_{r*epr} + 8m)*row_bytes, size=n*row_bytes,
+ *        num_tokens=n}: the destination keeps its experts' rows back to back.
+ *   Reading: after its WRITEs, each expert (also one with no rows) gets
+ *        ATOMIC{dst_rank=r, op=ADD, value=cnt_e, dst_offset=4*(e - r*epr)},
+ *        which adds its count into the receiver's per-expert count word.
+ *   Reading: rank r uses channel r mod C; per channel, ranks ascending, then
+ *        the rank's experts ascending.
+ * Returns the number of records, or -1 if max is too small. */
+int64_t oracle_ll_descriptors(int E, int R, int C, const int32_t* num_tokens_per_expert,
+                              const int32_t* expert_offset, int64_t row_bytes,
+                              orc_cmd_t* out, int64_t max) {
+    if (E % R != 0) return -1;
+    int epr = E / R;
+    int64_t n = 0;
+    for (int c = 0; c < C; c++) {
+        for (int r = c; r < R; r += C) {
+            int32_t base = expert_offset[r * epr];
+            for (int le = 0; le < epr; le++) {
+                int e = r * epr + le;
+                int32_t cnt = num_tokens_per_expert[e];
+                for (int32_t m = 0; 8 * m < cnt; m++) {
+                    int32_t rows = cnt - 8 * m < 8 ? cnt - 8 * m : 8;
+                    if (n >= max) return -1;
+                    orc_cmd_t d;
+                    memset(&d, 0, sizeof d);
+                    d.type = ORC_CMD_WRITE;
+                    d.num_tokens = (uint16_t)rows;
+                    d.dst_rank = (uint32_t)r;
+                    d.size_or_value = (uint32_t)(rows * row_bytes);
+                    d.src_offset = (uint64_t)(expert_offset[e] + 8LL * m) * (uint64_t)row_bytes;
+                    d.dst_offset = (uint64_t)(expert_offset[e] - base + 8LL * m) * (uint64_t)row_bytes;
+                    out[n++] = d;
+                }
+                if (n >= max) return -1;
+                orc_cmd_t a;
+                memset(&a, 0, sizeof a);
+                a.type = ORC_CMD_ATOMIC;
+                a.op = ORC_ATOMIC_ADD;
+                a.dst_rank = (uint32_t)r;
+                a.size_or_value = (uint32_t)num_tokens_per_expert[e];
+                a.dst_offset = (uint64_t)(4 * le);
+                out[n++] = a;
+            }
+        }
+    }
+    return n;
+}
+
+/* Per-expert combine: the expert outputs Y sit in the per-expert layout, row
+ * expert_slot[t, j] holding expert e_j's output for token t.  The combined
+ * output is the gate-weighted sum over the token's kept choices (the MoE
+ * output by definition):
+ *   out[t,h] = sum over j with e_j != -1 of w[t,j] * Y[expert_slot[t,j], h]
+ * evaluated in double precision. */
+void oracle_ll_combine(int T, int H, int k, const uint16_t* y, const int32_t* topk_idx,
+                       const float* topk_w, const int32_t* expert_slot, double* out) {
+    for (int t = 0; t < T; t++) {
+        double* o = out + (int64_t)t * H;
+        for (int h = 0; h < H; h++) o[h] = 0.0;
+        for (int j = 0; j < k; j++) {
+            if (topk_idx[(int64_t)t * k + j] < 0) continue;
+            int32_t s = expert_slot[(int64_t)t * k + j];
+            if (s < 0) continue;
+            double w = (double)topk_w[(int64_t)t * k + j];
+            const uint16_t* yrow = y + (int64_t)s * H;
+            for (int h = 0; h < H; h++) o[h] += w * (double)bf16_to_float(yrow[h]);
         }
     }
 }

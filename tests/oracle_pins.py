@@ -455,6 +455,180 @@ def pin_combine_identity(O, names=("tiny", "decode")):
         assert np.array_equal(o2, 2.0 * out)
 
 
+# ----------------------------------------------------------------- per-expert mode
+def brute_ll(idx: np.ndarray, E: int):
+    """Independent enumeration of the per-expert layout: the list of kept
+    choices (t, j, e) sorted by (e, t, j); a choice's row is its position."""
+    T, k = idx.shape
+    choices = [(int(idx[t, j]), t, j) for t in range(T) for j in range(k) if int(idx[t, j]) != -1]
+    ordered = sorted(choices)
+    slot = {(t, j): i for i, (_, t, j) in enumerate(ordered)}
+    cnt = collections.Counter(e for (e, _, _) in choices)
+    return ordered, slot, cnt
+
+
+def brute_ll_descriptors(ordered, E, R, rb, C):
+    """Group the rows of each expert into messages of 8 by walking them; one
+    count record per expert.  Returns records in channel-major order."""
+    epr = E // R
+    first = {}
+    rows = collections.defaultdict(list)
+    for i, (e, _, _) in enumerate(ordered):
+        rows[e].append(i)
+    recs = []
+    for c in range(C):
+        for r in range(c, R, C):
+            base = None
+            for le in range(epr):
+                e = r * epr + le
+                if base is None:
+                    # the rank's first row: the first row of any of its experts
+                    # (or, if none has rows, where the next expert would start)
+                    cand = [rows[r * epr + q][0] for q in range(epr) if rows[r * epr + q]]
+                    base = min(cand) if cand else 0
+                rs = rows[e]
+                for m in range(0, len(rs), 8):
+                    part = rs[m:m + 8]
+                    recs.append((1, 0, len(part), r, len(part) * rb, part[0] * rb, (part[0] - base) * rb))
+                recs.append((2, 1, 0, r, len(rs), 0, 4 * le))
+    return recs
+
+
+def pin_ll_golden(O):
+    g = json.load(open(os.path.join(GOLDEN, "ll_hand_example.json")))
+    idx = np.array(g["topk_idx"], np.int32)
+    w = np.array(g["topk_w"], np.float32)
+    T, H, E, R = g["T"], g["H"], g["E"], g["R"]
+    L = O.ll_layout(idx, E)
+    assert L["status"] == 0
+    assert np.array_equal(L["num_tokens_per_expert"], np.array(g["num_tokens_per_expert"]))
+    assert np.array_equal(L["expert_offset"], np.array(g["expert_offset"]))
+    assert np.array_equal(L["expert_slot"], np.array(g["expert_slot"]))
+    x = (np.arange(T * H, dtype=np.uint32) * 5 + 3).astype(np.uint16).reshape(T, H)
+    pk = O.ll_pack(x, w, L["expert_slot"], FMT_BF16, capacity_rows=9)
+    assert pk["status"] == 0
+    assert np.array_equal(pk["slot_src"][:7], np.array(g["slot_src"]))
+    assert np.array_equal(pk["slot_w"][:7], np.array(g["slot_w"], np.float32))
+    for s, t in enumerate(g["slot_src"]):
+        assert np.array_equal(pk["send_buf"][s].view(np.uint16), x[t])
+    assert np.all(pk["send_buf"][7:] == 0xA5)
+    d = O.ll_descriptors(L["num_tokens_per_expert"], L["expert_offset"], R, g["row_bytes_bf16"],
+                         g["channels"])
+    want = [(x_["type"], x_["op"], x_["num_tokens"], x_["dst_rank"], x_["size_or_value"],
+             x_["src_offset"], x_["dst_offset"]) for x_ in g["descriptors_channel_order"]]
+    assert [_rec(x_) for x_ in d] == want
+    y = np.repeat(W.f32_to_bf16_bits(np.arange(1, 8, dtype=np.float32))[:, None], H, axis=1)
+    out = O.ll_combine(y, idx, w, L["expert_slot"])
+    want_c = np.array(g["combine_y_row_value_is_slot_plus_1"])
+    assert np.array_equal(out, np.repeat(want_c[:, None], H, axis=1))
+
+
+def pin_ll_bruteforce(O, n_cases: int = 60, seed: int = 31):
+    rng = np.random.default_rng(seed)
+    for c in range(n_cases):
+        E, R, k = [(8, 4, 2), (16, 4, 3), (32, 8, 8), (4, 2, 4), (64, 64, 4), (256, 32, 8)][c % 6]
+        T = int(rng.integers(0, 40))
+        H = 128 * int(rng.integers(1, 3)) if c % 2 else 8 * int(rng.integers(1, 9))
+        fmt = FMT_FP8 if (c % 2 and H % 128 == 0) else FMT_BF16
+        inp = W.make_random_case(rng, T, H, E, R, k, drop_prob=0.2 if c % 3 == 0 else 0.0)
+        idx, w, x = inp["topk_idx"], inp["topk_w"], inp["x"]
+        if c % 7 == 0 and T > 0:
+            idx = idx.copy()
+            idx[0, :] = idx[0, 0]            # one token naming one expert k times
+        ordered, slot, cnt = brute_ll(idx, E)
+        Q = len(ordered)
+        L = O.ll_layout(idx, E)
+        assert L["status"] == 0 and L["Q"] == Q
+        assert np.array_equal(L["num_tokens_per_expert"], np.array([cnt[e] for e in range(E)]))
+        want_slot = np.full((T, k), -1, np.int32)
+        for (t, j), s in slot.items():
+            want_slot[t, j] = s
+        assert np.array_equal(L["expert_slot"], want_slot)
+        # pack: each row is its token's row (or its fp8 row), metadata per choice
+        cap = Q + 3
+        pk = O.ll_pack(x, w, L["expert_slot"], fmt, capacity_rows=cap)
+        assert pk["status"] == 0
+        for (t, j), s in slot.items():
+            if fmt == FMT_BF16:
+                assert np.array_equal(pk["send_buf"][s].view(np.uint16), x[t])
+            else:
+                assert np.array_equal(pk["send_buf"][s], O.quantize_row(x[t]))
+            assert pk["slot_src"][s] == t and pk["slot_w"][s] == w[t, j]
+        assert np.all(pk["send_buf"][Q:] == 0xA5) and np.all(pk["slot_src"][Q:] == -7)
+        if Q >= 2:
+            pk2 = O.ll_pack(x, w, L["expert_slot"], fmt, capacity_rows=Q - 1)
+            assert pk2["status"] == 3
+            assert np.array_equal(pk2["send_buf"], pk["send_buf"][:Q - 1])
+        # descriptors: brute-force grouping, and the WRITEs tile [0, Q*rb)
+        rb = O.row_bytes(H, fmt)
+        C = int(rng.integers(1, 9))
+        d = O.ll_descriptors(L["num_tokens_per_expert"], L["expert_offset"], R, rb, C)
+        assert [_rec(x_) for x_ in d] == brute_ll_descriptors(ordered, E, R, rb, C)
+        wr = sorted((int(x_["src_offset"]), int(x_["size_or_value"])) for x_ in d if x_["type"] == 1)
+        pos = 0
+        for s0, n in wr:
+            assert s0 == pos and n > 0
+            pos = s0 + n
+        assert pos == Q * rb
+        # combine: loop over the choices of each token
+        if fmt == FMT_BF16:
+            y = W.f32_to_bf16_bits(rng.standard_normal((max(Q, 1), H), dtype=np.float32))
+            yf = W.bf16_bits_to_f32(y).astype(np.float64)
+            out = O.ll_combine(y, idx, w, L["expert_slot"], H=H)
+            want = np.zeros((T, H))
+            for (t, j), s in slot.items():
+                want[t] += float(w[t, j]) * yf[s]
+            assert np.allclose(out, want, rtol=1e-12, atol=1e-12)
+
+
+def pin_ll_invariants(O, names=("tiny", "decode", "train")):
+    """The per-expert counts and offsets equal the rank layout's; the rows are
+    a bijection onto [0, Q) with Q = T*k minus drops; inside an expert the
+    source tokens ascend."""
+    for name in names:
+        w = W.WORKLOADS[name]
+        inp = workload_inputs(name)
+        idx = inp["topk_idx"]
+        L = O.ll_layout(idx, w.E)
+        R0 = O.layout(idx, w.E, w.R)
+        assert np.array_equal(L["num_tokens_per_expert"], R0["num_tokens_per_expert"])
+        assert np.array_equal(L["expert_offset"], R0["expert_offset"])
+        es = L["expert_slot"]
+        kept = idx != -1
+        assert L["Q"] == int(kept.sum())
+        assert np.array_equal(np.sort(es[kept]), np.arange(L["Q"]))
+        assert np.all(es[~kept] == -1)
+        t_of = np.repeat(np.arange(w.T), w.k).reshape(w.T, w.k)
+        src = np.empty(L["Q"], np.int64)
+        src[es[kept]] = t_of[kept]
+        e_of = np.empty(L["Q"], np.int64)
+        e_of[es[kept]] = idx[kept]
+        assert np.all(np.diff(e_of) >= 0)
+        same = np.diff(e_of) == 0
+        assert np.all(np.diff(src)[same] >= 0)
+
+
+def pin_ll_combine_identity(O, names=("tiny", "decode")):
+    """Identity experts: per-expert combine gives (sum_j w_j) * x, the same
+    as the rank-deduplicated combine on its own identity rows."""
+    for name in names:
+        w = W.WORKLOADS[name]
+        inp = workload_inputs(name)
+        L = O.ll_layout(inp["topk_idx"], w.E)
+        pk = O.ll_pack(inp["x"], inp["topk_w"], L["expert_slot"], FMT_BF16, capacity_rows=L["Q"])
+        y = pk["send_buf"].view(np.uint16).reshape(L["Q"], w.H)
+        out = O.ll_combine(y, inp["topk_idx"], inp["topk_w"], L["expert_slot"])
+        xf = W.bf16_bits_to_f32(inp["x"]).astype(np.float64)
+        wsum = inp["topk_w"].astype(np.float64).sum(axis=1)
+        assert np.allclose(out, wsum[:, None] * xf, rtol=1e-12, atol=1e-300)
+        R0 = O.layout(inp["topk_idx"], w.E, w.R)
+        pr = O.pack(inp["x"], inp["topk_idx"], inp["topk_w"], R0["send_slot"], w.E, w.R,
+                    FMT_BF16, capacity_rows=R0["P"])
+        yr = pr["send_buf"].view(np.uint16).reshape(R0["P"], w.H)
+        outr = O.combine(yr, inp["topk_idx"], inp["topk_w"], R0["send_slot"], w.E, w.R)
+        assert np.allclose(out, outr, rtol=1e-12, atol=1e-300)
+
+
 ALL_PINS = [
     pin_layout_golden, pin_layout_bruteforce, pin_layout_invariants,
     pin_layout_expected_fanout, pin_layout_errors,
@@ -462,4 +636,5 @@ ALL_PINS = [
     pin_pack_golden, pin_pack_bruteforce,
     pin_descriptors_golden, pin_descriptors,
     pin_combine_golden, pin_combine_bruteforce, pin_combine_identity,
+    pin_ll_golden, pin_ll_bruteforce, pin_ll_invariants, pin_ll_combine_identity,
 ]

@@ -48,6 +48,18 @@ MUTANTS = {
     "combine_rank_map": ("W[e / epr] += (double)topk_w", "W[e % R] += (double)topk_w"),
     "combine_unweighted": ("o[h] += W[r] * (double)bf16_to_float(yrow[h]);",
                            "o[h] += (double)bf16_to_float(yrow[h]);"),
+    "ll_slot_descending": ("expert_slot[i] = expert_offset[e] + run[e]++;",
+                           "expert_slot[i] = expert_offset[e + 1] - 1 - run[e]++;"),
+    "ll_drop_counted": ("if (e == -1) continue;\n        if (e < -1 || e >= E) { status = ORC_ERR_BAD_EXPERT; continue; }",
+                        "if (e == -1) e = 0;\n        if (e < -1 || e >= E) { status = ORC_ERR_BAD_EXPERT; continue; }"),
+    "ll_dst_absolute": ("d.dst_offset = (uint64_t)(expert_offset[e] - base + 8LL * m) * (uint64_t)row_bytes;",
+                        "d.dst_offset = (uint64_t)(expert_offset[e] + 8LL * m) * (uint64_t)row_bytes;"),
+    "ll_atomic_global_expert": ("a.dst_offset = (uint64_t)(4 * le);", "a.dst_offset = (uint64_t)(4 * e);"),
+    "ll_batch_7": ("int32_t rows = cnt - 8 * m < 8 ? cnt - 8 * m : 8;",
+                   "int32_t rows = cnt - 8 * m < 7 ? cnt - 8 * m : 7;"),
+    "ll_meta_first_gate": ("slot_w[s] = topk_w[(int64_t)t * k + j];", "slot_w[s] = topk_w[(int64_t)t * k];"),
+    "ll_combine_unweighted": ("o[h] += w * (double)bf16_to_float(yrow[h]);",
+                              "o[h] += (double)bf16_to_float(yrow[h]);"),
 }
 
 

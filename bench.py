@@ -53,6 +53,21 @@ def algorithmic_bytes(w, P: int) -> dict:
             "total": layout_r + layout_w + pack_r + pack_w + comb_r + comb_w}
 
 
+def algorithmic_bytes_ll(w, Q: int) -> dict:
+    """Per-expert mode: one row per kept choice (Q rows), each input read
+    once and each output written once."""
+    T, H, E, R, k = w.T, w.H, w.E, w.R, w.k
+    rb = row_bytes(H, w.fmt)
+    base = algorithmic_bytes(w, 0)
+    layout = base["layout"] + 4 * T * k + 4 * T * k    # + row table: read idx, write slots
+    pack_r = 2 * T * H + 8 * T * k + 4 * T * k + 4 * (E + 1)
+    pack_w = Q * rb + Q * 8
+    comb_r = 2 * Q * H + 8 * T * k + 4 * T * k
+    comb_w = 2 * T * H
+    return {"layout": layout, "dispatch": pack_r + pack_w, "combine": comb_r + comb_w,
+            "total": layout + pack_r + pack_w + comb_r + comb_w}
+
+
 KERNEL_SOURCES = ["combine_topk_rank_amd/csrc/ep_dispatch.hip",
                   "combine_topk_rank_amd/csrc/ep_combine.hip",
                   "combine_topk_rank_amd/csrc/ep_layout.hip",
@@ -85,7 +100,7 @@ def measured_traffic(kernel_prefix: str, workload: str):
     return None
 
 
-def cpu_baseline(w, inp, budget_s: float) -> dict:
+def cpu_baseline(w, inp, budget_s: float, mode: str = "rank") -> dict:
     """The oracle as it stands, single thread, on whole passes of the same
     workload until about budget_s seconds of CPU work."""
     import numpy as np
@@ -94,26 +109,38 @@ def cpu_baseline(w, inp, budget_s: float) -> dict:
     passes, t_total, P = 0, 0.0, 0
     while True:
         t0 = time.perf_counter()
-        L = oracle.layout(inp["topk_idx"], w.E, w.R)
-        P = L["P"]
-        pk = oracle.pack(inp["x"], inp["topk_idx"], inp["topk_w"], L["send_slot"], w.E, w.R,
-                         w.fmt, capacity_rows=P)
-        oracle.descriptors(L["num_tokens_per_rank"], L["rank_offset"], row_bytes(w.H, w.fmt),
-                           w.channels)
+        if mode == "ll":
+            L = oracle.ll_layout(inp["topk_idx"], w.E)
+            P = L["Q"]
+            pk = oracle.ll_pack(inp["x"], inp["topk_w"], L["expert_slot"], w.fmt, capacity_rows=P)
+            oracle.ll_descriptors(L["num_tokens_per_expert"], L["expert_offset"], w.R,
+                                  row_bytes(w.H, w.fmt), w.channels)
+        else:
+            L = oracle.layout(inp["topk_idx"], w.E, w.R)
+            P = L["P"]
+            pk = oracle.pack(inp["x"], inp["topk_idx"], inp["topk_w"], L["send_slot"], w.E, w.R,
+                             w.fmt, capacity_rows=P)
+            oracle.descriptors(L["num_tokens_per_rank"], L["rank_offset"],
+                               row_bytes(w.H, w.fmt), w.channels)
         if w.fmt == 0:
             y = pk["send_buf"].view(np.uint16).reshape(P, w.H)
         else:
             y = np.zeros((P, w.H), np.uint16)
-        oracle.combine(y, inp["topk_idx"], inp["topk_w"], L["send_slot"], w.E, w.R)
+        if mode == "ll":
+            oracle.ll_combine(y, inp["topk_idx"], inp["topk_w"], L["expert_slot"], H=w.H)
+        else:
+            oracle.combine(y, inp["topk_idx"], inp["topk_w"], L["send_slot"], w.E, w.R)
         t_total += time.perf_counter() - t0
         passes += 1
         del pk, y
         if t_total >= budget_s:
             break
     per = t_total / passes
-    gbs = algorithmic_bytes(w, P)["total"] / per / 1e9
+    ab = algorithmic_bytes_ll(w, P) if mode == "ll" else algorithmic_bytes(w, P)
+    gbs = ab["total"] / per / 1e9
     return {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{passes} whole pass(es) of the {w.name} workload (layout, pack, "
+            "sample": f"{passes} whole pass(es) of the {w.name} workload"
+                      f"{' (per-expert mode)' if mode == 'll' else ''} (layout, pack, "
                       f"descriptors, combine); {per:.3f} s per pass, "
                       f"{w.T / per:.0f} tokens/s"}
 
@@ -124,6 +151,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="train")
+    ap.add_argument("--mode", choices=("rank", "ll"), default="rank",
+                    help="rank: one row per (token, rank) pair; ll: the per-expert "
+                         "(low-latency) mode, one row per kept choice")
     ap.add_argument("--proxy-threads", type=int, default=4)
     ap.add_argument("--op-events-every", type=int, default=5,
                     help="record per-op HIP events on every n-th timed step (events between "
@@ -166,7 +196,8 @@ def main() -> int:
     d_idx = torch.from_numpy(inp["topk_idx"]).to(dev)
     d_w = torch.from_numpy(inp["topk_w"]).to(dev)
     s = ep.shape(w.T, w.H, w.E, w.R, w.k, w.fmt)
-    b = ep.Buffers(s, device=dev)
+    ll = args.mode == "ll"
+    b = ep.BuffersLL(s, device=dev) if ll else ep.Buffers(s, device=dev)
     cap = b.capacity_rows
     if w.fmt == 0:
         y = b.send_buf.view(torch.bfloat16).reshape(cap, w.H)
@@ -197,8 +228,12 @@ def main() -> int:
     if st != 0:
         eprint(f"device status after warmup: {ep.status_str(st)}")
         return 1
-    P = int(b.rank_offset[-1].item())
-    ab = algorithmic_bytes(w, P)
+    if ll:
+        P = int(b.expert_offset[-1].item())
+        ab = algorithmic_bytes_ll(w, P)
+    else:
+        P = int(b.rank_offset[-1].item())
+        ab = algorithmic_bytes(w, P)
 
     K = args.steps
     every = max(1, args.op_events_every)
@@ -266,16 +301,21 @@ def main() -> int:
     tokens_s = w.T * K / elapsed
     # dominant kernel: the longer of pack (inside ep_dispatch) and combine
     if t_disp >= t_comb:
-        dom, dom_ms, dom_bytes, prefix = "pack_kernel (ep_dispatch)", t_disp, ab["dispatch"], "pack_kernel"
+        if ll:
+            dom, prefix = "ll_pack_kernel (ep_dispatch_ll)", "ll_pack_kernel"
+        else:
+            dom, prefix = "pack_kernel (ep_dispatch)", "pack_kernel"
+        dom_ms, dom_bytes = t_disp, ab["dispatch"]
     else:
-        dom, dom_ms, dom_bytes, prefix = "combine_kernel (ep_combine)", t_comb, ab["combine"], "combine_kernel"
+        dom = "combine_kernel (ep_combine_ll)" if ll else "combine_kernel (ep_combine)"
+        dom_ms, dom_bytes, prefix = t_comb, ab["combine"], "combine_kernel"
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
-    traffic = measured_traffic(prefix, w.name)
+    traffic = measured_traffic(prefix, w.name + ("-ll" if ll else ""))
 
     cpu = None
     if args.cpu_budget > 0:
         eprint("bench: timing the CPU oracle")
-        cpu = cpu_baseline(w, inp, args.cpu_budget)
+        cpu = cpu_baseline(w, inp, args.cpu_budget, args.mode)
 
     out = {
         "metric": METRIC,
@@ -294,7 +334,8 @@ def main() -> int:
                                f"{w.channels} ring channels, depth {w.depth}, "
                                f"{w.max_inflight} in flight",
                    "tokens": w.T, "hidden": w.H, "experts": w.E, "ranks": w.R, "top_k": w.k,
-                   "pairs_P": P, "parallelism": "one GPU's share of EP"},
+                   "mode": "per-expert (low-latency)" if ll else "per-rank",
+                   ("rows_Q" if ll else "pairs_P"): P, "parallelism": "one GPU's share of EP"},
         "tokens_per_s": round(tokens_s, 1),
         "pct_of_hbm_peak": round(100 * value / PEAK_HBM_GBS, 2),
         "copy_ceiling_GBps": round(copy_gbs, 1),

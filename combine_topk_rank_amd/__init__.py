@@ -93,6 +93,12 @@ def _load() -> ctypes.CDLL:
     L.ep_dispatch.restype = ctypes.c_int
     L.ep_combine.argtypes = [S, P, i64, P, P, P, P, P, P]
     L.ep_combine.restype = ctypes.c_int
+    L.ep_dispatch_layout_ll.argtypes = [S, P, P, P, P, sz, P, P]
+    L.ep_dispatch_layout_ll.restype = ctypes.c_int
+    L.ep_dispatch_ll.argtypes = [S, P, P, P, P, P, P, i64, P, P, P, P, sz, P, P]
+    L.ep_dispatch_ll.restype = ctypes.c_int
+    L.ep_combine_ll.argtypes = [S, P, i64, P, P, P, P, P, P]
+    L.ep_combine_ll.restype = ctypes.c_int
     L.ep_ring_create.argtypes = [i32, i32, i32, i64]
     L.ep_ring_create.restype = P
     L.ep_ring_destroy.argtypes = [P]
@@ -181,6 +187,34 @@ def ep_combine(s, y, topk_idx, topk_w, send_slot, out, dev_status, stream=None) 
     st = lib.ep_combine(ctypes.byref(s), _ptr(y), y.shape[0], _ptr(topk_idx), _ptr(topk_w),
                         _ptr(send_slot), _ptr(out), _ptr(dev_status), _stream(stream))
     _check(st, "ep_combine")
+
+
+def ep_dispatch_layout_ll(s, topk_idx, expert_offset, expert_slot, workspace, dev_status,
+                          stream=None) -> None:
+    st = lib.ep_dispatch_layout_ll(ctypes.byref(s), _ptr(topk_idx), _ptr(expert_offset),
+                                   _ptr(expert_slot), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(),
+                                   _ptr(dev_status), _stream(stream))
+    _check(st, "ep_dispatch_layout_ll")
+
+
+def ep_dispatch_ll(s, x, topk_idx, topk_w, expert_offset, expert_slot, send_buf, slot_src,
+                   slot_w, ring, workspace, dev_status, stream=None,
+                   capacity_rows: Optional[int] = None) -> None:
+    cap = send_buf.shape[0] if capacity_rows is None else capacity_rows
+    st = lib.ep_dispatch_ll(ctypes.byref(s), _ptr(x), _ptr(topk_idx), _ptr(topk_w),
+                            _ptr(expert_offset), _ptr(expert_slot), _ptr(send_buf), cap,
+                            _ptr(slot_src), _ptr(slot_w),
+                            ring.handle if ring is not None else None, _ptr(workspace),
+                            workspace.numel() * workspace.element_size(), _ptr(dev_status),
+                            _stream(stream))
+    _check(st, "ep_dispatch_ll")
+
+
+def ep_combine_ll(s, y, topk_idx, topk_w, expert_slot, out, dev_status, stream=None) -> None:
+    st = lib.ep_combine_ll(ctypes.byref(s), _ptr(y), y.shape[0], _ptr(topk_idx), _ptr(topk_w),
+                           _ptr(expert_slot), _ptr(out), _ptr(dev_status), _stream(stream))
+    _check(st, "ep_combine_ll")
 
 
 class Ring:
@@ -273,3 +307,34 @@ class Buffers:
     def combine(self, y, topk_idx, topk_w, stream=None):
         ep_combine(self.shape, y, topk_idx, topk_w, self.send_slot, self.out, self.dev_status,
                    stream)
+
+
+class BuffersLL(Buffers):
+    """Buffers of one per-expert (low-latency) pass: the rank layout's
+    buffers (its counts, offsets and workspace are reused) plus the per-expert
+    rows, metadata and row table.  Capacity defaults to T*k rows."""
+
+    def __init__(self, s: ep_shape_t, capacity_rows: Optional[int] = None, device="cuda"):
+        import torch
+        super().__init__(s, capacity_rows=0, device=device)
+        T, k = s.T, s.k
+        cap = T * k if capacity_rows is None else capacity_rows
+        self.capacity_rows = cap
+        self.expert_slot = torch.empty((T, k), dtype=torch.int32, device=device)
+        self.send_buf = torch.empty((cap, self.row_bytes), dtype=torch.uint8, device=device)
+        self.slot_src = torch.empty(cap, dtype=torch.int32, device=device)
+        self.slot_w = torch.empty(cap, dtype=torch.float32, device=device)
+
+    def layout(self, topk_idx, stream=None):
+        super().layout(topk_idx, stream)
+        ep_dispatch_layout_ll(self.shape, topk_idx, self.expert_offset, self.expert_slot,
+                              self.workspace, self.dev_status, stream)
+
+    def dispatch(self, x, topk_idx, topk_w, ring=None, stream=None):
+        ep_dispatch_ll(self.shape, x, topk_idx, topk_w, self.expert_offset, self.expert_slot,
+                       self.send_buf, self.slot_src, self.slot_w, ring, self.workspace,
+                       self.dev_status, stream)
+
+    def combine(self, y, topk_idx, topk_w, stream=None):
+        ep_combine_ll(self.shape, y, topk_idx, topk_w, self.expert_slot, self.out,
+                      self.dev_status, stream)

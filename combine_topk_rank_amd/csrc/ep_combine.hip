@@ -24,10 +24,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int64_t kCombineSmallWaves = 2048;
 
 struct CombineArgs {
-    const u32x4* y;            // [P, H/8]
+    const u32x4* y;            // [P, H/8] (per-expert mode: [Q, H/8])
     const int32_t* idx;        // [T, k]
     const float* w;            // [T, k]
-    const int32_t* send_slot;  // [T, R]
+    const int32_t* send_slot;  // [T, R] (per-expert mode: expert_slot [T, k])
     u32x4* out;                // [T, H/8]
     int32_t* st;
     int64_t y_rows;
@@ -48,8 +48,14 @@ __device__ inline uint32_t pack2(float lo, float hi) {
 }
 
 // B destination rows are loaded before any of them is accumulated (memory
-// parallelism within a wavefront); accumulation stays in ascending rank order.
-template <int VPL, int B>
+// parallelism within a wavefront); accumulation stays in ascending rank order
+// (per-expert mode, LL: ascending choice order).
+//
+// Per-expert mode (UCCL-EP article s4.1, low-latency mode): the rows sit in
+// the per-expert layout, row expert_slot[t,j] holding expert e_j's output for
+// token t, and
+//   out[t,:] = bf16_rne( sum_{j ascending, e_j kept} w[t,j] * y[expert_slot[t,j], :] ).
+template <int VPL, int B, bool LL>
 __global__ __launch_bounds__(kBlock) void combine_kernel(CombineArgs a) {
     const int lane = lane_id();
     const int64_t gw = (int64_t)blockIdx.x * (kBlock / kWave) + (threadIdx.x / kWave);
@@ -58,26 +64,36 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(CombineArgs a) {
     if (t >= a.T) return;
 
     int32_t s_lane = -1;
-    if (lane < a.R) s_lane = a.send_slot[t * a.R + lane];
+    float W = 0.0f;
+    if (LL) {
+        // lane j: choice j's row and gate
+        if (lane < a.k) {
+            const int e = a.idx[t * a.k + lane];
+            if (e >= 0 && e < a.E) {
+                s_lane = a.send_slot[t * a.k + lane];
+                W = a.w[t * a.k + lane];
+            }
+        }
+    } else {
+        if (lane < a.R) s_lane = a.send_slot[t * a.R + lane];
+        // W for lane r: gate weights of t's experts on rank r, ascending j
+        int e_l = -1;
+        float w_l = 0.0f;
+        if (lane < a.k) {
+            e_l = a.idx[t * a.k + lane];
+            w_l = a.w[t * a.k + lane];
+        }
+        for (int j = 0; j < a.k; ++j) {
+            const int e = bcast(e_l, j);
+            const float wj = bcastf(w_l, j);
+            if (e >= 0 && e < a.E && e / a.epr == lane) W += wj;
+        }
+    }
     if (s_lane >= a.y_rows) {
         set_error(a.st, EP_ERR_CAPACITY);   // a slot beyond the rows of y: skipped
         s_lane = -1;
     }
     const uint64_t dmask = __ballot(s_lane >= 0);
-
-    // W for lane r: gate weights of t's experts on rank r, ascending j
-    int e_l = -1;
-    float w_l = 0.0f;
-    if (lane < a.k) {
-        e_l = a.idx[t * a.k + lane];
-        w_l = a.w[t * a.k + lane];
-    }
-    float W = 0.0f;
-    for (int j = 0; j < a.k; ++j) {
-        const int e = bcast(e_l, j);
-        const float wj = bcastf(w_l, j);
-        if (e >= 0 && e < a.E && e / a.epr == lane) W += wj;
-    }
 
     const int v0 = chunk * VPL * kWave;
     float acc[VPL][8];
@@ -152,14 +168,41 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(CombineArgs a) {
 using namespace ep;
 
 namespace {
-template <int VPL, int B>
+template <int VPL, int B, bool LL>
 int launch_combine(const CombineArgs& a, int64_t waves, hipStream_t stream) {
     const int64_t blocks = ceil_div(waves, kBlock / kWave);
     clear_hip_error();
-    hipLaunchKernelGGL((combine_kernel<VPL, B>), dim3((unsigned)blocks), dim3(kBlock), 0, stream,
-                       a);
+    hipLaunchKernelGGL((combine_kernel<VPL, B, LL>), dim3((unsigned)blocks), dim3(kBlock), 0,
+                       stream, a);
     EP_HIP_CHECK(hipGetLastError());
     return EP_OK;
+}
+
+// Large batches: 7 vectors per lane (two wavefronts per 7168-wide row), one
+// row in flight per wavefront (occupancy hides the latency; a second row's
+// registers would halve it).  Small batches (few wavefronts): 1-2 vectors per
+// lane and eight rows in flight, so each wavefront does not wait on its
+// token's rows one after another.
+template <bool LL>
+int launch_combine_any(CombineArgs& a, hipStream_t stream) {
+    const int vpl_big = a.nv <= 64 ? 1 : a.nv <= 128 ? 2 : a.nv <= 256 ? 4 : a.nv <= 512 ? 8 : 7;
+    const int64_t waves_big = (int64_t)a.T * ceil_div(a.nv, (int64_t)vpl_big * kWave);
+    if (waves_big < kCombineSmallWaves) {
+        const int vpl = a.nv <= 64 ? 1 : 2;
+        a.nchunks = (int32_t)ceil_div(a.nv, (int64_t)vpl * kWave);
+        const int64_t waves = (int64_t)a.T * a.nchunks;
+        return vpl == 1 ? launch_combine<1, 8, LL>(a, waves, stream)
+                        : launch_combine<2, 8, LL>(a, waves, stream);
+    }
+    a.nchunks = (int32_t)ceil_div(a.nv, (int64_t)vpl_big * kWave);
+    const int64_t waves = (int64_t)a.T * a.nchunks;
+    switch (vpl_big) {
+        case 1: return launch_combine<1, 4, LL>(a, waves, stream);
+        case 2: return launch_combine<2, 4, LL>(a, waves, stream);
+        case 4: return launch_combine<4, 2, LL>(a, waves, stream);
+        case 8: return launch_combine<8, 1, LL>(a, waves, stream);
+        default: return launch_combine<7, 1, LL>(a, waves, stream);
+    }
 }
 }  // namespace
 
@@ -188,27 +231,34 @@ extern "C" int ep_combine(const ep_shape_t* shape, const void* y, int64_t y_rows
     a.k = s.k;
     a.epr = s.E / s.R;
     a.nv = s.H / 8;
-    // Large batches: 7 vectors per lane (two wavefronts per 7168-wide row),
-    // one row in flight per wavefront (occupancy hides the latency; a second
-    // row's registers would halve it).  Small batches (few wavefronts): 1-2
-    // vectors per lane and eight rows in flight, so each wavefront does not
-    // wait on its token's rows one after another.
-    const int vpl_big = a.nv <= 64 ? 1 : a.nv <= 128 ? 2 : a.nv <= 256 ? 4 : a.nv <= 512 ? 8 : 7;
-    const int64_t waves_big = (int64_t)s.T * ceil_div(a.nv, (int64_t)vpl_big * kWave);
-    if (waves_big < kCombineSmallWaves) {
-        const int vpl = a.nv <= 64 ? 1 : 2;
-        a.nchunks = (int32_t)ceil_div(a.nv, (int64_t)vpl * kWave);
-        const int64_t waves = (int64_t)s.T * a.nchunks;
-        return vpl == 1 ? launch_combine<1, 8>(a, waves, stream)
-                        : launch_combine<2, 8>(a, waves, stream);
-    }
-    a.nchunks = (int32_t)ceil_div(a.nv, (int64_t)vpl_big * kWave);
-    const int64_t waves = (int64_t)s.T * a.nchunks;
-    switch (vpl_big) {
-        case 1: return launch_combine<1, 4>(a, waves, stream);
-        case 2: return launch_combine<2, 4>(a, waves, stream);
-        case 4: return launch_combine<4, 2>(a, waves, stream);
-        case 8: return launch_combine<8, 1>(a, waves, stream);
-        default: return launch_combine<7, 1>(a, waves, stream);
-    }
+    return launch_combine_any<false>(a, stream);
+}
+
+extern "C" int ep_combine_ll(const ep_shape_t* shape, const void* y, int64_t y_rows,
+                             const int32_t* topk_idx, const float* topk_w,
+                             const int32_t* expert_slot, void* out, int32_t* dev_status,
+                             hipStream_t stream) {
+    int v = validate_shape(shape);
+    if (v != EP_OK) return v;
+    const ep_shape_t s = *shape;
+    if (!dev_status) return EP_ERR_INVALID_ARG;
+    if (s.T == 0) return EP_OK;
+    if (y_rows < 0 || (y_rows > 0 && !y) || !topk_idx || !topk_w || !expert_slot || !out)
+        return EP_ERR_INVALID_ARG;
+    if (((uintptr_t)y | (uintptr_t)out) & 15) return EP_ERR_INVALID_ARG;
+    CombineArgs a{};
+    a.y = reinterpret_cast<const u32x4*>(y);
+    a.idx = topk_idx;
+    a.w = topk_w;
+    a.send_slot = expert_slot;
+    a.out = reinterpret_cast<u32x4*>(out);
+    a.st = dev_status;
+    a.y_rows = y_rows;
+    a.T = s.T;
+    a.E = s.E;
+    a.R = s.R;
+    a.k = s.k;
+    a.epr = s.E / s.R;
+    a.nv = s.H / 8;
+    return launch_combine_any<true>(a, stream);
 }

@@ -65,6 +65,10 @@ struct PackArgs {
     int32_t has_ring;
     int64_t ngroups;              // groups of a workgroup's wavefronts (one per pass)
     uint32_t* arrive;             // arrival counters (workspace, zero between calls)
+    // per-expert mode
+    const int32_t* exp_off;       // [E+1]
+    const int32_t* expert_slot;   // [T, k]
+    float* slot_w;                // [cap]
 };
 
 // ------------------------------------------------------------------ ring
@@ -491,6 +495,87 @@ constexpr int kPackVplFp8H7168 = 14;
 // Half the compute units already saturate HBM with 16 wavefronts each.
 constexpr int kPackGridPerCuNum = 1, kPackGridPerCuDen = 2;
 
+// Store chunk `chunk` of token t's row into every destination slot of the
+// wavefront: destination d (bit d of dmask) goes to slot bcast(s_lane, d).
+// bf16 copies 16-byte vectors; fp8 quantises the chunk once and stores codes
+// and scales.  Slots at or beyond the capacity are skipped.  All lanes of the
+// wavefront call this together.
+template <int VPL, int FMT>
+__device__ inline void store_row_chunk(const PackArgs& a, int64_t t, int chunk, int32_t s_lane,
+                                       uint64_t dmask) {
+    const int lane = lane_id();
+    // load this wavefront's chunk of the row: vectors v0 + lane + 64 i
+    const int v0 = chunk * VPL * kWave;
+    const u32x4* xr = a.x + t * a.nv;
+    u32x4 v[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        int vi = v0 + lane + i * kWave;
+        if (vi < a.nv) v[i] = xr[vi];
+        else v[i] = u32x4{0, 0, 0, 0};
+    }
+
+    if (FMT == EP_FMT_BF16) {
+        for (uint64_t m = dmask; m; m &= m - 1) {
+            const int r = __builtin_ctzll(m);
+            const int32_t s = bcast(s_lane, r);
+            if (s >= a.cap) continue;
+            const __amdgpu_buffer_rsrc_t dst =
+                buffer_rsrc(a.send_buf + (int64_t)s * a.row_bytes, (int32_t)a.row_bytes);
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) {
+                int vi = v0 + lane + i * kWave;
+                if (vi < a.nv)
+                    __builtin_amdgcn_raw_buffer_store_b128(v[i], dst, vi * 16, 0,
+                                                           kStoreSystem | kCacheNt);
+            }
+        }
+    } else {
+        // quantise once: per 128-element block, a = max(amax, 1e-4),
+        // codes = e4m3(x * (448 / a)), scale = a / 448.  The block max is
+        // taken on the bf16 bits: magnitudes of finite values order like
+        // unsigned integers, so no float copy of the row stays live.
+        u32x2 q[VPL];
+        float scale[VPL];
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            const u32x4 u = v[i];
+            const uint32_t m01 = max_bf16_mag(u.x, u.y);
+            const uint32_t m23 = max_bf16_mag(u.z, u.w);
+            const uint32_t mw = m01 > m23 ? m01 : m23;
+            float am = __uint_as_float(mw << 16);
+            am = group16_max(am);
+            const float av = fmaxf(am, 1e-4f);
+            const float inv = 448.0f / av;
+            scale[i] = av / 448.0f;
+            uint32_t lo = e4m3x2<false>(bf16lo(u.x) * inv, bf16hi(u.x) * inv, 0);
+            lo = e4m3x2<true>(bf16lo(u.y) * inv, bf16hi(u.y) * inv, lo);
+            uint32_t hi = e4m3x2<false>(bf16lo(u.z) * inv, bf16hi(u.z) * inv, 0);
+            hi = e4m3x2<true>(bf16lo(u.w) * inv, bf16hi(u.w) * inv, hi);
+            q[i] = u32x2{lo, hi};
+        }
+        for (uint64_t m = dmask; m; m &= m - 1) {
+            const int r = __builtin_ctzll(m);
+            const int32_t s = bcast(s_lane, r);
+            if (s >= a.cap) continue;
+            // codes at [0, H), scales at [H, H + H/32)
+            const __amdgpu_buffer_rsrc_t row =
+                buffer_rsrc(a.send_buf + (int64_t)s * a.row_bytes, (int32_t)a.row_bytes);
+#pragma unroll
+            for (int i = 0; i < VPL; ++i) {
+                int vi = v0 + lane + i * kWave;
+                if (vi < a.nv) {
+                    __builtin_amdgcn_raw_buffer_store_b64(q[i], row, vi * 8, 0, kStoreSystem);
+                    if ((lane & 15) == 0)
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(scale[i]), row,
+                                                              a.H + vi / 16 * 4, 0, kStoreSystem);
+                }
+            }
+        }
+    }
+
+}
+
 // How a pack kernel publishes descriptors.
 //   kPubNone:   no ring.
 //   kPubStream: as messages complete, overlapping the copy.  After each
@@ -538,75 +623,7 @@ __global__ __launch_bounds__(WAVES * kWave) void pack_kernel(PackArgs a) {
         if (PUB == kPubClosed && s_lane >= 0 && (s_lane < a.rank_off[lane] || s_lane >= a.rank_off[lane + 1]))
             set_error(a.st, EP_ERR_INVALID_ARG);   // send_slot not from this rank_offset
 
-        // load this wavefront's chunk of the row: vectors v0 + lane + 64 i
-        const int v0 = chunk * VPL * kWave;
-        const u32x4* xr = a.x + t * a.nv;
-        u32x4 v[VPL];
-#pragma unroll
-        for (int i = 0; i < VPL; ++i) {
-            int vi = v0 + lane + i * kWave;
-            if (vi < a.nv) v[i] = xr[vi];
-            else v[i] = u32x4{0, 0, 0, 0};
-        }
-
-        if (FMT == EP_FMT_BF16) {
-            for (uint64_t m = dmask; m; m &= m - 1) {
-                const int r = __builtin_ctzll(m);
-                const int32_t s = bcast(s_lane, r);
-                if (s >= a.cap) continue;
-                const __amdgpu_buffer_rsrc_t dst =
-                    buffer_rsrc(a.send_buf + (int64_t)s * a.row_bytes, (int32_t)a.row_bytes);
-#pragma unroll
-                for (int i = 0; i < VPL; ++i) {
-                    int vi = v0 + lane + i * kWave;
-                    if (vi < a.nv)
-                        __builtin_amdgcn_raw_buffer_store_b128(v[i], dst, vi * 16, 0,
-                                                               kStoreSystem | kCacheNt);
-                }
-            }
-        } else {
-            // quantise once: per 128-element block, a = max(amax, 1e-4),
-            // codes = e4m3(x * (448 / a)), scale = a / 448.  The block max is
-            // taken on the bf16 bits: magnitudes of finite values order like
-            // unsigned integers, so no float copy of the row stays live.
-            u32x2 q[VPL];
-            float scale[VPL];
-#pragma unroll
-            for (int i = 0; i < VPL; ++i) {
-                const u32x4 u = v[i];
-                const uint32_t m01 = max_bf16_mag(u.x, u.y);
-                const uint32_t m23 = max_bf16_mag(u.z, u.w);
-                const uint32_t mw = m01 > m23 ? m01 : m23;
-                float am = __uint_as_float(mw << 16);
-                am = group16_max(am);
-                const float av = fmaxf(am, 1e-4f);
-                const float inv = 448.0f / av;
-                scale[i] = av / 448.0f;
-                uint32_t lo = e4m3x2<false>(bf16lo(u.x) * inv, bf16hi(u.x) * inv, 0);
-                lo = e4m3x2<true>(bf16lo(u.y) * inv, bf16hi(u.y) * inv, lo);
-                uint32_t hi = e4m3x2<false>(bf16lo(u.z) * inv, bf16hi(u.z) * inv, 0);
-                hi = e4m3x2<true>(bf16lo(u.w) * inv, bf16hi(u.w) * inv, hi);
-                q[i] = u32x2{lo, hi};
-            }
-            for (uint64_t m = dmask; m; m &= m - 1) {
-                const int r = __builtin_ctzll(m);
-                const int32_t s = bcast(s_lane, r);
-                if (s >= a.cap) continue;
-                // codes at [0, H), scales at [H, H + H/32)
-                const __amdgpu_buffer_rsrc_t row =
-                    buffer_rsrc(a.send_buf + (int64_t)s * a.row_bytes, (int32_t)a.row_bytes);
-#pragma unroll
-                for (int i = 0; i < VPL; ++i) {
-                    int vi = v0 + lane + i * kWave;
-                    if (vi < a.nv) {
-                        __builtin_amdgcn_raw_buffer_store_b64(q[i], row, vi * 8, 0, kStoreSystem);
-                        if ((lane & 15) == 0)
-                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(scale[i]), row,
-                                                                  a.H + vi / 16 * 4, 0, kStoreSystem);
-                    }
-                }
-            }
-        }
+        store_row_chunk<VPL, FMT>(a, t, chunk, s_lane, dmask);
 
         // per-slot metadata, written by the token's first chunk
         if (chunk == 0) {
@@ -668,6 +685,168 @@ __global__ __launch_bounds__(WAVES * kWave) void pack_kernel(PackArgs a) {
     }
 }
 
+// ------------------------------------------------------------ per-expert mode
+// Commands of the per-expert stream in closed form, by the whole last
+// workgroup.  Per channel c: its ranks r = c, c + C, ... ascending, each
+// rank's experts ascending, per expert the WRITEs of its <= 8-row messages
+// and then its ATOMIC (value cnt_e, dst_offset 4 * local expert).  Experts
+// are numbered in that order (o = position of the rank * epr + local index);
+// an LDS scan of their command counts gives every command its place.
+__device__ inline int ll_rank_at(int rp, int C, int q, int rem) {
+    int c, i;
+    if (rp < rem * (q + 1)) {
+        c = rp / (q + 1);
+        i = rp % (q + 1);
+    } else {
+        const int l2 = rp - rem * (q + 1);
+        c = rem + l2 / q;
+        i = l2 % q;
+    }
+    return c + i * C;
+}
+
+__device__ inline int ll_first_pos(int c, int q, int rem) {   // first rank position of channel c
+    return c < rem ? c * (q + 1) : rem * (q + 1) + (c - rem) * q;
+}
+
+template <int WAVES>
+__device__ void ll_closed_publish(const PackArgs& a) {
+    __shared__ int32_t s_start[kMaxE + 1];
+    __shared__ int32_t s_eo[kMaxE + 1];   // expert_offset, staged once
+    __shared__ int32_t s_wsum[WAVES];
+    __shared__ unsigned long long s_cbase[kMaxR];
+    constexpr int kT = WAVES * kWave;
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+    const int E = a.E, R = a.R, C = a.ring.channels, epr = a.epr;
+    const int q = R / C, rem = R % C;
+    for (int e = tid; e <= E; e += kT) s_eo[e] = a.exp_off[e];
+    __syncthreads();
+    // commands per expert, in stream order, scanned: thread tid sums a run
+    const int per = (E + kT - 1) / kT;
+    const int o0 = tid * per;
+    int32_t sum = 0;
+    for (int i = 0; i < per; ++i) {
+        const int o = o0 + i;
+        if (o < E) {
+            const int e = ll_rank_at(o / epr, C, q, rem) * epr + o % epr;
+            const int32_t cnt = s_eo[e + 1] - s_eo[e];
+            s_start[o] = (cnt + kMsgRows - 1) / kMsgRows + 1;
+            sum += s_start[o];
+        }
+    }
+    int32_t incl = sum;
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int32_t v = __shfl_up(incl, d);
+        if (lane >= d) incl += v;
+    }
+    if (lane == kWave - 1) s_wsum[wave] = incl;
+    __syncthreads();
+    int32_t run = incl - sum;
+    for (int w = 0; w < wave; ++w) run += s_wsum[w];
+    for (int i = 0; i < per; ++i) {
+        const int o = o0 + i;
+        if (o < E) {
+            const int32_t n = s_start[o];
+            s_start[o] = run;
+            run += n;
+        }
+    }
+    if (tid == kT - 1) s_start[E] = run;
+    __syncthreads();
+    const int32_t total = s_start[E];
+    // one reservation per channel for its whole stream
+    const int nch = C < R ? C : R;
+    if (tid < nch) {
+        const int32_t f = s_start[ll_first_pos(tid, q, rem) * epr];
+        const int32_t l = tid + 1 < nch ? s_start[ll_first_pos(tid + 1, q, rem) * epr] : total;
+        s_cbase[tid] = ring_reserve(a.ring, tid, (unsigned)(l - f));
+    }
+    __syncthreads();
+    const uint64_t rb = (uint64_t)a.row_bytes;
+    for (int32_t g0 = wave * kWave; g0 < total; g0 += kT) {
+        const int32_t g = g0 + lane;
+        const bool have = g < total;
+        // the expert (stream position o) that command g belongs to
+        int lo = 0, hi = E - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_start[mid] <= g) lo = mid;
+            else hi = mid - 1;
+        }
+        const int o = lo;
+        const int r = ll_rank_at(o / epr, C, q, rem);
+        const int le = o % epr;
+        const int e = r * epr + le;
+        const int c = r % C;
+        const int32_t eo = s_eo[e];
+        const int32_t cnt = s_eo[e + 1] - eo;
+        const int32_t nmsg = (cnt + kMsgRows - 1) / kMsgRows;
+        const int32_t local = g - s_start[o];
+        const bool write = local < nmsg;
+        const int32_t rows = write ? min(kMsgRows, cnt - local * kMsgRows) : 0;
+        const int32_t rbase = s_eo[r * epr];
+        const unsigned long long ticket =
+            have ? s_cbase[c] + (unsigned long long)(g - s_start[ll_first_pos(c, q, rem) * epr]) : 0;
+        ring_publish<false>(a.ring, have, c, ticket, write ? EP_CMD_WRITE : EP_CMD_ATOMIC,
+                            write ? 0 : EP_ATOMIC_ADD, (uint32_t)rows, (uint32_t)r,
+                            write ? (uint32_t)(rows * rb) : (uint32_t)cnt,
+                            write ? (uint64_t)(eo + local * kMsgRows) * rb : 0,
+                            write ? (uint64_t)(eo - rbase + local * kMsgRows) * rb
+                                  : (uint64_t)(4 * le),
+                            a.st);
+    }
+}
+
+// Per-expert pack: wavefront g takes chunk g % nchunks of token g / nchunks
+// and stores it to the row of every kept choice of the token (no dedup by
+// rank: a token naming an expert twice sends two rows); the token's first
+// chunk also writes each row's source token and gate.  With a ring, the last
+// workgroup to finish publishes every command in closed form.
+template <int VPL, int FMT, int WAVES, int PUB>
+__global__ __launch_bounds__(WAVES * kWave) void ll_pack_kernel(PackArgs a) {
+    const int lane = lane_id();
+    const int wave = (int)(threadIdx.x / kWave);
+    const int64_t Q = a.exp_off[a.E];
+    const bool cap_ok = Q <= a.cap;
+    if (blockIdx.x == 0 && wave == 0) {
+        if (!cap_ok && lane == 0) set_error(a.st, EP_ERR_CAPACITY);
+        if (PUB == kPubClosed) refresh_tail_cache(a);
+    }
+    for (int64_t grp = blockIdx.x; grp < a.ngroups; grp += gridDim.x) {
+        const int64_t gw = grp * WAVES + wave;
+        const int64_t t = gw / a.nchunks;
+        const int chunk = (int)(gw - t * a.nchunks);
+        if (t >= a.T) continue;   // wavefront-uniform
+        int32_t s_lane = -1;
+        float w_lane = 0.0f;
+        if (lane < a.k) {
+            const int e = a.idx[t * a.k + lane];
+            if (e >= 0 && e < a.E) {
+                s_lane = a.expert_slot[t * a.k + lane];
+                w_lane = a.w[t * a.k + lane];
+                if (s_lane < a.exp_off[e] || s_lane >= a.exp_off[e + 1])
+                    set_error(a.st, EP_ERR_INVALID_ARG);   // expert_slot not from this layout
+            }
+        }
+        const uint64_t dmask = __ballot(s_lane >= 0);
+        store_row_chunk<VPL, FMT>(a, t, chunk, s_lane, dmask);
+        if (chunk == 0 && s_lane >= 0 && s_lane < a.cap) {
+            a.slot_src[s_lane] = (int32_t)t;
+            a.slot_w[s_lane] = w_lane;
+        }
+    }
+    if (PUB == kPubClosed) {
+        __shared__ int s_last;
+        wait_vm();   // this wavefront's rows are complete (system-scope stores)
+        __syncthreads();
+        if (threadIdx.x == 0)
+            s_last = arrive_last(a.arrive) && cap_ok && read_status(a.st) == 0;
+        __syncthreads();
+        if (!s_last) return;
+        ll_closed_publish<WAVES>(a);
+    }
+}
+
 }  // namespace ep
 
 using namespace ep;
@@ -688,10 +867,11 @@ int64_t pack_grid_cap() {
     return cap;
 }
 
-// SMALL: the small-batch configuration (closed-form publication).
-template <int VPL, int FMT, int WAVES, bool SMALL>
+// SMALL: the small-batch configuration (closed-form publication).  LL: the
+// per-expert pack (always closed-form publication with a ring).
+template <int VPL, int FMT, int WAVES, bool SMALL, bool LL>
 int launch_pack_fmt(PackArgs a, int64_t waves, hipStream_t stream) {
-    const int pub = !a.has_ring ? kPubNone : SMALL ? kPubClosed : kPubStream;
+    const int pub = !a.has_ring ? kPubNone : (SMALL || LL) ? kPubClosed : kPubStream;
     a.ngroups = ceil_div(waves, WAVES);
     // keep about the same number of wavefronts resident whatever WAVES is,
     // and give every workgroup the same number of passes (+-1 group), so no
@@ -701,7 +881,14 @@ int launch_pack_fmt(PackArgs a, int64_t waves, hipStream_t stream) {
     const int64_t blocks = ceil_div(a.ngroups, passes);
     const dim3 grid((unsigned)blocks), block(WAVES * kWave);
     clear_hip_error();
-    if (pub == kPubNone)
+    if (LL) {
+        if (pub == kPubNone)
+            hipLaunchKernelGGL((ll_pack_kernel<VPL, FMT, WAVES, kPubNone>), grid, block, 0, stream,
+                               a);
+        else
+            hipLaunchKernelGGL((ll_pack_kernel<VPL, FMT, WAVES, kPubClosed>), grid, block, 0,
+                               stream, a);
+    } else if (pub == kPubNone)
         hipLaunchKernelGGL((pack_kernel<VPL, FMT, WAVES, kPubNone>), grid, block, 0, stream, a);
     else if (pub == kPubClosed)
         hipLaunchKernelGGL((pack_kernel<VPL, FMT, WAVES, kPubClosed>), grid, block, 0, stream, a);
@@ -711,28 +898,66 @@ int launch_pack_fmt(PackArgs a, int64_t waves, hipStream_t stream) {
     return EP_OK;
 }
 
-template <int VPL, int WAVES, bool SMALL>
+template <int VPL, int WAVES, bool SMALL, bool LL>
 int launch_pack_wg(const PackArgs& a, int fmt, int64_t waves, hipStream_t stream) {
     if (fmt == EP_FMT_BF16)
-        return launch_pack_fmt<VPL, EP_FMT_BF16, WAVES, SMALL>(a, waves, stream);
-    return launch_pack_fmt<VPL, EP_FMT_FP8_E4M3_B128, WAVES, SMALL>(a, waves, stream);
+        return launch_pack_fmt<VPL, EP_FMT_BF16, WAVES, SMALL, LL>(a, waves, stream);
+    return launch_pack_fmt<VPL, EP_FMT_FP8_E4M3_B128, WAVES, SMALL, LL>(a, waves, stream);
 }
 
-template <int VPL>
+template <int VPL, bool LL>
 int launch_pack(const PackArgs& a, int fmt, int64_t waves, hipStream_t stream) {
     // fp8 holds the codes and scales too: half the wavefronts per workgroup
     // keep its registers (a 1024-thread workgroup caps a lane at 128)
-    if (fmt == EP_FMT_BF16) return launch_pack_wg<VPL, kPackWaves, false>(a, fmt, waves, stream);
-    return launch_pack_wg<VPL, kPackWavesFp8, false>(a, fmt, waves, stream);
+    if (fmt == EP_FMT_BF16)
+        return launch_pack_wg<VPL, kPackWaves, false, LL>(a, fmt, waves, stream);
+    return launch_pack_wg<VPL, kPackWavesFp8, false, LL>(a, fmt, waves, stream);
 }
 
 // Small batches: short chunks and small workgroups spread the rows over the
 // chip (a large workgroup of whole-row wavefronts would sit on a few CUs),
 // and the descriptors go out in closed form at the end: with few rows, the
 // copy is short and the publication latency is what remains.
-template <int VPL>
+template <int VPL, bool LL>
 int launch_pack_small(const PackArgs& a, int fmt, int64_t waves, hipStream_t stream) {
-    return launch_pack_wg<VPL, kPackWavesSmall, true>(a, fmt, waves, stream);
+    return launch_pack_wg<VPL, kPackWavesSmall, true, LL>(a, fmt, waves, stream);
+}
+
+// Vectors per lane and chunking of a pack launch (shared by both modes), then
+// the launch.
+template <bool LL>
+int launch_pack_any(PackArgs& a, int fmt, hipStream_t stream) {
+    // vectors per lane: one pass over the row when it fits (bf16: 16 per
+    // lane); fp8 also holds the codes and scales, so it takes at most 8
+    int vpl;
+    if (a.nv <= 64) vpl = 1;
+    else if (a.nv <= 128) vpl = 2;
+    else if (a.nv <= 256) vpl = 4;
+    else if (a.nv <= 512) vpl = 8;
+    else if (fmt != EP_FMT_BF16) vpl = a.nv <= 896 ? kPackVplFp8H7168 : 8;
+    else if (a.nv <= 896) vpl = kPackVplH7168;
+    else vpl = 16;
+    a.nchunks = (int32_t)ceil_div(a.nv, (int64_t)vpl * kWave);
+    int64_t waves = (int64_t)a.T * a.nchunks;
+    if (waves < kPackSmallWaves) {
+        vpl = a.nv <= 64 ? 1 : 2;
+        a.nchunks = (int32_t)ceil_div(a.nv, (int64_t)vpl * kWave);
+        waves = (int64_t)a.T * a.nchunks;
+        if (waves == 0) {
+            if (!a.has_ring) return EP_OK;
+            waves = 1;   // the zero-count ATOMICs still go out
+        }
+        return vpl == 1 ? launch_pack_small<1, LL>(a, fmt, waves, stream)
+                        : launch_pack_small<2, LL>(a, fmt, waves, stream);
+    }
+    switch (vpl) {
+        case 1: return launch_pack<1, LL>(a, fmt, waves, stream);
+        case 2: return launch_pack<2, LL>(a, fmt, waves, stream);
+        case 4: return launch_pack<4, LL>(a, fmt, waves, stream);
+        case 8: return launch_pack<8, LL>(a, fmt, waves, stream);
+        case 14: return launch_pack<14, LL>(a, fmt, waves, stream);
+        default: return launch_pack<16, LL>(a, fmt, waves, stream);
+    }
 }
 
 }  // namespace
@@ -784,36 +1009,48 @@ extern "C" int ep_dispatch(const ep_shape_t* shape, const void* x, const int32_t
     a.epr = s.E / s.R;
     a.nv = s.H / 8;
 
-    // vectors per lane: one pass over the row when it fits (bf16: 16 per
-    // lane); fp8 also holds the codes and scales, so it takes at most 8
-    int vpl;
-    if (a.nv <= 64) vpl = 1;
-    else if (a.nv <= 128) vpl = 2;
-    else if (a.nv <= 256) vpl = 4;
-    else if (a.nv <= 512) vpl = 8;
-    else if (s.fmt != EP_FMT_BF16) vpl = a.nv <= 896 ? kPackVplFp8H7168 : 8;
-    else if (a.nv <= 896) vpl = kPackVplH7168;
-    else vpl = 16;
-    a.nchunks = (int32_t)ceil_div(a.nv, (int64_t)vpl * kWave);
-    int64_t waves = (int64_t)s.T * a.nchunks;
-    if (waves < kPackSmallWaves) {
-        vpl = a.nv <= 64 ? 1 : 2;
-        a.nchunks = (int32_t)ceil_div(a.nv, (int64_t)vpl * kWave);
-        waves = (int64_t)s.T * a.nchunks;
-        if (waves == 0) {
-            if (!a.has_ring) return EP_OK;
-            waves = 1;   // the zero-count ATOMICs still go out
-        }
-        return vpl == 1 ? launch_pack_small<1>(a, s.fmt, waves, stream)
-                        : launch_pack_small<2>(a, s.fmt, waves, stream);
-    }
-    switch (vpl) {
-        case 1: return launch_pack<1>(a, s.fmt, waves, stream);
-        case 2: return launch_pack<2>(a, s.fmt, waves, stream);
-        case 4: return launch_pack<4>(a, s.fmt, waves, stream);
-        case 8: return launch_pack<8>(a, s.fmt, waves, stream);
-        case 7: return launch_pack<7>(a, s.fmt, waves, stream);
-        case 14: return launch_pack<14>(a, s.fmt, waves, stream);
-        default: return launch_pack<16>(a, s.fmt, waves, stream);
-    }
+    return launch_pack_any<false>(a, s.fmt, stream);
+}
+
+extern "C" int ep_dispatch_ll(const ep_shape_t* shape, const void* x, const int32_t* topk_idx,
+                              const float* topk_w, const int32_t* expert_offset,
+                              const int32_t* expert_slot, void* send_buf, int64_t capacity_rows,
+                              int32_t* slot_src, float* slot_w, ep_ring_t* ring, void* workspace,
+                              size_t ws_bytes, int32_t* dev_status, hipStream_t stream) {
+    int v = validate_shape(shape);
+    if (v != EP_OK) return v;
+    const ep_shape_t s = *shape;
+    if (!expert_offset || !dev_status || !workspace || capacity_rows < 0)
+        return EP_ERR_INVALID_ARG;
+    if (s.T > 0 && (!x || !topk_idx || !topk_w || !expert_slot)) return EP_ERR_INVALID_ARG;
+    if (capacity_rows > 0 && (!send_buf || !slot_src || !slot_w)) return EP_ERR_INVALID_ARG;
+    if (((uintptr_t)x | (uintptr_t)send_buf) & 15) return EP_ERR_INVALID_ARG;
+    if (ws_bytes < workspace_bytes(s)) return EP_ERR_INVALID_ARG;
+    if (ring && (uint64_t)capacity_rows * row_bytes(s.H, s.fmt) > kMaxRingOffset)
+        return EP_ERR_INVALID_ARG;   // descriptor offsets are 48-bit
+    Workspace w = carve_workspace(s, workspace);
+
+    PackArgs a{};
+    a.x = reinterpret_cast<const u32x4*>(x);
+    a.idx = topk_idx;
+    a.w = topk_w;
+    a.exp_off = expert_offset;
+    a.expert_slot = expert_slot;
+    a.send_buf = reinterpret_cast<uint8_t*>(send_buf);
+    a.slot_src = slot_src;
+    a.slot_w = slot_w;
+    a.arrive = w.arrive;
+    a.st = dev_status;
+    a.ring = ring_device_view(ring);
+    a.has_ring = ring != nullptr;
+    a.cap = capacity_rows;
+    a.row_bytes = (int64_t)row_bytes(s.H, s.fmt);
+    a.T = s.T;
+    a.H = s.H;
+    a.E = s.E;
+    a.R = s.R;
+    a.k = s.k;
+    a.epr = s.E / s.R;
+    a.nv = s.H / 8;
+    return launch_pack_any<true>(a, s.fmt, stream);
 }

@@ -103,38 +103,59 @@ __device__ inline void block_exclusive_scan_store(const int32_t* v, int n, int32
 
 // Sum the [nrows, ncols] int32 matrix m over its rows into LDS acc[ncols]
 // (zeroed by the caller); rows < split also go to acc_pre (may be null).
-// Flat and fully parallel: 16-byte loads when ncols % 4 == 0, LDS atomics.
+// Flat and fully parallel: 16-byte loads when ncols % 4 == 0, issued in
+// batches of kSumBatch before any of them is added (one memory latency per
+// batch, not per load), then LDS atomics.
+constexpr int kSumBatch = 4;
 __device__ inline void column_sums(const int32_t* __restrict__ m, int nrows, int ncols, int split,
                                    int32_t* acc, int32_t* acc_pre) {
     const int64_t n = (int64_t)nrows * ncols;
     if ((ncols & 3) == 0) {
         const int4* m4 = reinterpret_cast<const int4*>(m);
         const int64_t n4 = n >> 2;
-#pragma unroll 4
-        for (int64_t i = threadIdx.x; i < n4; i += kBlock) {
-            const int4 q = m4[i];
-            const int e0 = (int)(i * 4);
-            const int row = e0 / ncols;
-            const int col = e0 - row * ncols;
-            atomicAdd(&acc[col], q.x);
-            atomicAdd(&acc[col + 1], q.y);
-            atomicAdd(&acc[col + 2], q.z);
-            atomicAdd(&acc[col + 3], q.w);
-            if (acc_pre && row < split) {
-                atomicAdd(&acc_pre[col], q.x);
-                atomicAdd(&acc_pre[col + 1], q.y);
-                atomicAdd(&acc_pre[col + 2], q.z);
-                atomicAdd(&acc_pre[col + 3], q.w);
+        for (int64_t i0 = threadIdx.x; i0 < n4; i0 += (int64_t)kBlock * kSumBatch) {
+            int4 q[kSumBatch];
+#pragma unroll
+            for (int u = 0; u < kSumBatch; ++u) {
+                const int64_t i = i0 + (int64_t)u * kBlock;
+                q[u] = i < n4 ? m4[i] : int4{0, 0, 0, 0};
+            }
+#pragma unroll
+            for (int u = 0; u < kSumBatch; ++u) {
+                const int64_t i = i0 + (int64_t)u * kBlock;
+                if (i >= n4) break;
+                const int e0 = (int)(i * 4);
+                const int row = e0 / ncols;
+                const int col = e0 - row * ncols;
+                atomicAdd(&acc[col], q[u].x);
+                atomicAdd(&acc[col + 1], q[u].y);
+                atomicAdd(&acc[col + 2], q[u].z);
+                atomicAdd(&acc[col + 3], q[u].w);
+                if (acc_pre && row < split) {
+                    atomicAdd(&acc_pre[col], q[u].x);
+                    atomicAdd(&acc_pre[col + 1], q[u].y);
+                    atomicAdd(&acc_pre[col + 2], q[u].z);
+                    atomicAdd(&acc_pre[col + 3], q[u].w);
+                }
             }
         }
     } else {
-#pragma unroll 4
-        for (int64_t i = threadIdx.x; i < n; i += kBlock) {
-            const int32_t q = m[i];
-            const int row = (int)i / ncols;
-            const int col = (int)i - row * ncols;
-            atomicAdd(&acc[col], q);
-            if (acc_pre && row < split) atomicAdd(&acc_pre[col], q);
+        for (int64_t i0 = threadIdx.x; i0 < n; i0 += (int64_t)kBlock * kSumBatch) {
+            int32_t q[kSumBatch];
+#pragma unroll
+            for (int u = 0; u < kSumBatch; ++u) {
+                const int64_t i = i0 + (int64_t)u * kBlock;
+                q[u] = i < n ? m[i] : 0;
+            }
+#pragma unroll
+            for (int u = 0; u < kSumBatch; ++u) {
+                const int64_t i = i0 + (int64_t)u * kBlock;
+                if (i >= n) break;
+                const int row = (int)i / ncols;
+                const int col = (int)i - row * ncols;
+                atomicAdd(&acc[col], q[u]);
+                if (acc_pre && row < split) atomicAdd(&acc_pre[col], q[u]);
+            }
         }
     }
 }
@@ -350,6 +371,130 @@ __global__ __launch_bounds__(kBlock) void layout_main_kernel(
     if (SINGLE) zero_counters(counters, counters_n, tid, kBlock);
 }
 
+// ------------------------------------------------------------ per-expert mode
+// Row of every kept choice in the per-expert layout (UCCL-EP article s4.1,
+// low-latency mode: tokens go per expert; NCCL GIN article s3.1.1: each to
+// its expert's owner):
+//   expert_slot[t,j] = expert_offset[e] + #{kept (t',j') < (t,j) with e' = e}
+// in (t, j) order, e = topk_idx[t,j], or -1 for a dropped (or bad) choice.
+//
+// One wavefront per 64 tokens.  Its base per expert is expert_offset, plus
+// the counts of the earlier 256-token tiles (their histograms are still in
+// the workspace), plus the choices of the earlier 64-token groups of its own
+// tile (counted from topk_idx).  Inside the wavefront, every lane sets its
+// bit in an LDS mask per expert it names (64-bit atomic OR); a choice's place
+// among the same expert's choices of lower lanes is the popcount of that mask
+// below the lane.  A token naming an expert o+1 times takes part in o+1
+// rounds (round o: the masks of lanes with more than o such choices), so
+// repeats count once per choice.  No atomic decides an order: deterministic.
+__global__ __launch_bounds__(kWave) void ll_slot_kernel(
+    const int32_t* __restrict__ idx, int T, int E, int k,
+    const int32_t* __restrict__ blk_exp_cnt, const int32_t* __restrict__ exp_off,
+    int32_t* __restrict__ expert_slot, int32_t* st) {
+    __shared__ int32_t s_base[kMaxE];
+    __shared__ unsigned long long s_mask[kMaxE];
+    const int lane = threadIdx.x;
+    const int64_t q = blockIdx.x;                       // 64-token group
+    const int64_t tile = q / (kLayoutTile / kWave);      // its 256-token tile
+    const int64_t t_tile = tile * kLayoutTile;
+    const int64_t t = q * kWave + lane;
+    // this lane's choices: all loads issued before any is used
+    int32_t ids[kMaxK];
+    const int32_t* row = idx + t * k;
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) ids[j] = (j < k && t < T) ? row[j] : -1;
+    for (int e = lane; e < E; e += kWave) {
+        s_base[e] = 0;
+        s_mask[e] = 0ull;
+    }
+    __syncthreads();
+    // earlier tiles: rows < tile of the per-tile expert histograms
+    {
+        const int64_t n = tile * (int64_t)E;
+        constexpr int kBatch = 8;
+        for (int64_t i0 = lane; i0 < n; i0 += (int64_t)kWave * kBatch) {
+            int32_t v[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int64_t i = i0 + (int64_t)u * kWave;
+                v[u] = i < n ? blk_exp_cnt[i] : 0;
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int64_t i = i0 + (int64_t)u * kWave;
+                if (i < n && v[u]) atomicAdd(&s_base[(int)(i % E)], v[u]);
+            }
+        }
+    }
+    // earlier 64-token groups of this tile, from topk_idx
+    {
+        const int64_t n = (q * kWave - t_tile) * k;   // choices before this group in the tile
+        const int32_t* base = idx + t_tile * k;
+        constexpr int kBatch = 8;
+        for (int64_t i0 = lane; i0 < n; i0 += (int64_t)kWave * kBatch) {
+            int32_t v[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int64_t i = i0 + (int64_t)u * kWave;
+                v[u] = i < n ? base[i] : -1;
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u)
+                if (v[u] >= 0 && v[u] < E) atomicAdd(&s_base[v[u]], 1);
+        }
+    }
+    __syncthreads();
+    for (int e = lane; e < E; e += kWave) s_base[e] += exp_off[e];
+    // validate; occurrence of each choice among the lane's earlier choices
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+        if (ids[j] < -1 || ids[j] >= E) {
+            set_error(st, EP_ERR_BAD_EXPERT);
+            ids[j] = -1;
+        }
+    }
+    int32_t occ[kMaxK];
+    int my_rounds = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+        int o = 0;
+        if (j < k) {
+#pragma unroll
+            for (int i = 0; i < j; ++i) o += (ids[i] == ids[j]) ? 1 : 0;
+        }
+        occ[j] = o;
+        if (ids[j] >= 0 && o + 1 > my_rounds) my_rounds = o + 1;
+    }
+    int rounds = my_rounds;
+    for (int d = 1; d < kWave; d <<= 1) rounds = max(rounds, __shfl_xor(rounds, d));
+    const unsigned long long below = (1ull << lane) - 1ull;
+    int32_t pos[kMaxK];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) pos[j] = occ[j];
+    __syncthreads();
+    for (int o = 0; o < rounds; ++o) {
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j)
+            if (ids[j] >= 0 && occ[j] == o) atomicOr(&s_mask[ids[j]], 1ull << lane);
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j)
+            if (ids[j] >= 0) pos[j] += __popcll(s_mask[ids[j]] & below);
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j)
+            if (ids[j] >= 0) s_mask[ids[j]] = 0ull;
+        __syncthreads();
+    }
+    if (t < T) {
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j) {
+            if (j >= k) break;
+            expert_slot[t * k + j] = ids[j] >= 0 ? s_base[ids[j]] + pos[j] : -1;
+        }
+    }
+}
+
 // Tiles of the one-kernel layout that can be resident at once on the current
 // device (workgroups per CU from the occupancy calculator x CUs), or 0.
 int64_t max_resident_layout_tiles() {
@@ -413,6 +558,26 @@ extern "C" int ep_dispatch_layout(const ep_shape_t* shape, const int32_t* topk_i
                            w.msg_base, is_token_in_rank, send_slot, counters, w.counters_n,
                            w.barrier, dev_status);
     }
+    EP_HIP_CHECK(hipGetLastError());
+    return EP_OK;
+}
+
+extern "C" int ep_dispatch_layout_ll(const ep_shape_t* shape, const int32_t* topk_idx,
+                                     const int32_t* expert_offset, int32_t* expert_slot,
+                                     void* workspace, size_t ws_bytes, int32_t* dev_status,
+                                     hipStream_t stream) {
+    int v = validate_shape(shape);
+    if (v != EP_OK) return v;
+    const ep_shape_t s = *shape;
+    if (!expert_offset || !dev_status || !workspace) return EP_ERR_INVALID_ARG;
+    if (s.T == 0) return EP_OK;
+    if (!topk_idx || !expert_slot) return EP_ERR_INVALID_ARG;
+    if (ws_bytes < workspace_bytes(s)) return EP_ERR_INVALID_ARG;
+    Workspace w = carve_workspace(s, workspace);
+    clear_hip_error();
+    hipLaunchKernelGGL(ll_slot_kernel, dim3((unsigned)ceil_div(s.T, kWave)), dim3(kWave), 0, stream,
+                       topk_idx, s.T, s.E, s.k, w.blk_exp_cnt, expert_offset, expert_slot,
+                       dev_status);
     EP_HIP_CHECK(hipGetLastError());
     return EP_OK;
 }

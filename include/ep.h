@@ -191,6 +191,61 @@ int ep_combine(const ep_shape_t* shape, const void* y, int64_t y_rows,
                const int32_t* topk_idx, const float* topk_w, const int32_t* send_slot,
                void* out, int32_t* dev_status, hipStream_t stream);
 
+/* ---- Per-expert (low-latency) mode ------------------------------------------
+ * UCCL-EP s4.1 (low-latency mode: tokens are exchanged per expert, for small
+ * batches), NCCL GIN s3.1.1 (a token is sent to the owner of its expert).
+ * Every kept choice (t, j) (e_j != -1) is one row; no deduplication by rank,
+ * so a token naming an expert twice sends two rows.  Q = expert_offset[E] =
+ * the number of kept choices.  Expert e's rows are [expert_offset[e],
+ * expert_offset[e+1]) in ascending (t, j) order; since the experts of a rank
+ * are contiguous, so are a rank's rows. */
+
+/* The row of every choice: expert_slot[t*k + j] = expert_offset[e] + the
+ * number of kept choices (t', j') < (t, j) in (t, j) order naming the same
+ * expert e = topk_idx[t,j]; -1 for a dropped choice (or a bad id, reported as
+ * EP_ERR_BAD_EXPERT).
+ *   expert_offset int32 [E+1]  from ep_dispatch_layout
+ *   expert_slot   int32 [T,k]  output
+ * Must follow ep_dispatch_layout on the same stream with the same topk_idx
+ * and workspace: it reads the per-tile expert counts left there. */
+int ep_dispatch_layout_ll(const ep_shape_t* shape, const int32_t* topk_idx,
+                          const int32_t* expert_offset, int32_t* expert_slot,
+                          void* workspace, size_t workspace_bytes,
+                          int32_t* dev_status, hipStream_t stream);
+
+/* Per-expert pack and descriptors.  Row expert_slot[t,j] of send_buf gets
+ * x[t] (bf16, or its fp8 row as in ep_dispatch); metadata slot_src[s] = t and
+ * slot_w[s] = w[t,j] (the gate of that choice).
+ *   send_buf [capacity_rows, row bytes], 16-byte aligned; capacity_rows >= Q
+ *   slot_src int32 [capacity_rows], slot_w float [capacity_rows]
+ *   ring     may be NULL.  Otherwise, per expert e on rank r = e / (E/R), its
+ *            rows are cut into messages of <= 8 rows: WRITE{dst_rank r,
+ *            src_offset (expert_offset[e] + 8m) * row bytes, dst_offset
+ *            (expert_offset[e] - expert_offset[r*E/R] + 8m) * row bytes}, then
+ *            ATOMIC{ADD, value cnt_e, dst_offset 4 * (e - r*E/R)} (the
+ *            receiver's count word of that expert; also for cnt_e = 0).  Rank
+ *            r uses channel r % channels; per channel, ranks ascending, a
+ *            rank's experts ascending.  The commands are published once every
+ *            row is written (they are visible to other agents first).
+ * Device errors: EP_ERR_CAPACITY (rows >= capacity_rows are not written, no
+ * descriptor is emitted), EP_ERR_RING_TIMEOUT, EP_ERR_INVALID_ARG
+ * (expert_slot and expert_offset do not come from the same layout; no
+ * descriptor is emitted). */
+int ep_dispatch_ll(const ep_shape_t* shape, const void* x, const int32_t* topk_idx,
+                   const float* topk_w, const int32_t* expert_offset,
+                   const int32_t* expert_slot, void* send_buf, int64_t capacity_rows,
+                   int32_t* slot_src, float* slot_w, ep_ring_t* ring, void* workspace,
+                   size_t workspace_bytes, int32_t* dev_status, hipStream_t stream);
+
+/* Per-expert combine: y row expert_slot[t,j] is expert e_j's output for
+ * token t, and
+ *   out[t,:] = bf16_rne( sum over kept j ascending of w[t,j] * y[expert_slot[t,j], :] )
+ * accumulated with float fma.  y bf16 [y_rows,H] (y_rows >= Q), out bf16
+ * [T,H].  Device error: EP_ERR_CAPACITY if a row is >= y_rows (skipped). */
+int ep_combine_ll(const ep_shape_t* shape, const void* y, int64_t y_rows,
+                  const int32_t* topk_idx, const float* topk_w, const int32_t* expert_slot,
+                  void* out, int32_t* dev_status, hipStream_t stream);
+
 /* ---- TransferCmd ring (UCCL-EP s2.2, s2.3, s5.2) ---------------------------
  * `channels` FIFOs of `depth` slots each; a producer blocks while
  * `max_inflight` commands of its channel are published but not yet drained,

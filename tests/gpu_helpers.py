@@ -177,3 +177,92 @@ def combine_tolerance_check(got, ref, what=""):
         raise AssertionError(f"{what}: {int(bad.sum())} elements beyond tolerance, first {i.tolist()} "
                              f"gpu {got[tuple(i)]} ref {ref[tuple(i)]}")
     return float(err.max()) if err.size else 0.0, float((err / lim).max()) if err.size else 0.0
+
+
+def run_hip_ll(T, H, E, R, k, fmt, x, idx, w, capacity_rows=None, ring_cfg=None,
+               proxy_threads=4, poison=POISON, log_capacity=1 << 20, repeat=1):
+    """Per-expert mode through the C ABI: rank layout + per-expert row table +
+    per-expert pack (and descriptors when ring_cfg is given)."""
+    import combine_topk_rank_amd as ep
+    torch = torch_mod()
+    s = ep.shape(T, H, E, R, k, fmt)
+    cap = T * k if capacity_rows is None else capacity_rows
+    buf = ep.BuffersLL(s, capacity_rows=cap)
+    buf.send_buf.fill_(poison)
+    buf.slot_src.fill_(-7)
+    buf.slot_w.fill_(float("nan"))
+    buf.expert_slot.fill_(-99)
+    d_x, d_idx, d_w = dev_bf16(x), dev(idx), dev(w)
+    ring = None
+    if ring_cfg is not None:
+        ring = ep.Ring(*ring_cfg)
+        if proxy_threads:
+            ring.proxy_start(proxy_threads, log_capacity)
+    logs = []
+    for _ in range(repeat):
+        buf.layout(d_idx)
+        buf.dispatch(d_x, d_idx, d_w, ring=ring)
+        torch.cuda.synchronize()
+    if ring is not None and proxy_threads:
+        logs.append(ring.proxy_stop(log_capacity))
+    return {
+        "num_tokens_per_expert": host(buf.num_tokens_per_expert),
+        "expert_offset": host(buf.expert_offset),
+        "expert_slot": host(buf.expert_slot),
+        "send_buf": host(buf.send_buf),
+        "slot_src": host(buf.slot_src),
+        "slot_w": host(buf.slot_w),
+        "status": int(host(buf.dev_status)[0]),
+        "logs": logs,
+        "ring": ring,
+        "buffers": buf,
+        "d_idx": d_idx,
+        "d_w": d_w,
+    }
+
+
+def run_hip_combine_ll(buf, y_bits: np.ndarray, d_idx, d_w):
+    import combine_topk_rank_amd as ep
+    torch = torch_mod()
+    y = dev_bf16(y_bits) if y_bits.shape[0] else torch.zeros((1, buf.shape.H), dtype=torch.bfloat16,
+                                                              device="cuda")
+    buf.dev_status.zero_()
+    buf.out.fill_(float("nan"))
+    ep.ep_combine_ll(buf.shape, y, d_idx, d_w, buf.expert_slot, buf.out, buf.dev_status)
+    torch.cuda.synchronize()
+    o = buf.out.view(torch.int16).cpu().numpy().view(np.uint16)
+    return W.bf16_bits_to_f32(o).astype(np.float64), int(host(buf.dev_status)[0])
+
+
+def assert_ll_equal(g, L, pk, Q):
+    """Per-expert layout and pack against the oracle, element by element."""
+    for key in ("num_tokens_per_expert", "expert_offset", "expert_slot"):
+        a, b = g[key], L[key]
+        if not np.array_equal(a, b):
+            bad = np.argwhere(a != b)[:5]
+            raise AssertionError(f"{key} differs at {bad.tolist()}")
+    a, b = g["send_buf"], pk["send_buf"]
+    if not np.array_equal(a, b):
+        rows = np.nonzero(np.any(a != b, axis=1))[0]
+        raise AssertionError(f"per-expert send_buf differs in {rows.size} rows, first {rows[:5].tolist()}")
+    n = min(Q, g["slot_src"].shape[0])
+    assert np.array_equal(g["slot_src"][:n], pk["slot_src"][:n])
+    assert np.array_equal(g["slot_w"][:n].view(np.uint32), pk["slot_w"][:n].view(np.uint32))
+    assert np.all(g["slot_src"][n:] == -7)
+
+
+def assert_stream_in_order(log_, want, channels, calls=1):
+    """Closed-form publication: per channel, the logged commands in ticket
+    order are the oracle's channel stream, once per call; tickets run
+    1, 2, ... without gaps."""
+    by_ch = collections.defaultdict(list)
+    for d in sorted(log_, key=lambda d: int(d["seq"])):
+        by_ch[int(d["dst_rank"]) % channels].append(d)
+    for c in range(channels):
+        exp_c = [cmd_key(d) for d in want if int(d["dst_rank"]) % channels == c]
+        got_c = by_ch.get(c, [])
+        assert len(got_c) == calls * len(exp_c), f"channel {c}: {len(got_c)} vs {calls * len(exp_c)}"
+        assert [int(d["seq"]) for d in got_c] == list(range(1, len(got_c) + 1))
+        for i in range(calls):
+            part = [cmd_key(d) for d in got_c[i * len(exp_c):(i + 1) * len(exp_c)]]
+            assert part == exp_c, f"channel {c}, call {i}: stream differs"

@@ -32,7 +32,7 @@ def ep():
 
 def test_exports_every_declared_symbol(ep):
     names = declared_functions()
-    assert len(names) >= 13
+    assert len(names) >= 16
     lib = ctypes.CDLL(ep.LIB_PATH)
     missing = [n for n in names if not hasattr(lib, n)]
     assert not missing, missing
@@ -72,6 +72,18 @@ def test_host_validation_rejects_without_launch(ep):
     # T = 0 combine is a no-op
     zero = ep.shape(0, 64, 16, 4, 2)
     assert L.ep_combine(ctypes.byref(zero), None, 0, None, None, None, None, 16, None) == 0
+    # per-expert mode: bad shape, missing pointers, misaligned buffers
+    assert L.ep_dispatch_layout_ll(ctypes.byref(bad), None, 16, 16, 256, 1 << 20, 16, None) == 1
+    assert L.ep_dispatch_layout_ll(ctypes.byref(good), None, 16, None, 256, 1 << 20, 16, None) == 1
+    assert L.ep_dispatch_layout_ll(ctypes.byref(good), 16, 16, 16, 256, 0, 16, None) == 1
+    assert L.ep_dispatch_ll(ctypes.byref(good), *([None] * 6), 0, None, None, None, None, 0,
+                            None, None) == 1
+    assert L.ep_dispatch_ll(ctypes.byref(good), 8, 16, 16, 16, 16, 256, 10, 16, 16, None, 256,
+                            1 << 20, 16, None) == 1
+    assert L.ep_combine_ll(ctypes.byref(good), None, 0, None, None, None, None, None, None) == 1
+    assert L.ep_combine_ll(ctypes.byref(good), 8, 4, 16, 16, 16, 16, 16, None) == 1
+    assert L.ep_combine_ll(ctypes.byref(zero), None, 0, None, None, None, None, 16, None) == 0
+    assert L.ep_dispatch_layout_ll(ctypes.byref(zero), None, 16, None, 256, 1 << 20, 16, None) == 0
 
 
 def test_ring_create_rejects_bad_arguments(ep):

@@ -1,0 +1,122 @@
+"""Per-expert (low-latency) mode on the GPU against the oracle, through the C
+ABI: row table, packed rows and metadata bit-exact, the closed-form command
+stream command for command, combine within 1e-2 * max(1, |ref|)."""
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle_pins as pins
+import workloads as W
+from gpu_helpers import (assert_ll_equal, assert_stream_in_order, combine_tolerance_check, log,
+                         run_hip_combine_ll, run_hip_ll)
+
+pytestmark = pytest.mark.gpu
+
+RING_TIMEOUT_NS = 5_000_000_000
+
+
+def _check_case(T, H, E, R, k, fmt, inp, C, depth, mif, cap_extra=3, repeat=1, y_seed=7):
+    idx, w, x = inp["topk_idx"], inp["topk_w"], inp["x"]
+    L = oracle.ll_layout(idx, E)
+    Q = L["Q"]
+    pk = oracle.ll_pack(x, w, L["expert_slot"], fmt, capacity_rows=Q + cap_extra)
+    want = oracle.ll_descriptors(L["num_tokens_per_expert"], L["expert_offset"], R,
+                                 oracle.row_bytes(H, fmt), C)
+    g = run_hip_ll(T, H, E, R, k, fmt, x, idx, w, capacity_rows=Q + cap_extra,
+                   ring_cfg=(depth, C, mif, RING_TIMEOUT_NS), repeat=repeat)
+    assert g["status"] == 0, g["status"]
+    assert_ll_equal(g, L, pk, Q)
+    lg, nd = g["logs"][0]
+    assert nd == repeat * len(want)
+    assert_stream_in_order(lg, want, C, calls=repeat)
+    if fmt == 0:
+        y = W.make_expert_outputs(Q, H, y_seed)
+        ref = oracle.ll_combine(y, idx, w, L["expert_slot"], H=H)
+        got, st = run_hip_combine_ll(g["buffers"], y, g["d_idx"], g["d_w"])
+        assert st == 0
+        combine_tolerance_check(got, ref, f"per-expert combine T={T}")
+        # identity experts: the packed rows come back, out = (sum_j w_j) * x
+        yi = g["send_buf"][:Q].view(np.uint16).reshape(Q, H)
+        got_i, st = run_hip_combine_ll(g["buffers"], yi, g["d_idx"], g["d_w"])
+        ref_i = oracle.ll_combine(yi, idx, w, L["expert_slot"], H=H)
+        combine_tolerance_check(got_i, ref_i, f"per-expert identity T={T}")
+    return g
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "train", "fp8"])
+def test_ll_workload_parity(name):
+    w = W.WORKLOADS[name]
+    inp = pins.workload_inputs(name)
+    log(f"[ll] workload {name}")
+    _check_case(w.T, w.H, w.E, w.R, w.k, w.fmt, inp, w.channels, w.depth, w.max_inflight)
+
+
+# (T, H, E, R, k, fmt, drop_prob, channels, depth, max_inflight)
+LL_CASES = [
+    (1, 8, 1, 1, 1, 0, 0.0, 1, 4, 1),
+    (0, 64, 16, 4, 2, 0, 0.0, 2, 8, 4),
+    (5, 16, 6, 3, 2, 0, 0.3, 2, 8, 2),
+    (300, 200, 64, 8, 6, 0, 0.1, 3, 16, 4),
+    (257, 512, 32, 16, 8, 1, 0.0, 4, 32, 8),
+    (700, 1024, 64, 64, 4, 0, 0.0, 64, 32, 8),
+    (600, 128, 4096, 64, 32, 0, 0.05, 8, 1024, 256),
+    (3000, 136, 256, 32, 8, 0, 0.2, 5, 1024, 64),
+]
+
+
+@pytest.mark.parametrize("case", LL_CASES, ids=lambda c: "T%d_H%d_E%d_R%d_k%d_f%d" % c[:6])
+def test_ll_random_case_parity(case):
+    T, H, E, R, k, fmt, drop, C, depth, mif = case
+    rng = np.random.default_rng(2000 + LL_CASES.index(case))
+    inp = W.make_random_case(rng, T, H, E, R, k, drop_prob=drop)
+    log(f"[ll] case {case}")
+    _check_case(T, H, E, R, k, fmt, inp, C, depth, mif)
+
+
+def test_ll_repeated_experts_and_repeat_calls():
+    """Tokens naming one expert several times send one row per choice; three
+    calls on one ring keep tickets consecutive and each call's stream whole."""
+    rng = np.random.default_rng(77)
+    T, H, E, R, k = 200, 64, 32, 8, 4
+    inp = W.make_random_case(rng, T, H, E, R, k)
+    idx = inp["topk_idx"].copy()
+    idx[::7, 1] = idx[::7, 0]
+    idx[::11, :] = idx[::11, :1]
+    inp = dict(inp, topk_idx=idx)
+    log("[ll] repeated experts, three calls")
+    _check_case(T, H, E, R, k, 0, inp, 3, 16, 4, repeat=3)
+
+
+def test_ll_capacity_and_inconsistent_rows():
+    import combine_topk_rank_amd as ep
+    import torch
+    from gpu_helpers import dev, dev_bf16
+    rng = np.random.default_rng(5)
+    T, H, E, R, k = 64, 64, 16, 4, 2
+    inp = W.make_random_case(rng, T, H, E, R, k)
+    L = oracle.ll_layout(inp["topk_idx"], E)
+    Q = L["Q"]
+    log("[ll] capacity shortfall")
+    g = run_hip_ll(T, H, E, R, k, 0, inp["x"], inp["topk_idx"], inp["topk_w"], capacity_rows=Q - 1,
+                   ring_cfg=(64, 1, 16, RING_TIMEOUT_NS))
+    assert g["status"] == ep.EP_ERR_CAPACITY
+    lg, nd = g["logs"][0]
+    assert nd == 0
+    pk = oracle.ll_pack(inp["x"], inp["topk_w"], L["expert_slot"], 0, capacity_rows=Q - 1)
+    assert np.array_equal(g["send_buf"], pk["send_buf"])
+    log("[ll] expert_slot from another layout")
+    s = ep.shape(T, H, E, R, k)
+    b = ep.BuffersLL(s)
+    d_idx, d_w, d_x = dev(inp["topk_idx"]), dev(inp["topk_w"]), dev_bf16(inp["x"])
+    b.layout(d_idx)
+    torch.cuda.synchronize()
+    bad_slot = torch.flip(b.expert_slot, dims=[0]).contiguous()
+    ring = ep.Ring(64, 1, 16, RING_TIMEOUT_NS)
+    ring.proxy_start(1, 1024)
+    ep.ep_dispatch_ll(s, d_x, d_idx, d_w, b.expert_offset, bad_slot, b.send_buf, b.slot_src,
+                      b.slot_w, ring, b.workspace, b.dev_status)
+    torch.cuda.synchronize()
+    lg, nd = ring.proxy_stop(1024)
+    assert int(b.dev_status.item()) == ep.EP_ERR_INVALID_ARG
+    assert nd == 0

@@ -151,6 +151,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="train")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step (layout, dispatch, combine) in a HIP graph and time "
+                         "its replays (per-op times are then not sampled)")
     ap.add_argument("--mode", choices=("rank", "ll"), default="rank",
                     help="rank: one row per (token, rank) pair; ll: the per-expert "
                          "(low-latency) mode, one row per kept choice")
@@ -221,6 +224,28 @@ def main() -> int:
         if ev is not None:
             ev[3].record(stream)
 
+    graph = None
+    if args.graph:
+        # the library launches on torch's current stream, which is the capture
+        # stream inside the capture
+        def step_current():
+            b.layout(d_idx)
+            b.dispatch(d_x, d_idx, d_w, ring=ring)
+            b.combine(y, d_idx, d_w)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(max(2, args.warmup)):
+                step_current()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step_current()
+        torch.cuda.synchronize()
+
+        def step(ev=None):
+            graph.replay()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -237,7 +262,7 @@ def main() -> int:
 
     K = args.steps
     every = max(1, args.op_events_every)
-    sampled = [i for i in range(K) if i % every == 0]
+    sampled = [] if graph is not None else [i for i in range(K) if i % every == 0]
     evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(4)] for i in sampled}
     drained0 = ring.proxy_drained()
     torch.cuda.synchronize()
@@ -256,13 +281,20 @@ def main() -> int:
     def avg_ms(a, z):
         return sum(e[a].elapsed_time(e[z]) for e in evs.values()) / len(evs)
 
-    t_layout, t_disp, t_comb = avg_ms(0, 1), avg_ms(1, 2), avg_ms(2, 3)
+    if graph is None:
+        t_layout, t_disp, t_comb = avg_ms(0, 1), avg_ms(1, 2), avg_ms(2, 3)
+    else:
+        # no events inside a replay: split the step by the byte model instead
+        ms = elapsed * 1e3 / K
+        t_layout = ms * ab["layout"] / ab["total"]
+        t_disp = ms * ab["dispatch"] / ab["total"]
+        t_comb = ms * ab["combine"] / ab["total"]
 
     # cold: before each step, read 1 GiB so that the 256 MB memory-side
     # cache holds only clean lines of other data (a write flush would leave
     # dirty lines whose write-back then lands inside the timed step)
     cold = None
-    if args.cold_steps > 0:
+    if args.cold_steps > 0 and graph is None:
         scratch = torch.ones((1 << 30) // 4, dtype=torch.int32, device=dev)
         sink = torch.zeros((), dtype=torch.int64, device=dev)
         cev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.cold_steps)]
@@ -309,7 +341,7 @@ def main() -> int:
     else:
         dom = "combine_kernel (ep_combine_ll)" if ll else "combine_kernel (ep_combine)"
         dom_ms, dom_bytes, prefix = t_comb, ab["combine"], "combine_kernel"
-    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9 if graph is None else None
     traffic = measured_traffic(prefix, w.name + ("-ll" if ll else ""))
 
     cpu = None
@@ -343,12 +375,16 @@ def main() -> int:
         "algorithmic_bytes_per_step": ab,
         "per_op_us": {"layout": round(t_layout * 1e3, 2), "dispatch": round(t_disp * 1e3, 2),
                       "combine": round(t_comb * 1e3, 2),
-                      "note": f"HIP events on the launch stream, every {every}th of the {K} timed "
-                              f"steps ({len(evs)} samples)"},
+                      "note": (f"HIP events on the launch stream, every {every}th of the {K} timed "
+                               f"steps ({len(evs)} samples)") if graph is None else
+                              "graph replays: the step time split in proportion to the byte model, "
+                              "not measured per op"},
+        "graph": graph is not None,
         "descriptors_per_step": n_cmds,
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+        "roofline": {"bound": "hbm", "kernel": dom,
+                     "achieved": round(achieved, 1) if achieved is not None else None,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "frac": round(achieved / PEAK_HBM_GBS, 4) if achieved is not None else None,
                      "algorithmic_bytes": dom_bytes,
                      "traffic": traffic[0] if traffic else None,
                      "traffic_source": traffic[1] if traffic else None},

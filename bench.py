@@ -151,6 +151,10 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="train")
+    ap.add_argument("--loopback", action="store_true",
+                    help="proxy threads execute every command against per-rank receive regions "
+                         "and count words (copies on their own streams); the timed region then "
+                         "ends when every command has completed")
     ap.add_argument("--graph", action="store_true",
                     help="capture one step (layout, dispatch, combine) in a HIP graph and time "
                          "its replays (per-op times are then not sampled)")
@@ -208,6 +212,24 @@ def main() -> int:
         g = torch.Generator(device=dev).manual_seed(0)
         y = torch.randn((cap, w.H), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
     ring = ep.Ring(w.depth, w.channels, w.max_inflight, 10_000_000_000)
+    lb_bufs = None
+    if args.loopback:
+        # receive regions sized from one layout pass: rank r gets its rows
+        b.layout(d_idx)
+        torch.cuda.synchronize()
+        epr = w.E // w.R
+        if ll:
+            eo = b.expert_offset.cpu().numpy()
+            nrows = [int(eo[(r + 1) * epr] - eo[r * epr]) for r in range(w.R)]
+            nwords = epr
+        else:
+            ro = b.rank_offset.cpu().numpy()
+            nrows = [int(ro[r + 1] - ro[r]) for r in range(w.R)]
+            nwords = 1
+        recv = [torch.empty(max(n, 1) * b.row_bytes, dtype=torch.uint8, device=dev) for n in nrows]
+        cnt = [torch.zeros(nwords, dtype=torch.int32, device=dev) for _ in range(w.R)]
+        lb_bufs = (recv, cnt)
+        ring.set_loopback(b.send_buf, recv, cnt)
     ring.proxy_start(args.proxy_threads, 0)
     stream = torch.cuda.current_stream()
 
@@ -270,6 +292,8 @@ def main() -> int:
     for i in range(K):
         step(evs.get(i))
     torch.cuda.synchronize()
+    if lb_bufs is not None:
+        ring.wait_complete(60_000_000_000)
     t1 = time.perf_counter()
     elapsed = t1 - t0
     st = int(b.dev_status.item())
@@ -312,6 +336,7 @@ def main() -> int:
                 "GBps": round(ab["total"] / (tot * 1e-3) / 1e9, 1),
                 "note": "1 GiB read before each step; kernel spans from HIP events"}
         del scratch, sink
+    lb_stats = ring.loopback_stats() if lb_bufs is not None else None
     ring.proxy_stop(0)
     ring.destroy()
 
@@ -389,6 +414,11 @@ def main() -> int:
                      "traffic": traffic[0] if traffic else None,
                      "traffic_source": traffic[1] if traffic else None},
         "cold": cold,
+        "loopback": None if lb_stats is None else dict(
+            lb_stats,
+            note="commands executed by the proxy threads (row copies into per-rank receive "
+                 "regions, count adds); latency = pop to completion; the timed region ends "
+                 "when every command has completed"),
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -113,6 +113,18 @@ def _load() -> ctypes.CDLL:
     L.ep_ring_proxy_stop.restype = ctypes.c_int
     L.ep_ring_proxy_drained.argtypes = [P]
     L.ep_ring_proxy_drained.restype = i64
+    u64p = ctypes.POINTER(ctypes.c_uint64)
+    L.ep_ring_set_loopback.argtypes = [P, P, ctypes.c_uint64, i32, ctypes.POINTER(P), u64p,
+                                       ctypes.POINTER(P), u64p]
+    L.ep_ring_set_loopback.restype = ctypes.c_int
+    L.ep_ring_completed.argtypes = [P, i32]
+    L.ep_ring_completed.restype = i64
+    L.ep_ring_wait_complete.argtypes = [P, i64]
+    L.ep_ring_wait_complete.restype = ctypes.c_int
+    i64p = ctypes.POINTER(i64)
+    dp = ctypes.POINTER(ctypes.c_double)
+    L.ep_ring_loopback_stats.argtypes = [P, i64p, i64p, i64p, dp, dp]
+    L.ep_ring_loopback_stats.restype = ctypes.c_int
     L.ep_status_str.argtypes = [ctypes.c_int]
     L.ep_status_str.restype = ctypes.c_char_p
     L.ep_last_error.argtypes = []
@@ -259,6 +271,41 @@ class Ring:
                                       log_max, ctypes.byref(nl), ctypes.byref(nd)),
                "ep_ring_proxy_stop")
         return out[:min(nl.value, max(log_max, 0))], nd.value
+
+    def set_loopback(self, src, dst_list, count_list) -> None:
+        """Execute popped commands against local memory: src is the send
+        buffer, dst_list / count_list one device tensor (or None) per rank."""
+        if src is None:
+            _check(lib.ep_ring_set_loopback(self.handle, None, 0, 0, None, None, None, None),
+                   "ep_ring_set_loopback")
+            self._lb_keep = None
+            return
+        R = len(dst_list)
+        P = ctypes.c_void_p
+        dst = (P * R)(*[_ptr(t) for t in dst_list])
+        dsz = (ctypes.c_uint64 * R)(*[0 if t is None else t.numel() * t.element_size()
+                                      for t in dst_list])
+        cnt = (P * R)(*[_ptr(t) for t in count_list])
+        csz = (ctypes.c_uint64 * R)(*[0 if t is None else t.numel() * t.element_size()
+                                      for t in count_list])
+        self._lb_keep = (src, list(dst_list), list(count_list))   # keep the memory alive
+        _check(lib.ep_ring_set_loopback(self.handle, _ptr(src), src.numel() * src.element_size(),
+                                        R, dst, dsz, cnt, csz), "ep_ring_set_loopback")
+
+    def completed(self, channel: int) -> int:
+        return int(lib.ep_ring_completed(self.handle, channel))
+
+    def wait_complete(self, timeout_ns: int = 10_000_000_000) -> None:
+        _check(lib.ep_ring_wait_complete(self.handle, timeout_ns), "ep_ring_wait_complete")
+
+    def loopback_stats(self) -> dict:
+        n, e, c = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+        mean, mx = ctypes.c_double(), ctypes.c_double()
+        _check(lib.ep_ring_loopback_stats(self.handle, ctypes.byref(n), ctypes.byref(e),
+                                          ctypes.byref(c), ctypes.byref(mean), ctypes.byref(mx)),
+               "ep_ring_loopback_stats")
+        return {"completed": n.value, "errors": e.value, "copies": c.value,
+                "mean_latency_us": mean.value, "max_latency_us": mx.value}
 
     def proxy_drained(self) -> int:
         return int(lib.ep_ring_proxy_drained(self.handle))

@@ -286,6 +286,40 @@ int ep_ring_proxy_stop(ep_ring_t* ring, ep_transfer_cmd_t* log_out, int64_t log_
 /* Commands drained so far by the proxy threads (a live counter). */
 int64_t ep_ring_proxy_drained(const ep_ring_t* ring);
 
+/* Loopback execution target (UCCL-EP s2.3: the proxy executes each command it
+ * pops; s2.2: completions are tracked per command).  Host-only, while no
+ * proxy runs.  With src set, proxy threads started afterwards execute what
+ * they pop, each on its own stream, in ticket order per channel:
+ *   WRITE       copy size_or_value bytes from src + src_offset to
+ *               dst[dst_rank] + dst_offset (device to device); consecutive
+ *               WRITEs that continue each other become one copy;
+ *   ATOMIC ADD  add value to the int32 at counts[dst_rank] + dst_offset.
+ * A command is completed once its copy or add has finished.  Commands that
+ * fall outside the registered byte ranges (src_bytes, dst_bytes[r],
+ * count_bytes[r]) are skipped and counted as errors.  dst, dst_bytes, counts
+ * and count_bytes are host arrays of R entries (device pointers may be NULL
+ * with size 0); they are copied.  src = NULL switches loopback off. */
+int ep_ring_set_loopback(ep_ring_t* ring, const void* src, uint64_t src_bytes, int32_t R,
+                         void* const* dst, const uint64_t* dst_bytes, void* const* counts,
+                         const uint64_t* count_bytes);
+
+/* Commands of `channel` completed so far (-1 on bad arguments); a command
+ * with ticket t (its seq - 1) is complete once this exceeds t. */
+int64_t ep_ring_completed(const ep_ring_t* ring, int32_t channel);
+
+/* Block the calling host thread until every command published so far (the
+ * producers' ticket counters, read from the device) is completed.  Call it
+ * after the dispatch that published them has finished.  EP_ERR_RING_TIMEOUT
+ * after timeout_ns; EP_ERR_INVALID_ARG if loopback execution skipped a
+ * command (see ep_ring_set_loopback). */
+int ep_ring_wait_complete(ep_ring_t* ring, int64_t timeout_ns);
+
+/* Loopback counters since ep_ring_set_loopback: commands completed, commands
+ * skipped as errors, copies issued (after merging), and the mean and largest
+ * time from a command's pop to its completion, in microseconds. */
+int ep_ring_loopback_stats(const ep_ring_t* ring, int64_t* n_done, int64_t* n_errors,
+                           int64_t* n_copies, double* mean_latency_us, double* max_latency_us);
+
 /* Text of a status code. */
 const char* ep_status_str(int status);
 

@@ -34,7 +34,13 @@ def eprint(*a):
 
 
 def row_bytes(H: int, fmt: int) -> int:
+    """Payload bytes of one send-buffer row: the fp8 row's zero pad up to a
+    whole number of 128-byte lines is written but not counted."""
     return 2 * H if fmt == 0 else H + 4 * (H // 128)
+
+
+def row_pitch(H: int, fmt: int) -> int:
+    return row_bytes(H, fmt) if fmt == 0 else (row_bytes(H, fmt) + 127) // 128 * 128
 
 
 def algorithmic_bytes(w, P: int) -> dict:
@@ -114,14 +120,14 @@ def cpu_baseline(w, inp, budget_s: float, mode: str = "rank") -> dict:
             P = L["Q"]
             pk = oracle.ll_pack(inp["x"], inp["topk_w"], L["expert_slot"], w.fmt, capacity_rows=P)
             oracle.ll_descriptors(L["num_tokens_per_expert"], L["expert_offset"], w.R,
-                                  row_bytes(w.H, w.fmt), w.channels)
+                                  row_pitch(w.H, w.fmt), w.channels)
         else:
             L = oracle.layout(inp["topk_idx"], w.E, w.R)
             P = L["P"]
             pk = oracle.pack(inp["x"], inp["topk_idx"], inp["topk_w"], L["send_slot"], w.E, w.R,
                              w.fmt, capacity_rows=P)
             oracle.descriptors(L["num_tokens_per_rank"], L["rank_offset"],
-                               row_bytes(w.H, w.fmt), w.channels)
+                               row_pitch(w.H, w.fmt), w.channels)
         if w.fmt == 0:
             y = pk["send_buf"].view(np.uint16).reshape(P, w.H)
         else:

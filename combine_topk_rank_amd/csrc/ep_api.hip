@@ -17,8 +17,9 @@ void record_hip_error(hipError_t e, const char* what) {
 
 size_t row_bytes(int32_t H, int32_t fmt) {
     if (fmt == EP_FMT_BF16) return (size_t)2 * H;
-    // H code bytes, then one float scale per 128 elements
-    return (size_t)H + (size_t)4 * (H / 128);
+    // H code bytes, one float scale per 128 elements, then zero bytes up to a
+    // whole number of 128-byte lines, so that rows never share a cache line
+    return ((size_t)H + (size_t)4 * (H / 128) + 127) / 128 * 128;
 }
 
 int validate_shape(const ep_shape_t* p) {

@@ -554,23 +554,39 @@ __device__ inline void store_row_chunk(const PackArgs& a, int64_t t, int chunk, 
             hi = e4m3x2<true>(bf16lo(u.w) * inv, bf16hi(u.w) * inv, hi);
             q[i] = u32x2{lo, hi};
         }
+        // The tail of the row, [H, row_bytes), is 4-byte words: the scales of
+        // blocks 0 .. H/128 - 1, then zeros.  This chunk writes the words of
+        // its 4 VPL blocks, lane b holding block v0/16 + b (block 4i + l/16
+        // of the chunk sits in lane l of vector i); the last chunk also
+        // writes the zero words after them.  One store per destination
+        // instead of one per vector, and whole 128-byte lines.
+        static_assert(VPL <= 16, "a chunk's scales fit one wavefront");
+        const int nblk = a.H / 128;
+        const int nword = (int)((a.row_bytes - a.H) / 4);
+        const int w0 = v0 / 16;
+        const int wend = v0 + VPL * kWave >= a.nv ? nword : w0 + 4 * VPL;
+        float sg = 0.0f;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            const float g = __shfl(scale[i], (lane & 3) * 16);
+            if ((lane >> 2) == i) sg = g;
+        }
+        if (w0 + lane >= nblk) sg = 0.0f;
         for (uint64_t m = dmask; m; m &= m - 1) {
             const int r = __builtin_ctzll(m);
             const int32_t s = bcast(s_lane, r);
             if (s >= a.cap) continue;
-            // codes at [0, H), scales at [H, H + H/32)
             const __amdgpu_buffer_rsrc_t row =
                 buffer_rsrc(a.send_buf + (int64_t)s * a.row_bytes, (int32_t)a.row_bytes);
 #pragma unroll
             for (int i = 0; i < VPL; ++i) {
                 int vi = v0 + lane + i * kWave;
-                if (vi < a.nv) {
+                if (vi < a.nv)
                     __builtin_amdgcn_raw_buffer_store_b64(q[i], row, vi * 8, 0, kStoreSystem);
-                    if ((lane & 15) == 0)
-                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(scale[i]), row,
-                                                              a.H + vi / 16 * 4, 0, kStoreSystem);
-                }
             }
+            for (int wi = w0 + lane, j = 0; wi < wend; wi += kWave, ++j)
+                __builtin_amdgcn_raw_buffer_store_b32(j == 0 ? __float_as_uint(sg) : 0u, row,
+                                                      a.H + wi * 4, 0, kStoreSystem);
         }
     }
 

@@ -78,7 +78,8 @@ enum ep_status {
 /* Row format of the send buffer. */
 enum ep_format {
     EP_FMT_BF16 = 0,           /* a row is the token's H bf16 values: 2H bytes */
-    EP_FMT_FP8_E4M3_B128 = 1   /* H OCP e4m3 codes, then H/128 float scales */
+    EP_FMT_FP8_E4M3_B128 = 1   /* H OCP e4m3 codes, H/128 float scales, zero pad
+                                  to a multiple of 128 bytes */
 };
 
 /* TransferCmd types (UCCL-EP s3.1) and atomic ops (s3.2). */
@@ -113,7 +114,9 @@ typedef struct ep_transfer_cmd {
 
 typedef struct ep_ring ep_ring_t;
 
-/* Bytes of one send-buffer row: 2H for bf16, H + 4*(H/128) for fp8. */
+/* Bytes of one send-buffer row (the row pitch): 2H for bf16; for fp8,
+ * H + 4*(H/128) rounded up to a multiple of 128 (7424 at H = 7168), the bytes
+ * after the scales being zero. */
 size_t ep_row_bytes(int32_t H, int32_t fmt);
 
 /* Bytes of device workspace that ep_dispatch_layout and ep_dispatch need for

@@ -85,8 +85,11 @@ static float bf16_to_float(uint16_t b) {
 
 int64_t oracle_row_bytes(int H, int fmt) {
     if (fmt == ORC_FMT_BF16) return 2LL * H;
-    /* reading: H code bytes followed by H/128 fp32 scales, unpadded */
-    return (int64_t)H + 4LL * (H / 128);
+    /* reading: H code bytes, then H/128 fp32 scales, then zero bytes up to
+     * the next multiple of 128 (the row pitch is a whole number of 128-byte
+     * lines) */
+    int64_t payload = (int64_t)H + 4LL * (H / 128);
+    return (payload + 127) / 128 * 128;
 }
 
 /* ------------------------------------------------------------ routing layout
@@ -194,7 +197,8 @@ float oracle_e4m3_decode(uint8_t c) {
 }
 
 /* Quantise one bf16 row of H elements into the fp8 row format (reading):
- * H code bytes, then H/128 float32 scales.  Per 128-element block b (reading):
+ * H code bytes, then H/128 float32 scales, then zero padding to the row pitch
+ * (oracle_row_bytes).  Per 128-element block b (reading):
  *   amax = max |x_i|  (exact in float),  a = max(amax, 1e-4f),
  *   inv = 448 / a  (one IEEE float division),
  *   q_i = e4m3(x_i * inv)  (one IEEE float multiply, then the conversion),
@@ -220,6 +224,8 @@ void oracle_quantize_row(int H, const uint16_t* xrow, uint8_t* out_row) {
         float s = a / 448.0f;
         memcpy(scales + 4 * b, &s, 4);
     }
+    int64_t pitch = oracle_row_bytes(H, ORC_FMT_FP8);
+    for (int64_t i = (int64_t)H + 4LL * nb; i < pitch; i++) out_row[i] = 0;
 }
 
 /* ------------------------------------------------------------ pack

@@ -238,10 +238,15 @@ def pin_quantize(O, seed: int = 5):
         xb = W.f32_to_bf16_bits(x)
         xf = W.bf16_bits_to_f32(xb).astype(np.float64)
         row = O.quantize_row(xb)
-        assert row.size == H + 4 * (H // 128)
+        nb = H // 128
+        # the row: H codes, nb float32 scales, zero bytes up to a pitch that
+        # is the smallest whole number of 128-byte lines holding them
+        payload = H + 4 * nb
+        assert row.size % 128 == 0 and payload <= row.size < payload + 128
+        assert not row[payload:].any(), "pad bytes not zero"
         codes = row[:H]
-        scales = row[H:].view(np.float32).astype(np.float64)
-        for b in range(H // 128):
+        scales = row[H:payload].view(np.float32).astype(np.float64)
+        for b in range(nb):
             blk = slice(b * 128, (b + 1) * 128)
             amax = np.abs(xf[blk]).max()
             mag = codes[blk] & 0x7F

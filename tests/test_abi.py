@@ -40,7 +40,10 @@ def test_exports_every_declared_symbol(ep):
 
 def test_row_bytes(ep):
     assert ep.ep_row_bytes(7168, ep.EP_FMT_BF16) == 14336
-    assert ep.ep_row_bytes(7168, ep.EP_FMT_FP8_E4M3_B128) == 7392
+    # fp8: codes, scales, zero pad to a whole number of 128-byte lines
+    assert ep.ep_row_bytes(7168, ep.EP_FMT_FP8_E4M3_B128) == 7424
+    assert ep.ep_row_bytes(4096, ep.EP_FMT_FP8_E4M3_B128) == 4224
+    assert ep.ep_row_bytes(512, ep.EP_FMT_FP8_E4M3_B128) == 640
     assert ep.ep_row_bytes(512, ep.EP_FMT_BF16) == 1024
     assert ep.ep_row_bytes(7, ep.EP_FMT_BF16) == 0
     assert ep.ep_row_bytes(7168, 9) == 0

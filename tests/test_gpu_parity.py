@@ -86,7 +86,7 @@ def dequant_rows(rows: np.ndarray, H: int) -> np.ndarray:
     lut[codes_t | 0x80] = -vals
     lut[0x7F] = lut[0xFF] = np.nan
     codes = rows[:, :H]
-    scales = rows[:, H:].copy().view(np.float32).astype(np.float64)
+    scales = rows[:, H:H + 4 * (H // 128)].copy().view(np.float32).astype(np.float64)
     v = lut[codes] * np.repeat(scales, 128, axis=1)
     return W.f32_to_bf16_bits(v.astype(np.float32))
 

@@ -32,6 +32,8 @@ MUTANTS = {
     "quant_max_not_abs": ("float v = fabsf(bf16_to_float(xrow[b * 128 + i]));",
                           "float v = bf16_to_float(xrow[b * 128 + i]);"),
     "quant_scale_inverted": ("float s = a / 448.0f;", "float s = 448.0f / a;"),
+    "row_pitch_unpadded": ("return (payload + 127) / 128 * 128;", "return payload;"),
+    "row_pad_short": ("i < pitch; i++) out_row[i] = 0;", "i < pitch - 4; i++) out_row[i] = 0;"),
     "quant_block_64": ("float amax = 0.0f;\n        for (int i = 0; i < 128; i++) {",
                        "float amax = 0.0f;\n        for (int i = 0; i < 64; i++) {"),
     "meta_global_expert": ("slot_local_idx[(int64_t)s * k + j] = local ? e - r * epr : -1;",

@@ -617,7 +617,7 @@ __global__ __launch_bounds__(WAVES * kWave) void pack_kernel(PackArgs a) {
     const bool cap_ok = P <= a.cap;
     if (blockIdx.x == 0 && wave == 0) {
         if (!cap_ok && lane == 0) set_error(a.st, EP_ERR_CAPACITY);
-        if (PUB == kPubClosed) refresh_tail_cache(a);
+        if (PUB != kPubNone) refresh_tail_cache(a);
     }
     // stream publication runs when the ring exists and the rows fit
     const bool streaming = PUB == kPubStream && cap_ok;

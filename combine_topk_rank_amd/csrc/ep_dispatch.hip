@@ -124,9 +124,11 @@ struct RingCmd {
 // (best for a few commands per wavefront: each lane's 16-byte stores travel
 // on their own); otherwise cached stores and one system-scope release per
 // round (best for runs of consecutive slots, which leave the L2 as lines).
+// `seen0`, when not ~0, is the cached consumer position of channel c as the
+// caller already loaded it (saves this call a load).
 template <int N, bool SYS>
 __device__ void ring_publish_n(const RingDev& g, int n, int c, const unsigned long long* ticket,
-                               const RingCmd* cmd, int32_t* st) {
+                               const RingCmd* cmd, int32_t* st, unsigned long long seen0 = ~0ull) {
     if (!__ballot(n > 0)) return;
     const unsigned long long lim = (unsigned long long)g.max_inflight;
     unsigned long long* cache = g.tail_cache + (size_t)c * kPad;
@@ -135,7 +137,9 @@ __device__ void ring_publish_n(const RingDev& g, int n, int c, const unsigned lo
     unsigned long long seen = 0, t0 = 0;
     uint32_t pending = (1u << n) - 1u;
     bool polled = false;
-    if (pending) seen = __hip_atomic_load(cache, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (pending)
+        seen = seen0 != ~0ull ? seen0
+                              : __hip_atomic_load(cache, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     while (__ballot(pending != 0)) {
         bool progress = false;
         if (pending) {
@@ -225,18 +229,36 @@ __device__ void publish_empty_ranks(const PackArgs& a) {
 // are consecutive, so they fall into at most three consecutive messages;
 // each message gets one arrival atomic carrying the group's row count (x
 // chunks).  A message whose count completes is published (WRITE); the
-// rank's last message also publishes the rank's ATOMIC.  One publish round
-// (one release) per group.
+// rank's last message also publishes the rank's ATOMIC.
+//
+// The chain of memory round trips is kept short: the rank's rows and first
+// message (RankView) are loaded once per launch; the status word and the
+// channel's cached consumer position are loaded with the arrival atomics; the
+// WRITEs go out before the count of the rank's published messages returns,
+// which only the ATOMIC waits for.
+struct RankView {
+    int32_t o[kMaxR], cnt[kMaxR], mbase[kMaxR];   // rank r's first row, rows, first message
+};
+
+// Fill the workgroup's RankView (LDS); wavefront 0, once per launch.
+__device__ inline void load_rank_view(const PackArgs& a, RankView& v) {
+    const int lane = lane_id();
+    if (lane < a.R) {
+        const int32_t o = a.rank_off[lane];
+        v.o[lane] = o;
+        v.cnt[lane] = a.rank_off[lane + 1] - o;
+        v.mbase[lane] = a.msg_base[lane];
+    }
+}
+
 template <int W>
-__device__ void publish_group(const PackArgs& a, const int32_t (*slot)[kMaxR]) {
+__device__ void publish_group(const PackArgs& a, const RankView& rv,
+                              const int32_t (*slot)[kMaxR]) {
     const int lane = lane_id();
     const bool has = lane < a.R;
-    int32_t o = 0, cnt = 0, mbase = 0;
-    if (has) {
-        o = a.rank_off[lane];
-        cnt = a.rank_off[lane + 1] - o;
-        mbase = a.msg_base[lane];
-    }
+    const int C = a.ring.channels;
+    const int32_t o = has ? rv.o[lane] : 0, cnt = has ? rv.cnt[lane] : 0;
+    const int32_t mbase = has ? rv.mbase[lane] : 0;
     // rows per message, relative to the first message m0 the group touches
     int32_t m0 = -1, cnt3[3] = {0, 0, 0};
     bool bad = false;
@@ -257,7 +279,13 @@ __device__ void publish_group(const PackArgs& a, const int32_t (*slot)[kMaxR]) {
             }
         }
     }
-    // the (at most three) arrival atomics go out together: one latency
+    // the status, the cached consumer positions and the (at most three)
+    // arrival atomics go out together: one latency
+    const int32_t st0 = read_status(a.st);
+    unsigned long long tc = 0;
+    if (lane < C)
+        tc = __hip_atomic_load(a.ring.tail_cache + (size_t)lane * kPad, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
     int32_t old3[3] = {0, 0, 0};
     bool hit[3];
 #pragma unroll
@@ -269,7 +297,9 @@ __device__ void publish_group(const PackArgs& a, const int32_t (*slot)[kMaxR]) {
         }
         if (hit[i]) old3[i] = atomicAdd(&a.msg_arrivals[mbase + m0 + i], cnt3[i]);
     }
-    int32_t done_m[3];
+    // completed messages, in ascending order, in registers (no indexed
+    // private array)
+    int32_t done_m[3] = {0, 0, 0};
     int ndone = 0;
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
@@ -278,46 +308,51 @@ __device__ void publish_group(const PackArgs& a, const int32_t (*slot)[kMaxR]) {
         const int32_t nrows = min(kMsgRows, cnt - m * kMsgRows);
         if (old3[i] + cnt3[i] == nrows * a.nchunks) {
             a.msg_arrivals[mbase + m] = 0;   // every arrival is in: leave the counter clean
-            done_m[ndone++] = m;
+#pragma unroll
+            for (int q = 0; q <= i; ++q)
+                if (ndone == q) done_m[q] = m;
+            ++ndone;
         }
     }
     if (bad) set_error(a.st, EP_ERR_INVALID_ARG);
     if (!__ballot(ndone > 0)) return;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    const int c = lane % a.ring.channels;
-    unsigned long long tk[4] = {0, 0, 0, 0};
-    int ncmd = 0;
-    if (ndone > 0 && read_status(a.st) == 0) {
+    const int c = lane % C;
+    const unsigned long long seen = (unsigned long long)__shfl((long long)tc, c);
+    unsigned long long tk[3] = {0, 0, 0};
+    int nw = 0;
+    int32_t done = 0;
+    if (ndone > 0 && st0 == 0) {
         const unsigned long long t0 = ring_reserve(a.ring, c, (unsigned)ndone);
-        for (int i = 0; i < ndone; ++i) tk[i] = t0 + i;
-        ncmd = ndone;
+#pragma unroll
+        for (int i = 0; i < 3; ++i) tk[i] = t0 + i;
+        nw = ndone;
         // Count the messages into the rank once their WRITE tickets exist (the
         // added value depends on the ticket); the rank's last messages
         // reserve the ATOMIC's ticket, which then follows every WRITE ticket
         // of the rank.
-        const int32_t nmsgs = (cnt + kMsgRows - 1) / kMsgRows;
         const int32_t add = ndone + (int32_t)(t0 >> 62);
-        const int32_t done = atomicAdd(&a.rank_msgs_done[lane], add);
-        if (done + ndone == nmsgs) {
-            a.rank_msgs_done[lane] = 0;
-            tk[ncmd++] = ring_reserve(a.ring, c, 1);
-        }
+        done = atomicAdd(&a.rank_msgs_done[lane], add);
     }
     const uint64_t rb = (uint64_t)a.row_bytes;
-    RingCmd cmd[4];
+    RingCmd cmd[3];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        if (i < ndone) {
-            const int32_t m = done_m[i < 3 ? i : 0];
-            const int32_t nrows = min(kMsgRows, cnt - m * kMsgRows);
-            cmd[i] = RingCmd{EP_CMD_WRITE, 0, (uint32_t)nrows, (uint32_t)lane,
-                             (uint32_t)(nrows * rb), (uint64_t)(o + m * kMsgRows) * rb,
-                             (uint64_t)(m * kMsgRows) * rb};
-        } else {
-            cmd[i] = RingCmd{EP_CMD_ATOMIC, EP_ATOMIC_ADD, 0, (uint32_t)lane, (uint32_t)cnt, 0, 0};
-        }
+    for (int i = 0; i < 3; ++i) {
+        const int32_t m = done_m[i];
+        const int32_t nrows = min(kMsgRows, cnt - m * kMsgRows);
+        cmd[i] = RingCmd{EP_CMD_WRITE, 0, (uint32_t)nrows, (uint32_t)lane, (uint32_t)(nrows * rb),
+                         (uint64_t)(o + m * kMsgRows) * rb, (uint64_t)(m * kMsgRows) * rb};
     }
-    ring_publish_n<4, true>(a.ring, ncmd, c, tk, cmd, a.st);
+    ring_publish_n<3, true>(a.ring, nw, c, tk, cmd, a.st, seen);
+    bool atom = false;
+    unsigned long long ta = 0;
+    if (nw > 0 && done + ndone == (cnt + kMsgRows - 1) / kMsgRows) {
+        a.rank_msgs_done[lane] = 0;
+        ta = ring_reserve(a.ring, c, 1);
+        atom = true;
+    }
+    ring_publish<true>(a.ring, atom, c, ta, EP_CMD_ATOMIC, EP_ATOMIC_ADD, 0, (uint32_t)lane,
+                       (uint32_t)cnt, 0, 0, a.st);
 }
 
 // Closed-form command stream (every row written and released first).  Per
@@ -622,6 +657,8 @@ __global__ __launch_bounds__(WAVES * kWave) void pack_kernel(PackArgs a) {
     // stream publication runs when the ring exists and the rows fit
     const bool streaming = PUB == kPubStream && cap_ok;
     if (streaming && blockIdx.x == 0 && wave == 0) publish_empty_ranks(a);
+    __shared__ RankView rv;   // read by wavefront 0 only, which wrote it
+    if (streaming && wave == 0) load_rank_view(a, rv);
     // groups of kWaves wavefronts, taken in launch order; a workgroup that
     // finishes a group (rows, then descriptors) moves on to the next one
     int pass = 0;
@@ -675,7 +712,7 @@ __global__ __launch_bounds__(WAVES * kWave) void pack_kernel(PackArgs a) {
         // other wavefronts go on with the next group, whose slots go to the
         // other buffer; this one is written again only after the next
         // barrier, which wavefront 0 reaches once it is done here.
-        publish_group<kWaves>(a, s_slot[pass]);
+        publish_group<kWaves>(a, rv, s_slot[pass]);
     }
     }
 

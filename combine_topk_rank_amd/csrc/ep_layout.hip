@@ -18,6 +18,9 @@
 // When every tile can be resident at once, both passes run in one kernel
 // (layout_main_kernel<2>) whose tiles meet at a grid barrier instead of a
 // kernel boundary; one workgroup does everything when T fits one tile.
+// With several tiles, the second pass has one workgroup more than there are
+// tiles: it sums the tiles' expert histograms and scans them, in parallel
+// with the tiles' slot stores, so no tile carries the expert work.
 
 #include "ep_common.h"
 
@@ -160,6 +163,26 @@ __device__ inline void column_sums(const int32_t* __restrict__ m, int nrows, int
     }
 }
 
+// Totals of the [nrows, ncols] int32 matrix m over its rows, one column per
+// thread (consecutive threads read consecutive columns, so every load is
+// coalesced), kSumBatch * 4 rows in flight per thread; into LDS acc[ncols].
+__device__ inline void column_totals(const int32_t* __restrict__ m, int nrows, int ncols,
+                                     int32_t* acc) {
+    constexpr int kRows = kSumBatch * 4;
+    for (int c = threadIdx.x; c < ncols; c += kBlock) {
+        int32_t sum = 0;
+        for (int r0 = 0; r0 < nrows; r0 += kRows) {
+            int32_t q[kRows];
+#pragma unroll
+            for (int u = 0; u < kRows; ++u)
+                q[u] = r0 + u < nrows ? m[(int64_t)(r0 + u) * ncols + c] : 0;
+#pragma unroll
+            for (int u = 0; u < kRows; ++u) sum += q[u];
+        }
+        acc[c] = sum;
+    }
+}
+
 __device__ inline void zero_counters(int32_t* p, int64_t n, int64_t first, int64_t stride) {
     for (int64_t i = first; i < n; i += stride) p[i] = 0;
 }
@@ -192,6 +215,8 @@ __global__ __launch_bounds__(kBlock) void layout_count_kernel(
 // MODE 1: second pass after layout_count_kernel.
 // MODE 2: both passes in one kernel, the tiles meeting at a grid barrier
 //         (used only when every tile can be resident at once).
+// In modes 1 and 2 the grid has nblocks + 1 workgroups: workgroup nblocks
+// owns no tokens and computes the expert totals and offsets.
 template <int MODE>
 __global__ __launch_bounds__(kBlock) void layout_main_kernel(
     const int32_t* __restrict__ idx, int T, int E, int R, int k, int epr, int nblocks,
@@ -216,6 +241,8 @@ __global__ __launch_bounds__(kBlock) void layout_main_kernel(
     const int lane = lane_id();
     const int wave = tid / kWave;
     const int b = blockIdx.x;
+    // the extra workgroup of modes 1 and 2: expert totals and offsets only
+    const bool expert_wg = !SINGLE && b == nblocks;
 
     if (SINGLE || FUSED) {
         for (int e = tid; e < E; e += kBlock) s_hist[e] = 0;
@@ -223,22 +250,35 @@ __global__ __launch_bounds__(kBlock) void layout_main_kernel(
     }
     const int64_t t_first = (int64_t)b * kLayoutTile;
     const int64_t t = t_first + tid;
-    uint64_t mask =
-        token_rank_mask(idx, t, T, E, k, epr, st, (SINGLE || FUSED) ? s_hist : nullptr);
-    const uint64_t my_ball = wave_rank_counts(mask, R, s_wcnt[wave], s_ball[wave]);
+    uint64_t mask = 0, my_ball = 0;
+    if (!expert_wg) {
+        mask = token_rank_mask(idx, t, T, E, k, epr, st, (SINGLE || FUSED) ? s_hist : nullptr);
+        my_ball = wave_rank_counts(mask, R, s_wcnt[wave], s_ball[wave]);
+    }
     __syncthreads();
 
     if (FUSED) {
         // first pass: this tile's counts for the others, then meet them
-        if (tid < R) {
-            int32_t c = 0;
-            for (int w = 0; w < kBlock / kWave; ++w) c += s_wcnt[w][tid];
-            blk_rank_cnt[(int64_t)b * R + tid] = c;
+        if (!expert_wg) {
+            if (tid < R) {
+                int32_t c = 0;
+                for (int w = 0; w < kBlock / kWave; ++w) c += s_wcnt[w][tid];
+                blk_rank_cnt[(int64_t)b * R + tid] = c;
+            }
+            for (int e = tid; e < E; e += kBlock)
+                blk_exp_cnt[(int64_t)b * E + e] = s_hist[e];
         }
-        for (int e = tid; e < E; e += kBlock)
-            blk_exp_cnt[(int64_t)b * E + e] = s_hist[e];
         zero_counters(counters, counters_n, (int64_t)b * kBlock + tid, (int64_t)gridDim.x * kBlock);
         if (!grid_barrier<false>(bar, (uint32_t)gridDim.x, st)) return;
+    }
+
+    if (expert_wg) {
+        // per-expert totals of all tiles and their exclusive scan
+        column_totals(blk_exp_cnt, nblocks, E, s_exp);
+        __syncthreads();
+        for (int e = tid; e < E; e += kBlock) cnt_exp[e] = s_exp[e];
+        block_exclusive_scan_store(s_exp, E, exp_off, s_part);
+        return;
     }
 
     // rank totals and the prefix over earlier tiles
@@ -254,11 +294,8 @@ __global__ __launch_bounds__(kBlock) void layout_main_kernel(
             s_pre[tid] = 0;
             s_tot[tid] = 0;
         }
-        if (b == 0)
-            for (int e = tid; e < E; e += kBlock) s_exp[e] = 0;
         __syncthreads();
         column_sums(blk_rank_cnt, nblocks, R, b, s_tot, s_pre);
-        if (b == 0) column_sums(blk_exp_cnt, nblocks, E, 0, s_exp, nullptr);
     }
     __syncthreads();
     if (wave == 0) {
@@ -287,15 +324,6 @@ __global__ __launch_bounds__(kBlock) void layout_main_kernel(
                 msg_base[R] = mincl;
             }
         }
-    }
-    if (b == 0) {
-        // per-expert totals and their exclusive scan
-        for (int e = tid; e < E; e += kBlock) {
-            if (SINGLE) s_exp[e] = s_hist[e];   // (FUSED reads the tiles' totals)
-            cnt_exp[e] = s_exp[e];
-        }
-        __syncthreads();
-        block_exclusive_scan_store(s_exp, E, exp_off, s_part);
     }
     __syncthreads();
 
@@ -368,7 +396,17 @@ __global__ __launch_bounds__(kBlock) void layout_main_kernel(
         }
     }
     }
-    if (SINGLE) zero_counters(counters, counters_n, tid, kBlock);
+    if (SINGLE) {
+        // per-expert totals and their exclusive scan, while the slot stores
+        // complete
+        for (int e = tid; e < E; e += kBlock) {
+            s_exp[e] = s_hist[e];
+            cnt_exp[e] = s_hist[e];
+        }
+        __syncthreads();
+        block_exclusive_scan_store(s_exp, E, exp_off, s_part);
+        zero_counters(counters, counters_n, tid, kBlock);
+    }
 }
 
 // ------------------------------------------------------------ per-expert mode
@@ -542,8 +580,8 @@ extern "C" int ep_dispatch_layout(const ep_shape_t* shape, const int32_t* topk_i
                            num_tokens_per_rank, num_tokens_per_expert, rank_offset, expert_offset,
                            w.msg_base, is_token_in_rank, send_slot, counters, w.counters_n,
                            w.barrier, dev_status);
-    } else if (nb <= max_resident_layout_tiles()) {
-        hipLaunchKernelGGL(layout_main_kernel<2>, dim3(nb), dim3(kBlock), 0, stream, topk_idx, s.T,
+    } else if (nb + 1 <= max_resident_layout_tiles()) {
+        hipLaunchKernelGGL(layout_main_kernel<2>, dim3(nb + 1), dim3(kBlock), 0, stream, topk_idx, s.T,
                            s.E, s.R, s.k, epr, nb, w.blk_rank_cnt, w.blk_exp_cnt,
                            num_tokens_per_rank, num_tokens_per_expert, rank_offset, expert_offset,
                            w.msg_base, is_token_in_rank, send_slot, counters, w.counters_n,
@@ -552,7 +590,7 @@ extern "C" int ep_dispatch_layout(const ep_shape_t* shape, const int32_t* topk_i
         hipLaunchKernelGGL(layout_count_kernel, dim3(nb), dim3(kBlock), 0, stream, topk_idx, s.T,
                            s.E, s.R, s.k, epr, w.blk_rank_cnt, w.blk_exp_cnt, counters,
                            w.counters_n, dev_status);
-        hipLaunchKernelGGL(layout_main_kernel<1>, dim3(nb), dim3(kBlock), 0, stream, topk_idx, s.T,
+        hipLaunchKernelGGL(layout_main_kernel<1>, dim3(nb + 1), dim3(kBlock), 0, stream, topk_idx, s.T,
                            s.E, s.R, s.k, epr, nb, w.blk_rank_cnt, w.blk_exp_cnt,
                            num_tokens_per_rank, num_tokens_per_expert, rank_offset, expert_offset,
                            w.msg_base, is_token_in_rank, send_slot, counters, w.counters_n,

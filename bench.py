@@ -167,6 +167,9 @@ def main() -> int:
     ap.add_argument("--mode", choices=("rank", "ll"), default="rank",
                     help="rank: one row per (token, rank) pair; ll: the per-expert "
                          "(low-latency) mode, one row per kept choice")
+    ap.add_argument("--fused", choices=("auto", "on", "off"), default="auto",
+                    help="layout + dispatch in one call (ep_dispatch_fused; one kernel for "
+                         "T <= 256); auto: for batches of at most 256 tokens (rank mode)")
     ap.add_argument("--proxy-threads", type=int, default=4)
     ap.add_argument("--op-events-every", type=int, default=5,
                     help="record per-op HIP events on every n-th timed step (events between "
@@ -210,6 +213,7 @@ def main() -> int:
     d_w = torch.from_numpy(inp["topk_w"]).to(dev)
     s = ep.shape(w.T, w.H, w.E, w.R, w.k, w.fmt)
     ll = args.mode == "ll"
+    fused = not ll and (args.fused == "on" or (args.fused == "auto" and w.T <= 256))
     b = ep.BuffersLL(s, device=dev) if ll else ep.Buffers(s, device=dev)
     cap = b.capacity_rows
     if w.fmt == 0:
@@ -242,10 +246,14 @@ def main() -> int:
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        b.layout(d_idx, stream)
+        if not fused:
+            b.layout(d_idx, stream)
         if ev is not None:
             ev[1].record(stream)
-        b.dispatch(d_x, d_idx, d_w, ring=ring, stream=stream)
+        if fused:
+            b.dispatch_fused(d_x, d_idx, d_w, ring=ring, stream=stream)
+        else:
+            b.dispatch(d_x, d_idx, d_w, ring=ring, stream=stream)
         if ev is not None:
             ev[2].record(stream)
         b.combine(y, d_idx, d_w, stream)
@@ -257,8 +265,11 @@ def main() -> int:
         # the library launches on torch's current stream, which is the capture
         # stream inside the capture
         def step_current():
-            b.layout(d_idx)
-            b.dispatch(d_x, d_idx, d_w, ring=ring)
+            if fused:
+                b.dispatch_fused(d_x, d_idx, d_w, ring=ring)
+            else:
+                b.layout(d_idx)
+                b.dispatch(d_x, d_idx, d_w, ring=ring)
             b.combine(y, d_idx, d_w)
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
@@ -366,9 +377,11 @@ def main() -> int:
     if t_disp >= t_comb:
         if ll:
             dom, prefix = "ll_pack_kernel (ep_dispatch_ll)", "ll_pack_kernel"
+        elif fused:
+            dom, prefix = "fused_small_kernel (ep_dispatch_fused)", "fused_small_kernel"
         else:
             dom, prefix = "pack_kernel (ep_dispatch)", "pack_kernel"
-        dom_ms, dom_bytes = t_disp, ab["dispatch"]
+        dom_ms, dom_bytes = t_disp, ab["dispatch"] + (ab["layout"] if fused else 0)
     else:
         dom = "combine_kernel (ep_combine_ll)" if ll else "combine_kernel (ep_combine)"
         dom_ms, dom_bytes, prefix = t_comb, ab["combine"], "combine_kernel"
@@ -404,10 +417,13 @@ def main() -> int:
         "copy_ceiling_GBps": round(copy_gbs, 1),
         "pct_of_copy_ceiling": round(100 * value / copy_gbs, 2),
         "algorithmic_bytes_per_step": ab,
+        "fused_layout_dispatch": fused,
         "per_op_us": {"layout": round(t_layout * 1e3, 2), "dispatch": round(t_disp * 1e3, 2),
                       "combine": round(t_comb * 1e3, 2),
                       "note": (f"HIP events on the launch stream, every {every}th of the {K} timed "
-                               f"steps ({len(evs)} samples)") if graph is None else
+                               f"steps ({len(evs)} samples)" + ("; layout and dispatch are "
+                               "one call (ep_dispatch_fused): its time is under dispatch"
+                               if fused else "")) if graph is None else
                               "graph replays: the step time split in proportion to the byte model, "
                               "not measured per op"},
         "graph": graph is not None,

@@ -32,6 +32,7 @@
 // per-rank counts.
 
 #include "ep_common.h"
+#include "ep_route.h"
 
 namespace ep {
 RingDev ring_device_view(ep_ring_t* r);
@@ -69,6 +70,15 @@ struct PackArgs {
     const int32_t* exp_off;       // [E+1]
     const int32_t* expert_slot;   // [T, k]
     float* slot_w;                // [cap]
+    // one-kernel small batches: the layout outputs
+    int32_t* cnt_rank_out;        // [R]
+    int32_t* cnt_exp_out;         // [E]
+    int32_t* rank_off_out;        // [R+1]
+    int32_t* exp_off_out;         // [E+1]
+    uint8_t* in_rank_out;         // [T, R]
+    int32_t* send_slot_out;       // [T, R]
+    int32_t* msg_base_out;        // [R+1] (workspace)
+    int64_t counters_n;           // msg_arrivals .. rank_msgs_done
 };
 
 // ------------------------------------------------------------------ ring
@@ -370,7 +380,7 @@ struct ClosedOrder {
     int32_t total;    // all commands (wave-uniform)
 };
 
-__device__ inline ClosedOrder closed_order(const PackArgs& a) {
+__device__ inline ClosedOrder closed_order(const PackArgs& a, const int32_t* ro) {
     const int lane = lane_id();
     const int C = a.ring.channels, R = a.R;
     const int q = R / C, rem = R % C;   // channels < rem hold q + 1 ranks
@@ -386,8 +396,8 @@ __device__ inline ClosedOrder closed_order(const PackArgs& a) {
             i = l2 % q;
         }
         z.r = z.c + i * C;
-        z.o = a.rank_off[z.r];
-        z.cnt = a.rank_off[z.r + 1] - z.o;
+        z.o = ro[z.r];
+        z.cnt = ro[z.r + 1] - z.o;
         z.items = (z.cnt + kMsgRows - 1) / kMsgRows + 1;
     }
     int32_t incl = z.items;
@@ -535,20 +545,38 @@ constexpr int kPackGridPerCuNum = 1, kPackGridPerCuDen = 2;
 // bf16 copies 16-byte vectors; fp8 quantises the chunk once and stores codes
 // and scales.  Slots at or beyond the capacity are skipped.  All lanes of the
 // wavefront call this together.
-template <int VPL, int FMT>
-__device__ inline void store_row_chunk(const PackArgs& a, int64_t t, int chunk, int32_t s_lane,
-                                       uint64_t dmask) {
+// This wavefront's chunk of row t of x: vectors v0 + lane + 64 i.
+template <int VPL>
+__device__ inline void load_row_chunk(const PackArgs& a, int64_t t, int chunk, u32x4 (&v)[VPL]) {
     const int lane = lane_id();
-    // load this wavefront's chunk of the row: vectors v0 + lane + 64 i
     const int v0 = chunk * VPL * kWave;
     const u32x4* xr = a.x + t * a.nv;
-    u32x4 v[VPL];
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
         int vi = v0 + lane + i * kWave;
         if (vi < a.nv) v[i] = xr[vi];
         else v[i] = u32x4{0, 0, 0, 0};
     }
+}
+
+template <int VPL, int FMT>
+__device__ inline void store_row_chunk_v(const PackArgs& a, int chunk, int32_t s_lane,
+                                         uint64_t dmask, const u32x4 (&v)[VPL]);
+
+template <int VPL, int FMT>
+__device__ inline void store_row_chunk(const PackArgs& a, int64_t t, int chunk, int32_t s_lane,
+                                       uint64_t dmask) {
+    u32x4 v[VPL];
+    load_row_chunk<VPL>(a, t, chunk, v);
+    store_row_chunk_v<VPL, FMT>(a, chunk, s_lane, dmask, v);
+}
+
+// The stores of store_row_chunk, for a chunk already loaded into v.
+template <int VPL, int FMT>
+__device__ inline void store_row_chunk_v(const PackArgs& a, int chunk, int32_t s_lane,
+                                         uint64_t dmask, const u32x4 (&v)[VPL]) {
+    const int lane = lane_id();
+    const int v0 = chunk * VPL * kWave;
 
     if (FMT == EP_FMT_BF16) {
         for (uint64_t m = dmask; m; m &= m - 1) {
@@ -627,6 +655,32 @@ __device__ inline void store_row_chunk(const PackArgs& a, int64_t t, int chunk, 
 
 }
 
+// Metadata of token t's slots (one per destination rank, lane r holding the
+// slot of rank r): the source token, and per choice j the expert's index on
+// the slot's rank (or -1) and its gate (or 0).  Slots at or beyond the
+// capacity are skipped.  All lanes of the wavefront call this together.
+__device__ inline void store_slot_metadata(const PackArgs& a, int64_t t, int32_t s_lane,
+                                           uint64_t dmask) {
+    const int lane = lane_id();
+    int e = -1;
+    float wt = 0.0f;
+    if (lane < a.k) {
+        e = a.idx[t * a.k + lane];
+        wt = a.w[t * a.k + lane];
+    }
+    for (uint64_t m = dmask; m; m &= m - 1) {
+        const int r = __builtin_ctzll(m);
+        const int32_t s = bcast(s_lane, r);
+        if (s >= a.cap) continue;
+        if (lane < a.k) {
+            const bool local = e >= 0 && e < a.E && e / a.epr == r;
+            a.slot_local_idx[(int64_t)s * a.k + lane] = local ? e - r * a.epr : -1;
+            a.slot_local_w[(int64_t)s * a.k + lane] = local ? wt : 0.0f;
+        }
+        if (lane == 0) a.slot_src[s] = (int32_t)t;
+    }
+}
+
 // How a pack kernel publishes descriptors.
 //   kPubNone:   no ring.
 //   kPubStream: as messages complete, overlapping the copy.  After each
@@ -679,25 +733,7 @@ __global__ __launch_bounds__(WAVES * kWave) void pack_kernel(PackArgs a) {
         store_row_chunk<VPL, FMT>(a, t, chunk, s_lane, dmask);
 
         // per-slot metadata, written by the token's first chunk
-        if (chunk == 0) {
-            int e = -1;
-            float wt = 0.0f;
-            if (lane < a.k) {
-                e = a.idx[t * a.k + lane];
-                wt = a.w[t * a.k + lane];
-            }
-            for (uint64_t m = dmask; m; m &= m - 1) {
-                const int r = __builtin_ctzll(m);
-                const int32_t s = bcast(s_lane, r);
-                if (s >= a.cap) continue;
-                if (lane < a.k) {
-                    const bool local = e >= 0 && e < a.E && e / a.epr == r;
-                    a.slot_local_idx[(int64_t)s * a.k + lane] = local ? e - r * a.epr : -1;
-                    a.slot_local_w[(int64_t)s * a.k + lane] = local ? wt : 0.0f;
-                }
-                if (lane == 0) a.slot_src[s] = (int32_t)t;
-            }
-        }
+        if (chunk == 0) store_slot_metadata(a, t, s_lane, dmask);
     }
 
     if (!streaming) continue;   // uniform over the workgroup
@@ -722,7 +758,7 @@ __global__ __launch_bounds__(WAVES * kWave) void pack_kernel(PackArgs a) {
         // every command.
         __shared__ int s_last;
         __shared__ unsigned long long s_base[kMaxR];
-        const ClosedOrder z = closed_order(a);   // loads issued before the wait
+        const ClosedOrder z = closed_order(a, a.rank_off);   // loads issued before the wait
         wait_vm();   // this wavefront's rows are complete
         __syncthreads();
         if (threadIdx.x == 0) {
@@ -736,6 +772,147 @@ __global__ __launch_bounds__(WAVES * kWave) void pack_kernel(PackArgs a) {
         for (int32_t g0 = wave * kWave; g0 < z.total; g0 += kWaves * kWave)
             closed_publish(a, z, s_base, g0);
     }
+}
+
+// ------------------------------------------------- one-kernel small batches
+// Routing layout and pack of a batch of at most kFusedMaxT tokens in one
+// launch (UCCL-EP article s4.1: the low-latency path is for small decode
+// batches; its cost is latency, and a separate layout kernel is one more
+// chain of memory round trips and one more launch).  The layout is tiny
+// (T * k ids), so every workgroup computes all of it in LDS: wavefront w
+// builds the rank masks of tokens 64w .. 64w + 63 and its per-rank ballots;
+// the rank totals, offsets and every token's slots follow from the ballots.
+// No workgroup waits for another before copying.  Workgroup 0 also writes
+// the layout outputs that are not per token (counts, offsets, the expert
+// histogram and its scan, the message bases); the first chunk of each token
+// writes its send_slot and is_token_in_rank rows.  The rows, metadata and
+// closed-form publication are those of the small-batch pack.
+constexpr int kFusedMaxT = kPackWavesSmall * kWave;
+
+template <int VPL, int FMT>
+__global__ __launch_bounds__(kPackWavesSmall* kWave) void fused_small_kernel(PackArgs a) {
+    constexpr int kWaves = kPackWavesSmall;
+    static_assert(kWaves * kWave == kBlock, "the expert scan takes a kBlock-thread workgroup");
+    __shared__ uint64_t s_ball[kWaves][kMaxR];   // bit i: token 64w + i goes to rank r
+    __shared__ int32_t s_cnt[kWaves][kMaxR];     // tokens of wavefront w on rank r
+    __shared__ int32_t s_wbase[kWaves][kMaxR];   // first slot of rank r for wavefront w's tokens
+    __shared__ int32_t s_ro[kMaxR + 1];          // rank offsets
+    __shared__ int32_t s_hist[kMaxE];            // expert histogram (workgroup 0)
+    __shared__ int32_t s_part[kBlock];
+    __shared__ int s_last;
+    __shared__ unsigned long long s_base[kMaxR];
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+    const bool first = blockIdx.x == 0;
+    const int R = a.R;
+
+    // this wavefront's chunk of its first group, loaded before the layout so
+    // that the two memory latencies overlap
+    u32x4 v[VPL];
+    {
+        const int64_t gw = (int64_t)blockIdx.x * kWaves + wave;
+        const int64_t t = gw / a.nchunks;
+        if (blockIdx.x < a.ngroups && t < a.T)
+            load_row_chunk<VPL>(a, t, (int)(gw - t * a.nchunks), v);
+    }
+
+    // layout, in every workgroup
+    if (first)
+        for (int e = tid; e < a.E; e += kBlock) s_hist[e] = 0;
+    __syncthreads();
+    const uint64_t mask = token_rank_mask(a.idx, (int64_t)wave * kWave + lane, a.T, a.E, a.k,
+                                          a.epr, a.st, first ? s_hist : nullptr);
+    wave_rank_counts(mask, R, s_cnt[wave], s_ball[wave]);
+    __syncthreads();
+    if (wave == 0) {
+        int32_t tot = 0;
+        if (lane < R)
+            for (int w = 0; w < kWaves; ++w) tot += s_cnt[w][lane];
+        const int32_t msgs = (tot + kMsgRows - 1) / kMsgRows;
+        int32_t incl = tot, mincl = msgs;
+        for (int d = 1; d < kWave; d <<= 1) {
+            const int32_t o = __shfl_up(incl, d);
+            const int32_t mo = __shfl_up(mincl, d);
+            if (lane >= d) {
+                incl += o;
+                mincl += mo;
+            }
+        }
+        const int32_t off = incl - tot;
+        if (lane < R) {
+            s_ro[lane] = off;
+            int32_t run = off;
+            for (int w = 0; w < kWaves; ++w) {
+                s_wbase[w][lane] = run;
+                run += s_cnt[w][lane];
+            }
+        }
+        if (lane == R - 1) s_ro[R] = incl;
+        if (first) {
+            if (lane < R) {
+                a.cnt_rank_out[lane] = tot;
+                a.rank_off_out[lane] = off;
+                a.msg_base_out[lane] = mincl - msgs;
+            }
+            if (lane == R - 1) {
+                a.rank_off_out[R] = incl;
+                a.msg_base_out[R] = mincl;
+            }
+        }
+    }
+    __syncthreads();
+
+    // rows: wavefront g of the grid takes chunk g % nchunks of token g / nchunks
+    const int64_t P = s_ro[R];
+    const bool cap_ok = P <= a.cap;
+    if (first && wave == 0) {
+        if (!cap_ok && lane == 0) set_error(a.st, EP_ERR_CAPACITY);
+        if (a.has_ring) refresh_tail_cache(a);
+    }
+    for (int64_t grp = blockIdx.x; grp < a.ngroups; grp += gridDim.x) {
+        const int64_t gw = grp * kWaves + wave;
+        const int64_t t = gw / a.nchunks;
+        const int chunk = (int)(gw - t * a.nchunks);
+        if (t >= a.T) continue;   // wavefront-uniform
+        if (grp != blockIdx.x) load_row_chunk<VPL>(a, t, chunk, v);
+        const int tw = (int)(t / kWave), tl = (int)(t % kWave);
+        int32_t s_lane = -1;
+        uint32_t bit = 0;
+        if (lane < R) {
+            const uint64_t b = s_ball[tw][lane];
+            bit = (uint32_t)((b >> tl) & 1ull);
+            if (bit) s_lane = s_wbase[tw][lane] + (int32_t)__popcll(b & ((1ull << tl) - 1ull));
+        }
+        const uint64_t dmask = __ballot(s_lane >= 0);
+        store_row_chunk_v<VPL, FMT>(a, chunk, s_lane, dmask, v);
+        if (chunk == 0) {
+            store_slot_metadata(a, t, s_lane, dmask);
+            if (lane < R) {
+                a.send_slot_out[t * R + lane] = s_lane;
+                a.in_rank_out[t * R + lane] = (uint8_t)bit;
+            }
+        }
+    }
+    if (first) {
+        // expert counts and offsets, while the rows' stores complete
+        for (int e = tid; e < a.E; e += kBlock) a.cnt_exp_out[e] = s_hist[e];
+        block_exclusive_scan_store(s_hist, a.E, a.exp_off_out, s_part);
+        // the per-message counters of the streaming pack start at zero, as
+        // after a layout call
+        for (int64_t i = tid; i < a.counters_n; i += kBlock) a.msg_arrivals[i] = 0;
+    }
+
+    // closed-form publication by the last workgroup to finish its rows
+    if (!a.has_ring) return;   // grid-uniform
+    const ClosedOrder z = closed_order(a, s_ro);
+    wait_vm();   // this wavefront's rows are complete
+    __syncthreads();
+    if (tid == 0) s_last = arrive_last(a.arrive) && cap_ok && read_status(a.st) == 0;
+    __syncthreads();
+    if (!s_last) return;
+    if (wave == 0) closed_reserve(a, z, s_base);
+    __syncthreads();
+    for (int32_t g0 = wave * kWave; g0 < z.total; g0 += kWaves * kWave)
+        closed_publish(a, z, s_base, g0);
 }
 
 // ------------------------------------------------------------ per-expert mode
@@ -1013,7 +1190,105 @@ int launch_pack_any(PackArgs& a, int fmt, hipStream_t stream) {
     }
 }
 
+template <int VPL, int FMT>
+int launch_fused_fmt(PackArgs a, int64_t waves, hipStream_t stream) {
+    a.ngroups = ceil_div(waves, kPackWavesSmall);
+    const int64_t cap = pack_grid_cap() * kPackWaves / kPackWavesSmall;
+    const int64_t passes = ceil_div(a.ngroups, cap);
+    const int64_t blocks = ceil_div(a.ngroups, passes);
+    clear_hip_error();
+    hipLaunchKernelGGL((fused_small_kernel<VPL, FMT>), dim3((unsigned)blocks),
+                       dim3(kPackWavesSmall * kWave), 0, stream, a);
+    EP_HIP_CHECK(hipGetLastError());
+    return EP_OK;
+}
+
+// Chunking of the one-kernel small batch: that of the small-batch pack.
+int launch_fused(PackArgs& a, int fmt, hipStream_t stream) {
+    const int vpl = a.nv <= 64 ? 1 : 2;
+    a.nchunks = (int32_t)ceil_div(a.nv, (int64_t)vpl * kWave);
+    int64_t waves = (int64_t)a.T * a.nchunks;
+    if (waves == 0) waves = 1;   // the layout outputs and the zero-count ATOMICs still go out
+    if (fmt == EP_FMT_BF16)
+        return vpl == 1 ? launch_fused_fmt<1, EP_FMT_BF16>(a, waves, stream)
+                        : launch_fused_fmt<2, EP_FMT_BF16>(a, waves, stream);
+    return vpl == 1 ? launch_fused_fmt<1, EP_FMT_FP8_E4M3_B128>(a, waves, stream)
+                    : launch_fused_fmt<2, EP_FMT_FP8_E4M3_B128>(a, waves, stream);
+}
+
 }  // namespace
+
+extern "C" int ep_dispatch_fused(const ep_shape_t* shape, const void* x, const int32_t* topk_idx,
+                                 const float* topk_w, int32_t* num_tokens_per_rank,
+                                 int32_t* num_tokens_per_expert, int32_t* rank_offset,
+                                 int32_t* expert_offset, uint8_t* is_token_in_rank,
+                                 int32_t* send_slot, void* send_buf, int64_t capacity_rows,
+                                 int32_t* slot_src, int32_t* slot_local_idx, float* slot_local_w,
+                                 ep_ring_t* ring, void* workspace, size_t ws_bytes,
+                                 int32_t* dev_status, hipStream_t stream) {
+    int v = validate_shape(shape);
+    if (v != EP_OK) return v;
+    const ep_shape_t s = *shape;
+    if (s.T > kFusedMaxT) {
+        // the two-kernel path: layout, then pack
+        v = ep_dispatch_layout(shape, topk_idx, num_tokens_per_rank, num_tokens_per_expert,
+                               rank_offset, expert_offset, is_token_in_rank, send_slot, workspace,
+                               ws_bytes, dev_status, stream);
+        if (v != EP_OK) return v;
+        return ep_dispatch(shape, x, topk_idx, topk_w, rank_offset, send_slot, send_buf,
+                           capacity_rows, slot_src, slot_local_idx, slot_local_w, ring, workspace,
+                           ws_bytes, dev_status, stream);
+    }
+    if (!num_tokens_per_rank || !num_tokens_per_expert || !rank_offset || !expert_offset ||
+        !dev_status || !workspace || capacity_rows < 0)
+        return EP_ERR_INVALID_ARG;
+    if (s.T > 0 && (!x || !topk_idx || !topk_w || !is_token_in_rank || !send_slot))
+        return EP_ERR_INVALID_ARG;
+    if (capacity_rows > 0 && (!send_buf || !slot_src || !slot_local_idx || !slot_local_w))
+        return EP_ERR_INVALID_ARG;
+    if (((uintptr_t)x | (uintptr_t)send_buf) & 15) return EP_ERR_INVALID_ARG;
+    if (ws_bytes < workspace_bytes(s)) return EP_ERR_INVALID_ARG;
+    if (ring && (uint64_t)capacity_rows * row_bytes(s.H, s.fmt) > kMaxRingOffset)
+        return EP_ERR_INVALID_ARG;   // descriptor offsets are 48-bit
+    Workspace w = carve_workspace(s, workspace);
+
+    PackArgs a{};
+    a.x = reinterpret_cast<const u32x4*>(x);
+    a.idx = topk_idx;
+    a.w = topk_w;
+    a.rank_off = rank_offset;
+    a.send_slot = send_slot;
+    a.send_buf = reinterpret_cast<uint8_t*>(send_buf);
+    a.slot_src = slot_src;
+    a.slot_local_idx = slot_local_idx;
+    a.slot_local_w = slot_local_w;
+    a.msg_base = w.msg_base;
+    a.msg_arrivals = w.msg_arrivals;
+    a.rank_msgs_done = w.rank_msgs_done;
+    a.max_msgs = w.max_msgs;
+    a.arrive = w.arrive;
+    a.st = dev_status;
+    a.ring = ring_device_view(ring);
+    a.has_ring = ring != nullptr;
+    a.cap = capacity_rows;
+    a.row_bytes = (int64_t)row_bytes(s.H, s.fmt);
+    a.T = s.T;
+    a.H = s.H;
+    a.E = s.E;
+    a.R = s.R;
+    a.k = s.k;
+    a.epr = s.E / s.R;
+    a.nv = s.H / 8;
+    a.cnt_rank_out = num_tokens_per_rank;
+    a.cnt_exp_out = num_tokens_per_expert;
+    a.rank_off_out = rank_offset;
+    a.exp_off_out = expert_offset;
+    a.in_rank_out = is_token_in_rank;
+    a.send_slot_out = send_slot;
+    a.msg_base_out = w.msg_base;
+    a.counters_n = w.counters_n;
+    return launch_fused(a, s.fmt, stream);
+}
 
 extern "C" int ep_dispatch(const ep_shape_t* shape, const void* x, const int32_t* topk_idx,
                            const float* topk_w, const int32_t* rank_offset,

@@ -180,6 +180,23 @@ int ep_dispatch(const ep_shape_t* shape, const void* x, const int32_t* topk_idx,
                 ep_ring_t* ring, void* workspace, size_t workspace_bytes,
                 int32_t* dev_status, hipStream_t stream);
 
+/* Layout and pack in one call: the outputs of ep_dispatch_layout followed by
+ * ep_dispatch, with the same arguments, meanings and device errors.  UCCL-EP
+ * s4.1 (the low-latency path serves small decode batches, where latency, not
+ * bandwidth, is the cost).  For T <= 256 it is one kernel: every workgroup
+ * derives the whole (small) layout from topk_idx on chip and starts copying
+ * rows at once, and the descriptors are published in closed form by the last
+ * workgroup to finish its rows.  For larger T it makes the two calls.
+ * Leaves the workspace as the two calls would. */
+int ep_dispatch_fused(const ep_shape_t* shape, const void* x, const int32_t* topk_idx,
+                      const float* topk_w, int32_t* num_tokens_per_rank,
+                      int32_t* num_tokens_per_expert, int32_t* rank_offset,
+                      int32_t* expert_offset, uint8_t* is_token_in_rank, int32_t* send_slot,
+                      void* send_buf, int64_t capacity_rows,
+                      int32_t* slot_src, int32_t* slot_local_idx, float* slot_local_w,
+                      ep_ring_t* ring, void* workspace, size_t workspace_bytes,
+                      int32_t* dev_status, hipStream_t stream);
+
 /* Combine.  UCCL-EP s6 (EP combine), GPU communication notes s5
  * (DeepEP combine).  The returned expert outputs y sit in the dispatch
  * layout: y row send_slot[t,r] is rank r's result for token t.

@@ -39,10 +39,10 @@ def host(t) -> np.ndarray:
 
 
 def run_hip(T, H, E, R, k, fmt, x, idx, w, capacity_rows=None, ring_cfg=None,
-            proxy_threads=4, poison=POISON, log_capacity=1 << 20, repeat=1):
-    """layout + dispatch through the C ABI.  ring_cfg = (depth, channels,
-    max_inflight, timeout_ns) or None.  Returns numpy outputs, the proxy log
-    and the device status."""
+            proxy_threads=4, poison=POISON, log_capacity=1 << 20, repeat=1, fused=False):
+    """layout + dispatch through the C ABI (fused: ep_dispatch_fused, one
+    call).  ring_cfg = (depth, channels, max_inflight, timeout_ns) or None.
+    Returns numpy outputs, the proxy log and the device status."""
     import combine_topk_rank_amd as ep
     torch = torch_mod()
     s = ep.shape(T, H, E, R, k, fmt)
@@ -64,8 +64,11 @@ def run_hip(T, H, E, R, k, fmt, x, idx, w, capacity_rows=None, ring_cfg=None,
             ring.proxy_start(proxy_threads, log_capacity)
     logs = []
     for _ in range(repeat):
-        buf.layout(d_idx)
-        buf.dispatch(d_x, d_idx, d_w, ring=ring)
+        if fused:
+            buf.dispatch_fused(d_x, d_idx, d_w, ring=ring)
+        else:
+            buf.layout(d_idx)
+            buf.dispatch(d_x, d_idx, d_w, ring=ring)
         torch.cuda.synchronize()
     if ring is not None and proxy_threads:
         lg, n_drained = ring.proxy_stop(log_capacity)

@@ -72,6 +72,15 @@ def test_host_validation_rejects_without_launch(ep):
     # misaligned x
     assert L.ep_dispatch(ctypes.byref(good), 8, 16, 16, 16, 16, 256, 10, 16, 16, 16, None, 256,
                          1 << 20, 16, None) == 1
+    # one-call layout + dispatch: bad shape, null outputs, misaligned x, short workspace
+    assert L.ep_dispatch_fused(ctypes.byref(bad), *([None] * 9), None, 0, None, None, None, None,
+                               None, 0, None, None) == 1
+    assert L.ep_dispatch_fused(ctypes.byref(good), *([None] * 9), None, 0, None, None, None, None,
+                               None, 0, None, None) == 1
+    assert L.ep_dispatch_fused(ctypes.byref(good), 8, *([16] * 8), 256, 10, 16, 16, 16, None,
+                               256, 1 << 20, 16, None) == 1
+    assert L.ep_dispatch_fused(ctypes.byref(good), *([16] * 9), 256, 10, 16, 16, 16, None,
+                               256, 0, 16, None) == 1
     # T = 0 combine is a no-op
     zero = ep.shape(0, 64, 16, 4, 2)
     assert L.ep_combine(ctypes.byref(zero), None, 0, None, None, None, None, 16, None) == 0

@@ -1,5 +1,6 @@
-"""GPU parity of ep_dispatch_fused (routing layout and pack in one call; one
-kernel for T <= 256) against the CPU oracle, through the C ABI.
+"""GPU parity of ep_dispatch_fused (routing layout and pack in one call: one
+kernel for T <= 256, else the two calls) against the CPU oracle, through the
+C ABI.
 
 Bit-exact: counts, offsets, membership, send slots, packed bytes (poisoned
 buffers, rows past P untouched), metadata and fp8 codes.  The closed-form
@@ -30,7 +31,18 @@ def _check(g, L, pk, want, channels, calls=1):
     assert_stream_in_order(lg, want, channels, calls=calls)
 
 
-@pytest.mark.parametrize("name", ["tiny", "decode"])
+def _check_stream(g, L, pk, want, channels):
+    """streaming publication: the same multiset, tickets consecutive per
+    channel, each rank's ATOMIC after its WRITEs"""
+    assert g["status"] == 0, g["status"]
+    assert_layout_equal(g, L)
+    assert_pack_equal(g, pk, L["P"])
+    lg, nd = g["logs"][0]
+    assert nd == len(want) == len(lg)
+    assert_descriptors(lg, want, channels, first_seq=1)
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "train", "fp8"])
 def test_fused_workload_parity(name):
     w = W.WORKLOADS[name]
     inp = pins.workload_inputs(name)
@@ -44,7 +56,10 @@ def test_fused_workload_parity(name):
     g = run_hip(w.T, w.H, w.E, w.R, w.k, w.fmt, inp["x"], inp["topk_idx"], inp["topk_w"],
                 capacity_rows=P + 8,
                 ring_cfg=(w.depth, w.channels, w.max_inflight, RING_TIMEOUT_NS), fused=True)
-    _check(g, L, pk, want, w.channels)
+    if w.T <= 256:
+        _check(g, L, pk, want, w.channels)
+    else:
+        _check_stream(g, L, pk, want, w.channels)
     y = W.make_expert_outputs(P, w.H, 0)
     ref = oracle.combine(y, inp["topk_idx"], inp["topk_w"], L["send_slot"], w.E, w.R)
     got, st = run_hip_combine(g["buffers"], y, g["d_idx"], g["d_w"])
@@ -64,7 +79,10 @@ CASES = [
     (256, 136, 32, 4, 3, 0, 0.5, 1, 1024, 256),
     (128, 512, 32, 16, 8, 1, 0.0, 4, 16, 4),
     (256, 4096, 128, 8, 4, 1, 0.2, 8, 1024, 256),
-    (300, 7168, 256, 32, 8, 0, 0.0, 8, 1024, 256),   # above 256 tokens: layout, then pack
+    # above 256 tokens: layout, then pack (closed form or streaming publication)
+    (300, 7168, 256, 32, 8, 0, 0.0, 8, 1024, 256),
+    (1100, 7168, 64, 64, 8, 1, 0.1, 8, 64, 16),
+    (2000, 2304, 6, 3, 2, 0, 0.3, 2, 1024, 256),
 ]
 
 
@@ -86,13 +104,7 @@ def test_fused_random_case_parity(case):
     if T <= 256:
         _check(g, L, pk, want, C)
     else:
-        # the two-kernel path publishes by streaming: same multiset
-        assert g["status"] == 0
-        assert_layout_equal(g, L)
-        assert_pack_equal(g, pk, P)
-        lg, nd = g["logs"][0]
-        assert nd == len(want)
-        assert_descriptors(lg, want, C, first_seq=1)
+        _check_stream(g, L, pk, want, C)
     if T > 0:
         y = W.make_expert_outputs(P, H, 3)
         ref = oracle.combine(y, inp["topk_idx"], inp["topk_w"], L["send_slot"], E, R, H=H)
@@ -131,15 +143,16 @@ def test_fused_repeated_calls_on_one_ring():
     _check(g, L, pk, want, C, calls=3)
 
 
-def test_fused_errors():
+@pytest.mark.parametrize("name", ["decode", "train"])
+def test_fused_errors(name):
     """A bad expert id and a capacity shortfall are reported; no descriptor
     goes out, and the rows below the capacity are still written."""
     import combine_topk_rank_amd as ep
-    w = W.WORKLOADS["decode"]
-    inp = pins.workload_inputs("decode")
+    w = W.WORKLOADS[name]
+    inp = pins.workload_inputs(name)
     idx = inp["topk_idx"].copy()
     idx[7, 3] = w.E + 5
-    log("[fused] bad expert id")
+    log(f"[fused] {name}: bad expert id")
     g = run_hip(w.T, w.H, w.E, w.R, w.k, w.fmt, inp["x"], idx, inp["topk_w"],
                 ring_cfg=(w.depth, w.channels, w.max_inflight, RING_TIMEOUT_NS), fused=True)
     assert g["status"] == ep.EP_ERR_BAD_EXPERT
@@ -148,7 +161,7 @@ def test_fused_errors():
     cap = L["P"] - 10
     pk = oracle.pack(inp["x"], inp["topk_idx"], inp["topk_w"], L["send_slot"], w.E, w.R, w.fmt,
                      capacity_rows=cap)
-    log(f"[fused] capacity {cap} < P = {L['P']}")
+    log(f"[fused] {name}: capacity {cap} < P = {L['P']}")
     g = run_hip(w.T, w.H, w.E, w.R, w.k, w.fmt, inp["x"], inp["topk_idx"], inp["topk_w"],
                 capacity_rows=cap,
                 ring_cfg=(w.depth, w.channels, w.max_inflight, RING_TIMEOUT_NS), fused=True)

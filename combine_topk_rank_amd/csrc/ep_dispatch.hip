@@ -411,13 +411,10 @@ __device__ inline ClosedOrder closed_order(const PackArgs& a, const int32_t* ro)
     return z;
 }
 
-// Publish commands [g0, g0 + 64) of the concatenated closed-form order;
-// base[c] is the first ticket of channel c.
+// Publish command g of the concatenated closed-form order (lanes with
+// `have`); base[c] is the first ticket of channel c.
 __device__ void closed_publish(const PackArgs& a, const ClosedOrder& z,
-                               const unsigned long long* base, int32_t g0) {
-    const int lane = lane_id();
-    const int32_t g = g0 + lane;
-    const bool have = g < z.total;
+                               const unsigned long long* base, int32_t g, bool have) {
     int j = 0;   // position holding command g
     for (int p = 1; p < a.R; ++p)
         if (bcast(z.start, p) <= g) j = p;
@@ -438,8 +435,10 @@ __device__ void closed_publish(const PackArgs& a, const ClosedOrder& z,
 }
 
 // One ticket reservation per channel for all of its commands (wavefront-wide;
-// lane of a channel's first rank reserves), bases stored to base[c].
-__device__ void closed_reserve(const PackArgs& a, const ClosedOrder& z, unsigned long long* base) {
+// lane of a channel's first rank reserves), bases stored to base[c]; the
+// channel's first command and command count go to cstart[c] and cnum[c].
+__device__ void closed_reserve(const PackArgs& a, const ClosedOrder& z, unsigned long long* base,
+                               int32_t* cstart, int32_t* cnum) {
     const int lane = lane_id();
     const int C = a.ring.channels, R = a.R;
     const int q = R / C, rem = R % C;
@@ -449,6 +448,30 @@ __device__ void closed_reserve(const PackArgs& a, const ClosedOrder& z, unsigned
     if (lane < R && z.start == z.cstart) {   // lane of a channel's first rank
         const int32_t n = (nxt < R ? nxt_start : z.total) - z.cstart;
         base[z.c] = ring_reserve(a.ring, z.c, (unsigned)n);
+        cstart[z.c] = z.cstart;
+        cnum[z.c] = n;
+    }
+}
+
+// The whole closed-form stream, by every thread of a workgroup of NT
+// threads.  The channels advance together: in each round thread i takes
+// channel i % nch and the next command of that channel's stream, so every
+// channel's window fills (and its proxy drains) from the start instead of
+// one channel after another.
+template <int NT>
+__device__ void closed_publish_all(const PackArgs& a, const ClosedOrder& z,
+                                   const unsigned long long* base, const int32_t* cstart,
+                                   const int32_t* cnum) {
+    const int nch = a.ring.channels < a.R ? a.ring.channels : a.R;
+    const int per_round = NT / nch;
+    int32_t nmax = 0;
+    for (int c = 0; c < nch; ++c) nmax = cnum[c] > nmax ? cnum[c] : nmax;
+    const int c = (int)threadIdx.x % nch;
+    const int32_t jt = (int32_t)threadIdx.x / nch;
+    for (int32_t j0 = 0; j0 < nmax; j0 += per_round) {
+        const int32_t j = j0 + jt;
+        const bool have = jt < per_round && j < cnum[c];
+        closed_publish(a, z, base, have ? cstart[c] + j : 0, have);
     }
 }
 
@@ -767,10 +790,10 @@ __global__ __launch_bounds__(WAVES * kWave) void pack_kernel(PackArgs a) {
         }
         __syncthreads();
         if (!s_last) return;
-        if (wave == 0) closed_reserve(a, z, s_base);
+        __shared__ int32_t s_cstart[kMaxR], s_cnum[kMaxR];
+        if (wave == 0) closed_reserve(a, z, s_base, s_cstart, s_cnum);
         __syncthreads();
-        for (int32_t g0 = wave * kWave; g0 < z.total; g0 += kWaves * kWave)
-            closed_publish(a, z, s_base, g0);
+        closed_publish_all<kWaves * kWave>(a, z, s_base, s_cstart, s_cnum);
     }
 }
 
@@ -909,10 +932,10 @@ __global__ __launch_bounds__(kPackWavesSmall* kWave) void fused_small_kernel(Pac
     if (tid == 0) s_last = arrive_last(a.arrive) && cap_ok && read_status(a.st) == 0;
     __syncthreads();
     if (!s_last) return;
-    if (wave == 0) closed_reserve(a, z, s_base);
+    __shared__ int32_t s_cstart[kMaxR], s_cnum[kMaxR];
+    if (wave == 0) closed_reserve(a, z, s_base, s_cstart, s_cnum);
     __syncthreads();
-    for (int32_t g0 = wave * kWave; g0 < z.total; g0 += kWaves * kWave)
-        closed_publish(a, z, s_base, g0);
+    closed_publish_all<kWaves * kWave>(a, z, s_base, s_cstart, s_cnum);
 }
 
 // ------------------------------------------------------------ per-expert mode
@@ -993,9 +1016,22 @@ __device__ void ll_closed_publish(const PackArgs& a) {
     }
     __syncthreads();
     const uint64_t rb = (uint64_t)a.row_bytes;
-    for (int32_t g0 = wave * kWave; g0 < total; g0 += kT) {
-        const int32_t g = g0 + lane;
-        const bool have = g < total;
+    // the channels advance together (as in closed_publish_all): in each
+    // round thread i takes channel i % nch and that channel's next command
+    const int per_round = kT / nch;
+    const int ch = tid % nch;
+    const int32_t jt = tid / nch;
+    const int32_t cfirst = s_start[ll_first_pos(ch, q, rem) * epr];
+    const int32_t cnum = (ch + 1 < nch ? s_start[ll_first_pos(ch + 1, q, rem) * epr] : total) - cfirst;
+    int32_t nmax = 0;
+    for (int c2 = 0; c2 < nch; ++c2) {
+        const int32_t f = s_start[ll_first_pos(c2, q, rem) * epr];
+        const int32_t l = c2 + 1 < nch ? s_start[ll_first_pos(c2 + 1, q, rem) * epr] : total;
+        nmax = l - f > nmax ? l - f : nmax;
+    }
+    for (int32_t j0 = 0; j0 < nmax; j0 += per_round) {
+        const bool have = jt < per_round && j0 + jt < cnum;
+        const int32_t g = have ? cfirst + j0 + jt : 0;
         // the expert (stream position o) that command g belongs to
         int lo = 0, hi = E - 1;
         while (lo < hi) {

@@ -89,7 +89,9 @@ __device__ inline void column_sums(const int32_t* __restrict__ m, int nrows, int
 // Totals of the [nrows, ncols] int32 matrix m over its rows, one column per
 // thread (consecutive threads read consecutive columns, so every load is
 // coalesced), kSumBatch * 4 rows in flight per thread; into LDS acc[ncols].
-__device__ inline void column_totals(const int32_t* __restrict__ m, int nrows, int ncols,
+// Each column of m is replaced by its exclusive prefix over the rows (row i:
+// the sum of rows < i), which the per-expert row table reads.
+__device__ inline void column_totals(int32_t* __restrict__ m, int nrows, int ncols,
                                      int32_t* acc) {
     constexpr int kRows = kSumBatch * 4;
     for (int c = threadIdx.x; c < ncols; c += kBlock) {
@@ -100,7 +102,10 @@ __device__ inline void column_totals(const int32_t* __restrict__ m, int nrows, i
             for (int u = 0; u < kRows; ++u)
                 q[u] = r0 + u < nrows ? m[(int64_t)(r0 + u) * ncols + c] : 0;
 #pragma unroll
-            for (int u = 0; u < kRows; ++u) sum += q[u];
+            for (int u = 0; u < kRows; ++u) {
+                if (r0 + u < nrows) m[(int64_t)(r0 + u) * ncols + c] = sum;
+                sum += q[u];
+            }
         }
         acc[c] = sum;
     }
@@ -340,9 +345,9 @@ __global__ __launch_bounds__(kBlock) void layout_main_kernel(
 // in (t, j) order, e = topk_idx[t,j], or -1 for a dropped (or bad) choice.
 //
 // One wavefront per 64 tokens.  Its base per expert is expert_offset, plus
-// the counts of the earlier 256-token tiles (their histograms are still in
-// the workspace), plus the choices of the earlier 64-token groups of its own
-// tile (counted from topk_idx).  Inside the wavefront, every lane sets its
+// the counts of the earlier 256-token tiles (the layout leaves their
+// per-tile prefix in the workspace: one row to read), plus the choices of the
+// earlier 64-token groups of its own tile (counted from topk_idx).  Inside the wavefront, every lane sets its
 // bit in an LDS mask per expert it names (64-bit atomic OR); a choice's place
 // among the same expert's choices of lower lanes is the popcount of that mask
 // below the lane.  A token naming an expert o+1 times takes part in o+1
@@ -350,7 +355,7 @@ __global__ __launch_bounds__(kBlock) void layout_main_kernel(
 // repeats count once per choice.  No atomic decides an order: deterministic.
 __global__ __launch_bounds__(kWave) void ll_slot_kernel(
     const int32_t* __restrict__ idx, int T, int E, int k,
-    const int32_t* __restrict__ blk_exp_cnt, const int32_t* __restrict__ exp_off,
+    const int32_t* __restrict__ blk_exp_pre, const int32_t* __restrict__ exp_off,
     int32_t* __restrict__ expert_slot, int32_t* st) {
     __shared__ int32_t s_base[kMaxE];
     __shared__ unsigned long long s_mask[kMaxE];
@@ -369,24 +374,11 @@ __global__ __launch_bounds__(kWave) void ll_slot_kernel(
         s_mask[e] = 0ull;
     }
     __syncthreads();
-    // earlier tiles: rows < tile of the per-tile expert histograms
-    {
-        const int64_t n = tile * (int64_t)E;
-        constexpr int kBatch = 8;
-        for (int64_t i0 = lane; i0 < n; i0 += (int64_t)kWave * kBatch) {
-            int32_t v[kBatch];
-#pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                const int64_t i = i0 + (int64_t)u * kWave;
-                v[u] = i < n ? blk_exp_cnt[i] : 0;
-            }
-#pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                const int64_t i = i0 + (int64_t)u * kWave;
-                if (i < n && v[u]) atomicAdd(&s_base[(int)(i % E)], v[u]);
-            }
-        }
-    }
+    // earlier tiles: the layout left, per tile, the exclusive prefix of the
+    // tiles' expert counts
+    if (tile > 0)
+        for (int e = lane; e < E; e += kWave) s_base[e] = blk_exp_pre[tile * (int64_t)E + e];
+    __syncthreads();
     // earlier 64-token groups of this tile, from topk_idx
     {
         const int64_t n = (q * kWave - t_tile) * k;   // choices before this group in the tile

@@ -227,7 +227,7 @@ int ep_combine(const ep_shape_t* shape, const void* y, int64_t y_rows,
  *   expert_offset int32 [E+1]  from ep_dispatch_layout
  *   expert_slot   int32 [T,k]  output
  * Must follow ep_dispatch_layout on the same stream with the same topk_idx
- * and workspace: it reads the per-tile expert counts left there. */
+ * and workspace: it reads the per-tile expert count prefixes left there. */
 int ep_dispatch_layout_ll(const ep_shape_t* shape, const int32_t* topk_idx,
                           const int32_t* expert_offset, int32_t* expert_slot,
                           void* workspace, size_t workspace_bytes,

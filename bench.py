@@ -168,8 +168,9 @@ def main() -> int:
                     help="rank: one row per (token, rank) pair; ll: the per-expert "
                          "(low-latency) mode, one row per kept choice")
     ap.add_argument("--fused", choices=("auto", "on", "off"), default="auto",
-                    help="layout + dispatch in one call (ep_dispatch_fused; one kernel for "
-                         "T <= 256); auto: for batches of at most 256 tokens (rank mode)")
+                    help="layout + dispatch in one call (ep_dispatch_fused, one kernel for "
+                         "T <= 256; per-expert mode: ep_dispatch_ll_fused, T <= 256 and "
+                         "E <= 1024); auto: for batches of at most 256 tokens")
     ap.add_argument("--proxy-threads", type=int, default=4)
     ap.add_argument("--op-events-every", type=int, default=5,
                     help="record per-op HIP events on every n-th timed step (events between "
@@ -213,7 +214,12 @@ def main() -> int:
     d_w = torch.from_numpy(inp["topk_w"]).to(dev)
     s = ep.shape(w.T, w.H, w.E, w.R, w.k, w.fmt)
     ll = args.mode == "ll"
-    fused = not ll and (args.fused == "on" or (args.fused == "auto" and w.T <= 256))
+    # one-call layout + pack: rank mode any T (one kernel up to 256 tokens);
+    # per-expert mode up to 256 tokens and 1024 experts
+    if ll:
+        fused = args.fused == "on" or (args.fused == "auto" and w.T <= 256 and w.E <= 1024)
+    else:
+        fused = args.fused == "on" or (args.fused == "auto" and w.T <= 256)
     b = ep.BuffersLL(s, device=dev) if ll else ep.Buffers(s, device=dev)
     cap = b.capacity_rows
     if w.fmt == 0:
@@ -375,7 +381,9 @@ def main() -> int:
     tokens_s = w.T * K / elapsed
     # dominant kernel: the longer of pack (inside ep_dispatch) and combine
     if t_disp >= t_comb:
-        if ll:
+        if ll and fused:
+            dom, prefix = "ll_fused_small_kernel (ep_dispatch_ll_fused)", "ll_fused_small_kernel"
+        elif ll:
             dom, prefix = "ll_pack_kernel (ep_dispatch_ll)", "ll_pack_kernel"
         elif fused:
             dom, prefix = "fused_small_kernel (ep_dispatch_fused)", "fused_small_kernel"
@@ -422,8 +430,9 @@ def main() -> int:
                       "combine": round(t_comb * 1e3, 2),
                       "note": (f"HIP events on the launch stream, every {every}th of the {K} timed "
                                f"steps ({len(evs)} samples)" + ("; layout and dispatch are "
-                               "one call (ep_dispatch_fused): its time is under dispatch"
-                               if fused else "")) if graph is None else
+                               "one call (" + ("ep_dispatch_ll_fused" if ll else
+                                               "ep_dispatch_fused") +
+                               "): its time is under dispatch" if fused else "")) if graph is None else
                               "graph replays: the step time split in proportion to the byte model, "
                               "not measured per op"},
         "graph": graph is not None,

@@ -100,6 +100,8 @@ def _load() -> ctypes.CDLL:
     L.ep_dispatch_layout_ll.restype = ctypes.c_int
     L.ep_dispatch_ll.argtypes = [S, P, P, P, P, P, P, i64, P, P, P, P, sz, P, P]
     L.ep_dispatch_ll.restype = ctypes.c_int
+    L.ep_dispatch_ll_fused.argtypes = [S, P, P, P, P, P, P, P, i64, P, P, P, P, sz, P, P]
+    L.ep_dispatch_ll_fused.restype = ctypes.c_int
     L.ep_combine_ll.argtypes = [S, P, i64, P, P, P, P, P, P]
     L.ep_combine_ll.restype = ctypes.c_int
     L.ep_ring_create.argtypes = [i32, i32, i32, i64]
@@ -240,6 +242,19 @@ def ep_dispatch_ll(s, x, topk_idx, topk_w, expert_offset, expert_slot, send_buf,
                             workspace.numel() * workspace.element_size(), _ptr(dev_status),
                             _stream(stream))
     _check(st, "ep_dispatch_ll")
+
+
+def ep_dispatch_ll_fused(s, x, topk_idx, topk_w, num_tokens_per_expert, expert_offset,
+                         expert_slot, send_buf, slot_src, slot_w, ring, workspace, dev_status,
+                         stream=None, capacity_rows: Optional[int] = None) -> None:
+    cap = send_buf.shape[0] if capacity_rows is None else capacity_rows
+    st = lib.ep_dispatch_ll_fused(ctypes.byref(s), _ptr(x), _ptr(topk_idx), _ptr(topk_w),
+                                  _ptr(num_tokens_per_expert), _ptr(expert_offset),
+                                  _ptr(expert_slot), _ptr(send_buf), cap, _ptr(slot_src),
+                                  _ptr(slot_w), ring.handle if ring is not None else None,
+                                  _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                  _ptr(dev_status), _stream(stream))
+    _check(st, "ep_dispatch_ll_fused")
 
 
 def ep_combine_ll(s, y, topk_idx, topk_w, expert_slot, out, dev_status, stream=None) -> None:
@@ -408,6 +423,13 @@ class BuffersLL(Buffers):
         ep_dispatch_ll(self.shape, x, topk_idx, topk_w, self.expert_offset, self.expert_slot,
                        self.send_buf, self.slot_src, self.slot_w, ring, self.workspace,
                        self.dev_status, stream)
+
+    def dispatch_fused(self, x, topk_idx, topk_w, ring=None, stream=None):
+        """per-expert layout, row table and pack in one kernel (T <= 256,
+        E <= 1024); the rank-layout buffers are left untouched"""
+        ep_dispatch_ll_fused(self.shape, x, topk_idx, topk_w, self.num_tokens_per_expert,
+                             self.expert_offset, self.expert_slot, self.send_buf, self.slot_src,
+                             self.slot_w, ring, self.workspace, self.dev_status, stream)
 
     def combine(self, y, topk_idx, topk_w, stream=None):
         ep_combine_ll(self.shape, y, topk_idx, topk_w, self.expert_slot, self.out,

@@ -963,7 +963,7 @@ __device__ inline int ll_first_pos(int c, int q, int rem) {   // first rank posi
 }
 
 template <int WAVES>
-__device__ void ll_closed_publish(const PackArgs& a) {
+__device__ void ll_closed_publish(const PackArgs& a, const int32_t* exp_off) {
     __shared__ int32_t s_start[kMaxE + 1];
     __shared__ int32_t s_eo[kMaxE + 1];   // expert_offset, staged once
     __shared__ int32_t s_wsum[WAVES];
@@ -972,7 +972,7 @@ __device__ void ll_closed_publish(const PackArgs& a) {
     const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
     const int E = a.E, R = a.R, C = a.ring.channels, epr = a.epr;
     const int q = R / C, rem = R % C;
-    for (int e = tid; e <= E; e += kT) s_eo[e] = a.exp_off[e];
+    for (int e = tid; e <= E; e += kT) s_eo[e] = exp_off[e];
     __syncthreads();
     // commands per expert, in stream order, scanned: thread tid sums a run
     const int per = (E + kT - 1) / kT;
@@ -1109,8 +1109,183 @@ __global__ __launch_bounds__(WAVES * kWave) void ll_pack_kernel(PackArgs a) {
             s_last = arrive_last(a.arrive) && cap_ok && read_status(a.st) == 0;
         __syncthreads();
         if (!s_last) return;
-        ll_closed_publish<WAVES>(a);
+        ll_closed_publish<WAVES>(a, a.exp_off);
     }
+}
+
+// ---------------------------------------- one-kernel per-expert small batches
+// Per-expert layout, row table and pack of a batch of at most kFusedMaxT
+// tokens with at most kLLFusedMaxE experts in one launch (UCCL-EP article
+// s4.1: the low-latency mode serves small decode batches, where the chain of
+// kernels and memory round trips is the cost).  Every workgroup derives the
+// whole row table in LDS: wavefront w takes tokens 64w .. 64w + 63; for each
+// round o (the o-th occurrence of an expert within a token, for repeats) its
+// lanes set their bit in a per-wavefront mask per expert, a choice's place
+// among the wavefront's earlier choices of its expert is the popcount of the
+// mask below the lane, and the masks' popcounts are the wavefront's counts.
+// The expert offsets are the scan of the totals; a wavefront's base for
+// expert e is the offset plus the counts of the lower wavefronts.  No
+// workgroup waits for another before copying.  Workgroup 0 writes the counts
+// and offsets; the first chunk of each token writes its expert_slot row.  The
+// last workgroup to finish its rows publishes in closed form.
+constexpr int kLLFusedMaxE = 1024;
+
+// KMAX: the bound on k the kernel is built for (8, or the library's bound);
+// the loops over a token's choices run to it.
+template <int VPL, int FMT, int KMAX>
+__global__ __launch_bounds__(kPackWavesSmall* kWave) void ll_fused_small_kernel(PackArgs a) {
+    constexpr int kWaves = kPackWavesSmall;
+    constexpr int kT = kWaves * kWave;
+    static_assert(kT == kBlock, "the expert scan takes a kBlock-thread workgroup");
+    __shared__ int32_t s_cnt[kWaves][kLLFusedMaxE];              // counts, then bases
+    __shared__ unsigned long long s_mask[kWaves][kLLFusedMaxE];  // one round's lanes per expert
+    __shared__ int32_t s_eo[kLLFusedMaxE + 1];                   // expert offsets
+    __shared__ int32_t s_tot[kLLFusedMaxE];
+    __shared__ int32_t s_row[kFusedMaxT][KMAX];                 // row of choice (t, j), or -1
+    __shared__ int32_t s_part[kBlock];
+    __shared__ int s_rounds, s_last;
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+    const bool first = blockIdx.x == 0;
+    const int E = a.E, k = a.k;
+
+    // this wavefront's chunk of its first group, loaded before the layout
+    u32x4 v[VPL];
+    {
+        const int64_t gw = (int64_t)blockIdx.x * kWaves + wave;
+        const int64_t t = gw / a.nchunks;
+        if (blockIdx.x < a.ngroups && t < a.T)
+            load_row_chunk<VPL>(a, t, (int)(gw - t * a.nchunks), v);
+    }
+
+    // the lane's token and its choices
+    const int64_t t = (int64_t)wave * kWave + lane;
+    int32_t ids[KMAX];
+    const int32_t* row = a.idx + t * k;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) ids[j] = (j < k && t < a.T) ? row[j] : -1;
+    for (int e = lane; e < E; e += kWave) {
+        s_cnt[wave][e] = 0;
+        s_mask[wave][e] = 0ull;
+    }
+    if (tid == 0) s_rounds = 0;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+        if (ids[j] < -1 || ids[j] >= E) {
+            set_error(a.st, EP_ERR_BAD_EXPERT);
+            ids[j] = -1;
+        }
+    int32_t occ[KMAX];
+    int my_rounds = 0;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+        int o = 0;
+#pragma unroll
+        for (int i = 0; i < j; ++i) o += (ids[i] == ids[j]) ? 1 : 0;
+        occ[j] = o;
+        if (ids[j] >= 0 && o + 1 > my_rounds) my_rounds = o + 1;
+    }
+    __syncthreads();
+    if (my_rounds) atomicMax(&s_rounds, my_rounds);
+    __syncthreads();
+    const int rounds = s_rounds;
+    const unsigned long long below = (1ull << lane) - 1ull;
+    int32_t pos[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) pos[j] = occ[j];
+    for (int o = 0; o < rounds; ++o) {
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j)
+            if (ids[j] >= 0 && occ[j] == o) atomicOr(&s_mask[wave][ids[j]], 1ull << lane);
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j)
+            if (ids[j] >= 0) pos[j] += __popcll(s_mask[wave][ids[j]] & below);
+        for (int e = lane; e < E; e += kWave) s_cnt[wave][e] += __popcll(s_mask[wave][e]);
+        __syncthreads();
+        for (int e = lane; e < E; e += kWave) s_mask[wave][e] = 0ull;
+        __syncthreads();
+    }
+    // totals, per-wavefront bases, offsets
+    for (int e = tid; e < E; e += kT) {
+        int32_t run = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const int32_t c = s_cnt[w][e];
+            s_cnt[w][e] = run;
+            run += c;
+        }
+        s_tot[e] = run;
+    }
+    __syncthreads();
+    {
+        // exclusive scan of the totals into s_eo (all kT threads)
+        const int per = (E + kT - 1) / kT;
+        const int b0 = tid * per;
+        int32_t sum = 0;
+        for (int i = 0; i < per; ++i)
+            if (b0 + i < E) sum += s_tot[b0 + i];
+        int32_t incl = sum;
+        for (int d = 1; d < kWave; d <<= 1) {
+            const int32_t o = __shfl_up(incl, d);
+            if (lane >= d) incl += o;
+        }
+        if (lane == kWave - 1) s_part[wave] = incl;
+        __syncthreads();
+        int32_t run = incl - sum;
+        for (int w = 0; w < wave; ++w) run += s_part[w];
+        if (tid == kT - 1) s_eo[E] = run + sum;
+        for (int i = 0; i < per; ++i)
+            if (b0 + i < E) {
+                s_eo[b0 + i] = run;
+                run += s_tot[b0 + i];
+            }
+    }
+    __syncthreads();
+    if (t < a.T) {
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j)
+            if (j < k) s_row[t][j] = ids[j] >= 0 ? s_eo[ids[j]] + s_cnt[wave][ids[j]] + pos[j] : -1;
+    }
+    __syncthreads();
+
+    // rows: wavefront g of the grid takes chunk g % nchunks of token g / nchunks
+    const int64_t Q = s_eo[E];
+    const bool cap_ok = Q <= a.cap;
+    if (first && wave == 0) {
+        if (!cap_ok && lane == 0) set_error(a.st, EP_ERR_CAPACITY);
+        if (a.has_ring) refresh_tail_cache(a);
+    }
+    for (int64_t grp = blockIdx.x; grp < a.ngroups; grp += gridDim.x) {
+        const int64_t gw = grp * kWaves + wave;
+        const int64_t tt = gw / a.nchunks;
+        const int chunk = (int)(gw - tt * a.nchunks);
+        if (tt >= a.T) continue;   // wavefront-uniform
+        if (grp != blockIdx.x) load_row_chunk<VPL>(a, tt, chunk, v);
+        const int32_t s_lane = lane < k ? s_row[tt][lane] : -1;
+        const uint64_t dmask = __ballot(s_lane >= 0);
+        store_row_chunk_v<VPL, FMT>(a, chunk, s_lane, dmask, v);
+        if (chunk == 0 && lane < k) {
+            a.send_slot_out[tt * k + lane] = s_lane;
+            if (s_lane >= 0 && s_lane < a.cap) {
+                a.slot_src[s_lane] = (int32_t)tt;
+                a.slot_w[s_lane] = a.w[tt * k + lane];
+            }
+        }
+    }
+    if (first) {
+        // counts and offsets, while the rows' stores complete
+        for (int e = tid; e < E; e += kT) a.cnt_exp_out[e] = s_tot[e];
+        for (int e = tid; e <= E; e += kT) a.exp_off_out[e] = s_eo[e];
+    }
+
+    // closed-form publication by the last workgroup to finish its rows
+    if (!a.has_ring) return;   // grid-uniform
+    wait_vm();   // this wavefront's rows are complete
+    __syncthreads();
+    if (tid == 0) s_last = arrive_last(a.arrive) && cap_ok && read_status(a.st) == 0;
+    __syncthreads();
+    if (!s_last) return;
+    ll_closed_publish<kWaves>(a, s_eo);
 }
 
 }  // namespace ep
@@ -1252,7 +1427,84 @@ int launch_fused(PackArgs& a, int fmt, hipStream_t stream) {
                     : launch_fused_fmt<2, EP_FMT_FP8_E4M3_B128>(a, waves, stream);
 }
 
+// One-kernel per-expert small batch: the chunking of the small-batch pack.
+template <int VPL, int FMT>
+int launch_ll_fused_fmt(PackArgs a, int64_t waves, hipStream_t stream) {
+    a.ngroups = ceil_div(waves, kPackWavesSmall);
+    const int64_t cap = pack_grid_cap() * kPackWaves / kPackWavesSmall;
+    const int64_t passes = ceil_div(a.ngroups, cap);
+    const int64_t blocks = ceil_div(a.ngroups, passes);
+    clear_hip_error();
+    if (a.k <= 8)
+        hipLaunchKernelGGL((ll_fused_small_kernel<VPL, FMT, 8>), dim3((unsigned)blocks),
+                           dim3(kPackWavesSmall * kWave), 0, stream, a);
+    else
+        hipLaunchKernelGGL((ll_fused_small_kernel<VPL, FMT, kMaxK>), dim3((unsigned)blocks),
+                           dim3(kPackWavesSmall * kWave), 0, stream, a);
+    EP_HIP_CHECK(hipGetLastError());
+    return EP_OK;
+}
+
+int launch_ll_fused(PackArgs& a, int fmt, hipStream_t stream) {
+    const int vpl = a.nv <= 64 ? 1 : 2;
+    a.nchunks = (int32_t)ceil_div(a.nv, (int64_t)vpl * kWave);
+    int64_t waves = (int64_t)a.T * a.nchunks;
+    if (waves == 0) waves = 1;   // the counts and the zero-count ATOMICs still go out
+    if (fmt == EP_FMT_BF16)
+        return vpl == 1 ? launch_ll_fused_fmt<1, EP_FMT_BF16>(a, waves, stream)
+                        : launch_ll_fused_fmt<2, EP_FMT_BF16>(a, waves, stream);
+    return vpl == 1 ? launch_ll_fused_fmt<1, EP_FMT_FP8_E4M3_B128>(a, waves, stream)
+                    : launch_ll_fused_fmt<2, EP_FMT_FP8_E4M3_B128>(a, waves, stream);
+}
+
 }  // namespace
+
+extern "C" int ep_dispatch_ll_fused(const ep_shape_t* shape, const void* x,
+                                    const int32_t* topk_idx, const float* topk_w,
+                                    int32_t* num_tokens_per_expert, int32_t* expert_offset,
+                                    int32_t* expert_slot, void* send_buf, int64_t capacity_rows,
+                                    int32_t* slot_src, float* slot_w, ep_ring_t* ring,
+                                    void* workspace, size_t ws_bytes, int32_t* dev_status,
+                                    hipStream_t stream) {
+    int v = validate_shape(shape);
+    if (v != EP_OK) return v;
+    const ep_shape_t s = *shape;
+    if (s.T > kFusedMaxT || s.E > kLLFusedMaxE) return EP_ERR_INVALID_ARG;
+    if (!num_tokens_per_expert || !expert_offset || !dev_status || !workspace || capacity_rows < 0)
+        return EP_ERR_INVALID_ARG;
+    if (s.T > 0 && (!x || !topk_idx || !topk_w || !expert_slot)) return EP_ERR_INVALID_ARG;
+    if (capacity_rows > 0 && (!send_buf || !slot_src || !slot_w)) return EP_ERR_INVALID_ARG;
+    if (((uintptr_t)x | (uintptr_t)send_buf) & 15) return EP_ERR_INVALID_ARG;
+    if (ws_bytes < workspace_bytes(s)) return EP_ERR_INVALID_ARG;
+    if (ring && (uint64_t)capacity_rows * row_bytes(s.H, s.fmt) > kMaxRingOffset)
+        return EP_ERR_INVALID_ARG;   // descriptor offsets are 48-bit
+    Workspace w = carve_workspace(s, workspace);
+
+    PackArgs a{};
+    a.x = reinterpret_cast<const u32x4*>(x);
+    a.idx = topk_idx;
+    a.w = topk_w;
+    a.send_buf = reinterpret_cast<uint8_t*>(send_buf);
+    a.slot_src = slot_src;
+    a.slot_w = slot_w;
+    a.arrive = w.arrive;
+    a.st = dev_status;
+    a.ring = ring_device_view(ring);
+    a.has_ring = ring != nullptr;
+    a.cap = capacity_rows;
+    a.row_bytes = (int64_t)row_bytes(s.H, s.fmt);
+    a.T = s.T;
+    a.H = s.H;
+    a.E = s.E;
+    a.R = s.R;
+    a.k = s.k;
+    a.epr = s.E / s.R;
+    a.nv = s.H / 8;
+    a.cnt_exp_out = num_tokens_per_expert;
+    a.exp_off_out = expert_offset;
+    a.send_slot_out = expert_slot;
+    return launch_ll_fused(a, s.fmt, stream);
+}
 
 extern "C" int ep_dispatch_fused(const ep_shape_t* shape, const void* x, const int32_t* topk_idx,
                                  const float* topk_w, int32_t* num_tokens_per_rank,

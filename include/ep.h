@@ -257,6 +257,22 @@ int ep_dispatch_ll(const ep_shape_t* shape, const void* x, const int32_t* topk_i
                    int32_t* slot_src, float* slot_w, ep_ring_t* ring, void* workspace,
                    size_t workspace_bytes, int32_t* dev_status, hipStream_t stream);
 
+/* Per-expert layout, row table and pack in one call, for small decode
+ * batches: the outputs num_tokens_per_expert, expert_offset and expert_slot
+ * of ep_dispatch_layout + ep_dispatch_layout_ll, and the rows, metadata and
+ * descriptors of ep_dispatch_ll, with the same meanings and device errors.
+ * UCCL-EP s4.1 (the low-latency mode serves small batches, where latency is
+ * the cost).  One kernel: every workgroup derives the row table on chip and
+ * starts copying at once; the last workgroup to finish its rows publishes in
+ * closed form.  The rank-layout outputs are not produced.  Only for
+ * T <= 256 and E <= 1024 (else EP_ERR_INVALID_ARG, nothing launched). */
+int ep_dispatch_ll_fused(const ep_shape_t* shape, const void* x, const int32_t* topk_idx,
+                         const float* topk_w, int32_t* num_tokens_per_expert,
+                         int32_t* expert_offset, int32_t* expert_slot,
+                         void* send_buf, int64_t capacity_rows, int32_t* slot_src, float* slot_w,
+                         ep_ring_t* ring, void* workspace, size_t workspace_bytes,
+                         int32_t* dev_status, hipStream_t stream);
+
 /* Per-expert combine: y row expert_slot[t,j] is expert e_j's output for
  * token t, and
  *   out[t,:] = bf16_rne( sum over kept j ascending of w[t,j] * y[expert_slot[t,j], :] )

@@ -183,9 +183,10 @@ def combine_tolerance_check(got, ref, what=""):
 
 
 def run_hip_ll(T, H, E, R, k, fmt, x, idx, w, capacity_rows=None, ring_cfg=None,
-               proxy_threads=4, poison=POISON, log_capacity=1 << 20, repeat=1):
+               proxy_threads=4, poison=POISON, log_capacity=1 << 20, repeat=1, fused=False):
     """Per-expert mode through the C ABI: rank layout + per-expert row table +
-    per-expert pack (and descriptors when ring_cfg is given)."""
+    per-expert pack (and descriptors when ring_cfg is given); fused: the
+    one-call ep_dispatch_ll_fused."""
     import combine_topk_rank_amd as ep
     torch = torch_mod()
     s = ep.shape(T, H, E, R, k, fmt)
@@ -202,9 +203,14 @@ def run_hip_ll(T, H, E, R, k, fmt, x, idx, w, capacity_rows=None, ring_cfg=None,
         if proxy_threads:
             ring.proxy_start(proxy_threads, log_capacity)
     logs = []
+    buf.num_tokens_per_expert.fill_(-99)
+    buf.expert_offset.fill_(-99)
     for _ in range(repeat):
-        buf.layout(d_idx)
-        buf.dispatch(d_x, d_idx, d_w, ring=ring)
+        if fused:
+            buf.dispatch_fused(d_x, d_idx, d_w, ring=ring)
+        else:
+            buf.layout(d_idx)
+            buf.dispatch(d_x, d_idx, d_w, ring=ring)
         torch.cuda.synchronize()
     if ring is not None and proxy_threads:
         logs.append(ring.proxy_stop(log_capacity))

@@ -81,6 +81,14 @@ def test_host_validation_rejects_without_launch(ep):
                                256, 1 << 20, 16, None) == 1
     assert L.ep_dispatch_fused(ctypes.byref(good), *([16] * 9), 256, 10, 16, 16, 16, None,
                                256, 0, 16, None) == 1
+    # one-call per-expert dispatch: bad shape, beyond its bounds, null outputs
+    assert L.ep_dispatch_ll_fused(ctypes.byref(bad), *([16] * 6), 256, 10, 16, 16, None, 256,
+                                  1 << 20, 16, None) == 1
+    for big in [ep.shape(257, 64, 16, 4, 2), ep.shape(16, 64, 2048, 4, 2)]:
+        assert L.ep_dispatch_ll_fused(ctypes.byref(big), *([16] * 6), 256, 10, 16, 16, None, 256,
+                                      1 << 30, 16, None) == 1
+    assert L.ep_dispatch_ll_fused(ctypes.byref(good), *([None] * 6), None, 0, None, None, None,
+                                  None, 0, None, None) == 1
     # T = 0 combine is a no-op
     zero = ep.shape(0, 64, 16, 4, 2)
     assert L.ep_combine(ctypes.byref(zero), None, 0, None, None, None, None, 16, None) == 0

@@ -1,6 +1,7 @@
 """Per-expert (low-latency) mode on the GPU against the oracle, through the C
 ABI: row table, packed rows and metadata bit-exact, the closed-form command
-stream command for command, combine within 1e-2 * max(1, |ref|)."""
+stream command for command, combine within 1e-2 * max(1, |ref|).  The same
+checks run on the one-call ep_dispatch_ll_fused (T <= 256, E <= 1024)."""
 
 import numpy as np
 import pytest
@@ -16,7 +17,8 @@ pytestmark = pytest.mark.gpu
 RING_TIMEOUT_NS = 5_000_000_000
 
 
-def _check_case(T, H, E, R, k, fmt, inp, C, depth, mif, cap_extra=3, repeat=1, y_seed=7):
+def _check_case(T, H, E, R, k, fmt, inp, C, depth, mif, cap_extra=3, repeat=1, y_seed=7,
+                fused=False):
     idx, w, x = inp["topk_idx"], inp["topk_w"], inp["x"]
     L = oracle.ll_layout(idx, E)
     Q = L["Q"]
@@ -24,7 +26,7 @@ def _check_case(T, H, E, R, k, fmt, inp, C, depth, mif, cap_extra=3, repeat=1, y
     want = oracle.ll_descriptors(L["num_tokens_per_expert"], L["expert_offset"], R,
                                  oracle.row_bytes(H, fmt), C)
     g = run_hip_ll(T, H, E, R, k, fmt, x, idx, w, capacity_rows=Q + cap_extra,
-                   ring_cfg=(depth, C, mif, RING_TIMEOUT_NS), repeat=repeat)
+                   ring_cfg=(depth, C, mif, RING_TIMEOUT_NS), repeat=repeat, fused=fused)
     assert g["status"] == 0, g["status"]
     assert_ll_equal(g, L, pk, Q)
     lg, nd = g["logs"][0]
@@ -120,3 +122,82 @@ def test_ll_capacity_and_inconsistent_rows():
     lg, nd = ring.proxy_stop(1024)
     assert int(b.dev_status.item()) == ep.EP_ERR_INVALID_ARG
     assert nd == 0
+
+
+# ------------------------------------------------- one-call per-expert dispatch
+@pytest.mark.parametrize("name", ["tiny", "decode"])
+def test_ll_fused_workload_parity(name):
+    w = W.WORKLOADS[name]
+    inp = pins.workload_inputs(name)
+    log(f"[ll-fused] workload {name}")
+    _check_case(w.T, w.H, w.E, w.R, w.k, w.fmt, inp, w.channels, w.depth, w.max_inflight,
+                fused=True)
+
+
+LL_FUSED_CASES = [
+    (0, 64, 16, 4, 2, 0, 0.0, 2, 8, 4),
+    (1, 8, 1, 1, 1, 0, 0.0, 1, 4, 1),
+    (5, 16, 6, 3, 2, 0, 0.3, 2, 8, 2),
+    (63, 7168, 256, 32, 8, 0, 0.0, 1, 1024, 256),
+    (64, 200, 64, 8, 6, 0, 0.1, 3, 16, 4),
+    (65, 512, 32, 16, 8, 1, 0.0, 4, 32, 8),
+    (128, 7168, 256, 32, 8, 1, 0.0, 1, 1024, 256),
+    (200, 1024, 64, 64, 4, 0, 0.0, 64, 32, 8),
+    (256, 128, 1024, 64, 32, 0, 0.05, 8, 1024, 256),
+    (256, 136, 256, 32, 8, 0, 0.2, 5, 1024, 64),
+]
+
+
+@pytest.mark.parametrize("case", LL_FUSED_CASES, ids=lambda c: "T%d_H%d_E%d_R%d_k%d_f%d" % c[:6])
+def test_ll_fused_random_case_parity(case):
+    T, H, E, R, k, fmt, drop, C, depth, mif = case
+    rng = np.random.default_rng(3000 + LL_FUSED_CASES.index(case))
+    inp = W.make_random_case(rng, T, H, E, R, k, drop_prob=drop)
+    log(f"[ll-fused] case {case}")
+    _check_case(T, H, E, R, k, fmt, inp, C, depth, mif, fused=True)
+
+
+def test_ll_fused_repeated_experts_and_repeat_calls():
+    """Repeats within a token (up to k occurrences) and three calls on one
+    ring, through the one-call path."""
+    rng = np.random.default_rng(78)
+    T, H, E, R, k = 200, 64, 32, 8, 4
+    inp = W.make_random_case(rng, T, H, E, R, k)
+    idx = inp["topk_idx"].copy()
+    idx[::7, 1] = idx[::7, 0]
+    idx[::11, :] = idx[::11, :1]
+    inp = dict(inp, topk_idx=idx)
+    log("[ll-fused] repeated experts, three calls")
+    _check_case(T, H, E, R, k, 0, inp, 3, 16, 4, repeat=3, fused=True)
+
+
+def test_ll_fused_errors():
+    """Capacity shortfall and a bad expert id: reported, no descriptor; rows
+    below the capacity written.  Shapes beyond the one-kernel bounds are
+    rejected on the host."""
+    import combine_topk_rank_amd as ep
+    rng = np.random.default_rng(6)
+    T, H, E, R, k = 64, 64, 16, 4, 2
+    inp = W.make_random_case(rng, T, H, E, R, k)
+    L = oracle.ll_layout(inp["topk_idx"], E)
+    Q = L["Q"]
+    log("[ll-fused] capacity shortfall")
+    g = run_hip_ll(T, H, E, R, k, 0, inp["x"], inp["topk_idx"], inp["topk_w"], capacity_rows=Q - 1,
+                   ring_cfg=(64, 1, 16, RING_TIMEOUT_NS), fused=True)
+    assert g["status"] == ep.EP_ERR_CAPACITY
+    assert g["logs"][0][1] == 0
+    pk = oracle.ll_pack(inp["x"], inp["topk_w"], L["expert_slot"], 0, capacity_rows=Q - 1)
+    assert np.array_equal(g["send_buf"], pk["send_buf"])
+    assert np.array_equal(g["expert_slot"], L["expert_slot"])
+    log("[ll-fused] bad expert id")
+    idx = inp["topk_idx"].copy()
+    idx[3, 1] = E + 2
+    g = run_hip_ll(T, H, E, R, k, 0, inp["x"], idx, inp["topk_w"],
+                   ring_cfg=(64, 1, 16, RING_TIMEOUT_NS), fused=True)
+    assert g["status"] == ep.EP_ERR_BAD_EXPERT
+    assert g["logs"][0][1] == 0
+    for T2, E2 in [(257, 16), (64, 2048)]:
+        s = ep.shape(T2, H, E2, R, k)
+        b = ep.BuffersLL(s)
+        with pytest.raises(ep.EpError):
+            b.dispatch_fused(b.out, b.expert_slot, b.slot_w)

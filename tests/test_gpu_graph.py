@@ -26,8 +26,10 @@ def _streams_by_call(lg, want, C, calls):
             assert_descriptors(got_c[i * len(exp_c):(i + 1) * len(exp_c)], exp_c, C)
 
 
-@pytest.mark.parametrize("name,mode", [("decode", "rank"), ("tiny", "ll"), ("train", "rank")])
-def test_graph_replays_match_eager(name, mode):
+@pytest.mark.parametrize("name,mode,fused", [("decode", "rank", False), ("tiny", "ll", False),
+                                             ("train", "rank", False), ("decode", "rank", True),
+                                             ("decode", "ll", True)])
+def test_graph_replays_match_eager(name, mode, fused):
     import combine_topk_rank_amd as ep
     import torch
     w = W.WORKLOADS[name]
@@ -41,11 +43,14 @@ def test_graph_replays_match_eager(name, mode):
     ring.proxy_start(4, 1 << 20)
 
     def step():
-        b.layout(d_idx)
-        b.dispatch(d_x, d_idx, d_w, ring=ring)
+        if fused:   # the one-call layout + pack
+            b.dispatch_fused(d_x, d_idx, d_w, ring=ring)
+        else:
+            b.layout(d_idx)
+            b.dispatch(d_x, d_idx, d_w, ring=ring)
         b.combine(y, d_idx, d_w)
 
-    log(f"[graph] {name} {mode}: eager")
+    log(f"[graph] {name} {mode} fused={fused}: eager")
     step()
     torch.cuda.synchronize()
     keys = (["expert_slot", "expert_offset", "send_buf", "slot_src", "slot_w", "out"] if mode == "ll"
@@ -72,7 +77,7 @@ def test_graph_replays_match_eager(name, mode):
     scratch = torch.empty(1 << 24, dtype=torch.uint8, device="cuda")
     replays = 3
     for i in range(replays):
-        log(f"[graph] {name} {mode}: replay {i}")
+        log(f"[graph] {name} {mode} fused={fused}: replay {i}")
         for k_ in keys:
             getattr(b, k_).fill_(0 if getattr(b, k_).dtype != torch.bfloat16 else 1.0)
         scratch.fill_(i)                      # eager work between replays

@@ -159,15 +159,21 @@ __device__ inline void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Grid-wide barrier for a grid whose workgroups are all resident: bar[0]
 // counts arrivals, bar[1] is a generation number.  Each workgroup reads the
-// generation before it arrives; the last arrival resets the count and bumps
-// the generation, which releases the others.  The words stay consistent from
+// generation before it arrives (thread 0 passes what it loaded with
+// grid_barrier_generation, as early as it likes: the generation cannot move
+// before this workgroup arrives); the last arrival resets the count and
+// bumps the generation, which releases the others.  The words stay consistent from
 // one call to the next for any grid size (they start at zero).  The wait is
 // bounded by about a second of wall clock; on timeout the status is set and
 // false is returned.  Stores made before the barrier by any workgroup are
 // visible to loads made after it by every workgroup; with SYSTEM they are
 // also released at system scope (visible to other agents, e.g. a CPU or NIC).
+__device__ inline uint32_t grid_barrier_generation(const uint32_t* bar) {
+    return __hip_atomic_load(&bar[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <bool SYSTEM>
-__device__ bool grid_barrier(uint32_t* bar, uint32_t nblocks, int32_t* st) {
+__device__ bool grid_barrier(uint32_t* bar, uint32_t nblocks, int32_t* st, uint32_t gen) {
     __shared__ int s_ok;
     wait_vm();   // this workgroup's stores complete before thread 0 releases them
     __syncthreads();
@@ -177,7 +183,6 @@ __device__ bool grid_barrier(uint32_t* bar, uint32_t nblocks, int32_t* st) {
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");
         else
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        const uint32_t gen = __hip_atomic_load(&bar[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const uint32_t old = atomicAdd(&bar[0], 1u);
         if (old == nblocks - 1) {
             atomicExch(&bar[0], 0u);

@@ -171,6 +171,10 @@ __global__ __launch_bounds__(kBlock) void layout_main_kernel(
     const int b = blockIdx.x;
     // the extra workgroup of modes 1 and 2: expert totals and offsets only
     const bool expert_wg = !SINGLE && b == nblocks;
+    // the barrier's generation, loaded now so that its latency overlaps the
+    // counting (thread 0 only)
+    uint32_t gen = 0;
+    if (FUSED && tid == 0) gen = grid_barrier_generation(bar);
 
     if (SINGLE || FUSED) {
         for (int e = tid; e < E; e += kBlock) s_hist[e] = 0;
@@ -196,8 +200,11 @@ __global__ __launch_bounds__(kBlock) void layout_main_kernel(
             for (int e = tid; e < E; e += kBlock)
                 blk_exp_cnt[(int64_t)b * E + e] = s_hist[e];
         }
+        if (!grid_barrier<false>(bar, (uint32_t)gridDim.x, st, gen)) return;
+        // the dispatch's message counters start at zero; cleared after the
+        // barrier so that its wait for this workgroup's stores does not
+        // include them (the kernel's end completes them)
         zero_counters(counters, counters_n, (int64_t)b * kBlock + tid, (int64_t)gridDim.x * kBlock);
-        if (!grid_barrier<false>(bar, (uint32_t)gridDim.x, st)) return;
     }
 
     if (expert_wg) {

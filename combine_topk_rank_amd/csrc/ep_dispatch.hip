@@ -512,6 +512,21 @@ __device__ void refresh_tail_cache(const PackArgs& a) {
     }
 }
 
+// The same in two halves, for a wavefront that also copies rows: the PCIe
+// read is issued first and its value applied after the wavefront's rows,
+// so the read's latency does not delay them.
+__device__ inline unsigned long long tail_read(const PackArgs& a) {
+    const int c = lane_id();
+    return c < a.ring.channels
+               ? __hip_atomic_load(a.ring.host_tail + (size_t)c * kPad, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_SYSTEM)
+               : 0ull;
+}
+__device__ inline void tail_apply(const PackArgs& a, unsigned long long h) {
+    const int c = lane_id();
+    if (c < a.ring.channels) atomicMax(a.ring.tail_cache + (size_t)c * kPad, h);
+}
+
 // ------------------------------------------------------------------ fp8
 // Round to nearest even with saturation to +-448: clamp, then the gfx950
 // OCP e4m3 conversion (round to nearest even).
@@ -887,9 +902,11 @@ __global__ __launch_bounds__(kPackWavesSmall* kWave) void fused_small_kernel(Pac
     // rows: wavefront g of the grid takes chunk g % nchunks of token g / nchunks
     const int64_t P = s_ro[R];
     const bool cap_ok = P <= a.cap;
+    const bool refresh = first && wave == 0 && a.has_ring;   // wavefront-uniform
+    unsigned long long tail_h = 0;
     if (first && wave == 0) {
         if (!cap_ok && lane == 0) set_error(a.st, EP_ERR_CAPACITY);
-        if (a.has_ring) refresh_tail_cache(a);
+        if (refresh) tail_h = tail_read(a);
     }
     for (int64_t grp = blockIdx.x; grp < a.ngroups; grp += gridDim.x) {
         const int64_t gw = grp * kWaves + wave;
@@ -926,6 +943,7 @@ __global__ __launch_bounds__(kPackWavesSmall* kWave) void fused_small_kernel(Pac
 
     // closed-form publication by the last workgroup to finish its rows
     if (!a.has_ring) return;   // grid-uniform
+    if (refresh) tail_apply(a, tail_h);
     const ClosedOrder z = closed_order(a, s_ro);
     wait_vm();   // this wavefront's rows are complete
     __syncthreads();
@@ -1251,9 +1269,11 @@ __global__ __launch_bounds__(kPackWavesSmall* kWave) void ll_fused_small_kernel(
     // rows: wavefront g of the grid takes chunk g % nchunks of token g / nchunks
     const int64_t Q = s_eo[E];
     const bool cap_ok = Q <= a.cap;
+    const bool refresh = first && wave == 0 && a.has_ring;   // wavefront-uniform
+    unsigned long long tail_h = 0;
     if (first && wave == 0) {
         if (!cap_ok && lane == 0) set_error(a.st, EP_ERR_CAPACITY);
-        if (a.has_ring) refresh_tail_cache(a);
+        if (refresh) tail_h = tail_read(a);
     }
     for (int64_t grp = blockIdx.x; grp < a.ngroups; grp += gridDim.x) {
         const int64_t gw = grp * kWaves + wave;
@@ -1280,6 +1300,7 @@ __global__ __launch_bounds__(kPackWavesSmall* kWave) void ll_fused_small_kernel(
 
     // closed-form publication by the last workgroup to finish its rows
     if (!a.has_ring) return;   // grid-uniform
+    if (refresh) tail_apply(a, tail_h);
     wait_vm();   // this wavefront's rows are complete
     __syncthreads();
     if (tid == 0) s_last = arrive_last(a.arrive) && cap_ok && read_status(a.st) == 0;

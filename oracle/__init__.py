@@ -38,7 +38,7 @@ CMD_DTYPE = np.dtype([
 ])
 assert CMD_DTYPE.itemsize == 32
 
-GCC_FLAGS = ["-O2", "-fno-fast-math", "-ffp-contract=off", "-std=c11",
+GCC_FLAGS = ["-O2", "-fno-fast-math", "-ffp-contract=off", "-std=c11", "-fopenmp",
              "-Wall", "-Wextra", "-fPIC", "-shared"]
 
 
@@ -94,11 +94,18 @@ class Oracle:
         L.oracle_ll_descriptors.restype = i64
         L.oracle_ll_combine.argtypes = [i32, i32, i32, P, P, P, P, P]
         L.oracle_ll_combine.restype = None
+        L.oracle_set_threads.argtypes = [i32]
+        L.oracle_set_threads.restype = i32
         self.L = L
         self.path = path
 
     def row_bytes(self, H: int, fmt: int) -> int:
         return int(self.L.oracle_row_bytes(H, fmt))
+
+    def set_threads(self, n: int) -> int:
+        """Threads for the token loops of pack and combine; returns the number
+        in effect.  Results do not depend on it."""
+        return int(self.L.oracle_set_threads(n))
 
     def layout(self, topk_idx: np.ndarray, E: int, R: int) -> dict:
         """Rank membership, histograms, offsets and send slots."""
@@ -263,6 +270,10 @@ def default() -> Oracle:
 
 def row_bytes(H, fmt):
     return default().row_bytes(H, fmt)
+
+
+def set_threads(n):
+    return default().set_threads(n)
 
 
 def layout(topk_idx, E, R):

@@ -41,11 +41,20 @@
  *   oracle_ll_combine     pinned: per-choice brute force, identity, agreement
  *                         with oracle_combine on identity experts
  *   end-to-end values vs the pages: parity unpinned (no printed example)
+ *
+ * Threads: pack and combine handle each token on its own, so their token
+ * loops may be split over OpenMP threads (oracle_set_threads; the CPU
+ * baseline times one thread and all host cores).  A token's arithmetic and
+ * its order are the same on any number of threads.  Layout and descriptors
+ * are sequential by definition (running counters) and stay on one thread.
  */
 
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define ORC_OK 0
 #define ORC_ERR_INVALID_ARG 1
@@ -90,6 +99,18 @@ int64_t oracle_row_bytes(int H, int fmt) {
      * lines) */
     int64_t payload = (int64_t)H + 4LL * (H / 128);
     return (payload + 127) / 128 * 128;
+}
+
+/* Threads used by the token loops of pack and combine (n >= 1); returns the
+ * number in effect (1 when built without OpenMP). */
+int oracle_set_threads(int n) {
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+    return omp_get_max_threads();
+#else
+    (void)n;
+    return 1;
+#endif
 }
 
 /* ------------------------------------------------------------ routing layout
@@ -244,13 +265,10 @@ int oracle_pack(int T, int H, int E, int R, int k, int fmt,
     int epr = E / R;
     int64_t rb = oracle_row_bytes(H, fmt);
     int status = ORC_OK;
-    uint8_t* qrow = NULL;
-    uint8_t qbuf[1 << 16];
-    if (fmt == ORC_FMT_FP8) {
-        if (rb > (int64_t)sizeof(qbuf)) return ORC_ERR_INVALID_ARG;
-        qrow = qbuf;
-    }
+    if (fmt == ORC_FMT_FP8 && rb > (1 << 16)) return ORC_ERR_INVALID_ARG;
+#pragma omp parallel for schedule(static) reduction(max : status)
     for (int t = 0; t < T; t++) {
+        uint8_t qrow[1 << 16];   /* this token's fp8 row */
         const uint16_t* xrow = x + (int64_t)t * H;
         if (fmt == ORC_FMT_FP8) oracle_quantize_row(H, xrow, qrow);   /* once per token */
         for (int r = 0; r < R; r++) {
@@ -334,8 +352,9 @@ void oracle_combine(int T, int H, int E, int R, int k, const uint16_t* y,
                     const int32_t* topk_idx, const float* topk_w,
                     const int32_t* send_slot, double* out) {
     int epr = E / R;
-    double W[64];
+#pragma omp parallel for schedule(static)
     for (int t = 0; t < T; t++) {
+        double W[64];
         for (int r = 0; r < R; r++) W[r] = 0.0;
         for (int j = 0; j < k; j++) {
             int e = topk_idx[(int64_t)t * k + j];
@@ -403,9 +422,10 @@ int oracle_ll_pack(int T, int H, int k, int fmt, const uint16_t* x, const float*
     if (fmt == ORC_FMT_FP8 && H % 128 != 0) return ORC_ERR_INVALID_ARG;
     int64_t rb = oracle_row_bytes(H, fmt);
     int status = ORC_OK;
-    uint8_t qbuf[1 << 16];
-    if (fmt == ORC_FMT_FP8 && rb > (int64_t)sizeof(qbuf)) return ORC_ERR_INVALID_ARG;
+    if (fmt == ORC_FMT_FP8 && rb > (1 << 16)) return ORC_ERR_INVALID_ARG;
+#pragma omp parallel for schedule(static) reduction(max : status)
     for (int t = 0; t < T; t++) {
+        uint8_t qbuf[1 << 16];   /* this token's fp8 row */
         const uint16_t* xrow = x + (int64_t)t * H;
         if (fmt == ORC_FMT_FP8) oracle_quantize_row(H, xrow, qbuf);
         for (int j = 0; j < k; j++) {
@@ -482,6 +502,7 @@ int64_t oracle_ll_descriptors(int E, int R, int C, const int32_t* num_tokens_per
  * evaluated in double precision. */
 void oracle_ll_combine(int T, int H, int k, const uint16_t* y, const int32_t* topk_idx,
                        const float* topk_w, const int32_t* expert_slot, double* out) {
+#pragma omp parallel for schedule(static)
     for (int t = 0; t < T; t++) {
         double* o = out + (int64_t)t * H;
         for (int h = 0; h < H; h++) o[h] = 0.0;

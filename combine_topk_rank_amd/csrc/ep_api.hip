@@ -27,7 +27,7 @@ int validate_shape(const ep_shape_t* p) {
     const ep_shape_t& s = *p;
     if (s.T < 0 || s.H < 8 || s.H % 8 != 0 || s.H > kMaxH) return EP_ERR_INVALID_ARG;
     if (s.fmt != EP_FMT_BF16 && s.fmt != EP_FMT_FP8_E4M3_B128) return EP_ERR_INVALID_ARG;
-    if (s.fmt == EP_FMT_FP8_E4M3_B128 && s.H % 512 != 0) return EP_ERR_INVALID_ARG;
+    if (s.fmt == EP_FMT_FP8_E4M3_B128 && s.H % 128 != 0) return EP_ERR_INVALID_ARG;
     if (s.R < 1 || s.R > kMaxR || s.E < 1 || s.E > kMaxE || s.E % s.R != 0) return EP_ERR_INVALID_ARG;
     if (s.k < 1 || s.k > kMaxK || s.k > s.E) return EP_ERR_INVALID_ARG;
     const int64_t m = s.k > s.R ? s.k : s.R;

@@ -16,8 +16,8 @@ constexpr int kLayoutTile = 256;   // tokens per layout workgroup
 constexpr int kMsgRows = 8;        // rows per WRITE message (UCCL-EP s4.1 packing, s5.3 batch 8)
 constexpr int kMaxR = 64;          // a rank set is one 64-bit mask
 constexpr int kMaxE = 4096;        // per-expert LDS histogram bound
-constexpr int kMaxK = 32;
-constexpr int kMaxH = 1 << 24;        // rows stay far below 2^31 bytes (buffer records)          // experts of a token sit in lanes 0..k-1
+constexpr int kMaxK = 32;          // experts of a token sit in lanes 0..k-1
+constexpr int kMaxH = 1 << 24;     // rows stay far below 2^31 bytes (buffer records)
 constexpr int kPad = 8;            // 64-byte stride between per-channel counters
 // Bound on a grid-barrier wait, in s_memrealtime ticks (100 MHz): one second.
 constexpr unsigned long long kBarrierTimeoutTicks = 100000000ull;

@@ -541,13 +541,43 @@ __device__ inline float bf16lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ inline float bf16hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
 
 // Largest magnitude among the four bf16 values of two words, as the bf16
-// bit pattern (finite values).
+// bit pattern.  Magnitudes of bf16 values order like unsigned integers, an
+// infinity (0x7F80) above every finite value and NaN patterns above that.
 __device__ inline uint32_t max_bf16_mag(uint32_t a, uint32_t b) {
     const uint32_t a0 = a & 0x7FFFu, a1 = (a >> 16) & 0x7FFFu;
     const uint32_t b0 = b & 0x7FFFu, b1 = (b >> 16) & 0x7FFFu;
     const uint32_t x = a0 > a1 ? a0 : a1;
     const uint32_t y = b0 > b1 ? b0 : b1;
     return x > y ? x : y;
+}
+
+// The same with NaN patterns left out (they count as zero): a NaN has no
+// magnitude to compare, so it does not take part in a block's maximum.
+__device__ inline uint32_t max_bf16_mag_num(uint32_t a, uint32_t b) {
+    uint32_t m[4] = {a & 0x7FFFu, (a >> 16) & 0x7FFFu, b & 0x7FFFu, (b >> 16) & 0x7FFFu};
+    uint32_t r = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r = (m[i] <= 0x7F80u && m[i] > r) ? m[i] : r;
+    return r;
+}
+
+// Codes of the eight values of u (bytes in element order) whose product
+// x * inv is NaN -- x is NaN, or x is infinite in a block whose maximum is
+// infinite (inv = 0) -- become the NaN code 0x7F with the sign of x; the
+// clamp before the conversion would have turned them into -448.
+__device__ inline u32x2 nan_codes(const u32x4 u, float inv, u32x2 q) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    uint32_t out[2] = {q.x, q.y};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const uint32_t b = (w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+        const float p = __uint_as_float(b << 16) * inv;
+        if (p != p) {
+            const int sh = 8 * (e & 3);
+            out[e >> 2] = (out[e >> 2] & ~(0xFFu << sh)) | ((0x7Fu | ((b >> 8) & 0x80u)) << sh);
+        }
+    }
+    return u32x2{out[0], out[1]};
 }
 
 // max over the 16 lanes of a row group (a 128-element block is 16 lanes x 8)
@@ -634,8 +664,10 @@ __device__ inline void store_row_chunk_v(const PackArgs& a, int chunk, int32_t s
     } else {
         // quantise once: per 128-element block, a = max(amax, 1e-4),
         // codes = e4m3(x * (448 / a)), scale = a / 448.  The block max is
-        // taken on the bf16 bits: magnitudes of finite values order like
-        // unsigned integers, so no float copy of the row stays live.
+        // taken on the bf16 bits (magnitudes order like unsigned integers),
+        // so no float copy of the row stays live.  A lane holding an
+        // infinity or a NaN (rare) takes the slow steps: NaNs stay out of
+        // the maximum, NaN products get the NaN code.
         u32x2 q[VPL];
         float scale[VPL];
 #pragma unroll
@@ -643,7 +675,13 @@ __device__ inline void store_row_chunk_v(const PackArgs& a, int chunk, int32_t s
             const u32x4 u = v[i];
             const uint32_t m01 = max_bf16_mag(u.x, u.y);
             const uint32_t m23 = max_bf16_mag(u.z, u.w);
-            const uint32_t mw = m01 > m23 ? m01 : m23;
+            uint32_t mw = m01 > m23 ? m01 : m23;
+            const bool nonfinite = mw >= 0x7F80u;
+            if (mw > 0x7F80u) {
+                const uint32_t n01 = max_bf16_mag_num(u.x, u.y);
+                const uint32_t n23 = max_bf16_mag_num(u.z, u.w);
+                mw = n01 > n23 ? n01 : n23;
+            }
             float am = __uint_as_float(mw << 16);
             am = group16_max(am);
             const float av = fmaxf(am, 1e-4f);
@@ -654,6 +692,7 @@ __device__ inline void store_row_chunk_v(const PackArgs& a, int chunk, int32_t s
             uint32_t hi = e4m3x2<false>(bf16lo(u.z) * inv, bf16hi(u.z) * inv, 0);
             hi = e4m3x2<true>(bf16lo(u.w) * inv, bf16hi(u.w) * inv, hi);
             q[i] = u32x2{lo, hi};
+            if (nonfinite) q[i] = nan_codes(u, inv, q[i]);
         }
         // The tail of the row, [H, row_bytes), is 4-byte words: the scales of
         // blocks 0 .. H/128 - 1, then zeros.  This chunk writes the words of

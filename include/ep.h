@@ -42,7 +42,7 @@
  *     the device word `*dev_status` (int32, first error wins; the caller zeroes
  *     it and reads it after synchronising the stream).
  *   - Shapes: T tokens, H hidden size, E experts, R ranks, k experts per token.
- *     Requirements: T >= 0; H >= 8 and H % 8 == 0 (bf16) or H % 512 == 0
+ *     Requirements: T >= 0; H >= 8 and H % 8 == 0 (bf16) or H % 128 == 0
  *     (fp8); 1 <= R <= 64; E % R == 0; E <= 4096; 1 <= k <= min(E, 32);
  *     T * R < 2^31; T * max(k, R) < 2^31.
  *   - Expert e lives on rank e / (E / R).  A token goes once to every rank
@@ -159,7 +159,10 @@ int ep_dispatch_layout(const ep_shape_t* shape, const int32_t* topk_idx,
  *   send_buf       [capacity_rows, ep_row_bytes(H, fmt)]  rank-contiguous rows;
  *                  for fp8 each row is quantised once per token: per 128-element
  *                  block a = max(max|x|, 1e-4), codes e4m3(x * (448/a)) with
- *                  round-to-nearest-even and saturation, scale a/448
+ *                  round-to-nearest-even and saturation, scale a/448.  A NaN
+ *                  element takes no part in max|x|; an infinite one makes a
+ *                  and the scale infinite; a NaN product gets code 0x7F with
+ *                  the element's sign
  *   slot_src       int32 [capacity_rows]    token of each row
  *   slot_local_idx int32 [capacity_rows,k]  e_j - r*E/R if e_j is on the row's
  *                                           rank r, else -1

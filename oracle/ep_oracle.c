@@ -224,7 +224,12 @@ float oracle_e4m3_decode(uint8_t c) {
  *   inv = 448 / a  (one IEEE float division),
  *   q_i = e4m3(x_i * inv)  (one IEEE float multiply, then the conversion),
  *   s_b = a / 448  (one IEEE float division).
- * Dequantised value: q_i * s_b. */
+ * Dequantised value: q_i * s_b.
+ * Non-finite inputs (reading; the pages fix no fp8 behaviour): a NaN has no
+ * magnitude, so it takes no part in amax; an infinity does, which makes amax
+ * and the scale infinite and inv zero.  A product x_i * inv that is NaN (x_i
+ * NaN, or x_i infinite with inv = 0) gets the NaN code 0x7F with the sign of
+ * x_i, so the sign never depends on how a platform signs a NaN it creates. */
 void oracle_quantize_row(int H, const uint16_t* xrow, uint8_t* out_row) {
     int nb = H / 128;
     uint8_t* codes = out_row;
@@ -240,7 +245,10 @@ void oracle_quantize_row(int H, const uint16_t* xrow, uint8_t* out_row) {
         for (int i = 0; i < 128; i++) {
             float xv = bf16_to_float(xrow[b * 128 + i]);
             float prod = xv * inv;
-            codes[b * 128 + i] = oracle_e4m3_encode(prod);
+            if (isnan(prod))
+                codes[b * 128 + i] = (uint8_t)((signbit(xv) ? 0x80 : 0x00) | 0x7F);
+            else
+                codes[b * 128 + i] = oracle_e4m3_encode(prod);
         }
         float s = a / 448.0f;
         memcpy(scales + 4 * b, &s, 4);

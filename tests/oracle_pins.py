@@ -268,6 +268,29 @@ def pin_quantize(O, seed: int = 5):
             assert np.all((codes[blk][nz] >> 7) == (xf[blk][nz] < 0))
 
 
+def pin_quantize_golden(O):
+    """Hand-worked fp8 rows (tests/golden/fp8_quant_hand_example.json): one
+    whose two possible operation orders, x * (448 / a) and x / (a / 448),
+    round to different codes, and one with NaN and infinite elements."""
+    g = json.load(open(os.path.join(GOLDEN, "fp8_quant_hand_example.json")))
+    for row in g["rows"]:
+        H = row["H"]
+        x = np.zeros(H, np.uint16)
+        for i, b in row["x_bf16"].items():
+            x[int(i)] = int(b, 16)
+        want = np.zeros(H, np.uint8)
+        for i, c in row["codes"].items():
+            want[int(i)] = int(c, 16)
+        out = O.quantize_row(x)
+        bad = np.nonzero(out[:H] != want)[0]
+        assert bad.size == 0, (row["name"], [(int(i), hex(int(out[i])), hex(int(want[i])))
+                                             for i in bad[:4]])
+        nb = H // 128
+        scales = out[H:H + 4 * nb].copy().view(np.uint32)
+        assert [hex(int(v)) for v in scales] == row["scales_f32_bits"], row["name"]
+        assert not out[H + 4 * nb:].any()
+
+
 # ----------------------------------------------------------------- pack
 def pin_pack_golden(O):
     g = json.load(open(os.path.join(GOLDEN, "layout_hand_example.json")))
@@ -637,7 +660,7 @@ def pin_ll_combine_identity(O, names=("tiny", "decode")):
 ALL_PINS = [
     pin_layout_golden, pin_layout_bruteforce, pin_layout_invariants,
     pin_layout_expected_fanout, pin_layout_errors,
-    pin_e4m3_golden, pin_e4m3_nearest, pin_e4m3_torch, pin_quantize,
+    pin_e4m3_golden, pin_e4m3_nearest, pin_e4m3_torch, pin_quantize, pin_quantize_golden,
     pin_pack_golden, pin_pack_bruteforce,
     pin_descriptors_golden, pin_descriptors,
     pin_combine_golden, pin_combine_bruteforce, pin_combine_identity,

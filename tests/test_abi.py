@@ -45,16 +45,21 @@ def test_row_bytes(ep):
     assert ep.ep_row_bytes(4096, ep.EP_FMT_FP8_E4M3_B128) == 4224
     assert ep.ep_row_bytes(512, ep.EP_FMT_FP8_E4M3_B128) == 640
     assert ep.ep_row_bytes(512, ep.EP_FMT_BF16) == 1024
+    # fp8 at any multiple of 128: 384 codes + 3 scales = 396 -> 512
+    assert ep.ep_row_bytes(384, ep.EP_FMT_FP8_E4M3_B128) == 512
+    assert ep.ep_row_bytes(7168 + 64, ep.EP_FMT_FP8_E4M3_B128) == 0
     assert ep.ep_row_bytes(7, ep.EP_FMT_BF16) == 0
     assert ep.ep_row_bytes(7168, 9) == 0
 
 
 def test_workspace_bytes(ep):
     assert ep.ep_workspace_bytes(ep.shape(4096, 7168, 256, 32, 8)) > 0
+    for H in (128, 384, 640, 6400, 8320):   # fp8 needs H % 128 == 0 only
+        assert ep.ep_workspace_bytes(ep.shape(16, H, 16, 4, 2, 1)) > 0
     assert ep.ep_workspace_bytes(ep.shape(0, 64, 16, 4, 2)) > 0
     for bad in [ep.shape(-1, 64, 16, 4, 2), ep.shape(16, 7, 16, 4, 2), ep.shape(16, 64, 15, 4, 2),
                 ep.shape(16, 64, 16, 65, 2), ep.shape(16, 64, 16, 4, 0), ep.shape(16, 64, 16, 4, 17),
-                ep.shape(16, 64, 8192, 4, 2), ep.shape(16, 7168 + 128, 256, 32, 8, 1),
+                ep.shape(16, 64, 8192, 4, 2), ep.shape(16, 7168 + 64, 256, 32, 8, 1),
                 ep.shape(16, 64, 16, 4, 2, 5), ep.shape(16, 64, 64, 4, 33)]:
         assert ep.ep_workspace_bytes(bad) == 0
 

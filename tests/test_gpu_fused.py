@@ -79,6 +79,8 @@ CASES = [
     (256, 136, 32, 4, 3, 0, 0.5, 1, 1024, 256),
     (128, 512, 32, 16, 8, 1, 0.0, 4, 16, 4),
     (256, 4096, 128, 8, 4, 1, 0.2, 8, 1024, 256),
+    (100, 384, 64, 16, 4, 1, 0.1, 4, 64, 16),
+    (256, 640, 32, 4, 3, 1, 0.0, 1, 1024, 256),
     # above 256 tokens: layout, then pack (closed form or streaming publication)
     (300, 7168, 256, 32, 8, 0, 0.0, 8, 1024, 256),
     (1100, 7168, 64, 64, 8, 1, 0.1, 8, 64, 16),

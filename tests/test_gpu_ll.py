@@ -64,6 +64,7 @@ LL_CASES = [
     (700, 1024, 64, 64, 4, 0, 0.0, 64, 32, 8),
     (600, 128, 4096, 64, 32, 0, 0.05, 8, 1024, 256),
     (3000, 136, 256, 32, 8, 0, 0.2, 5, 1024, 64),
+    (2000, 384, 64, 16, 4, 1, 0.0, 4, 1024, 256),
 ]
 
 
@@ -145,6 +146,7 @@ LL_FUSED_CASES = [
     (200, 1024, 64, 64, 4, 0, 0.0, 64, 32, 8),
     (256, 128, 1024, 64, 32, 0, 0.05, 8, 1024, 256),
     (256, 136, 256, 32, 8, 0, 0.2, 5, 1024, 64),
+    (100, 128, 64, 8, 4, 1, 0.1, 2, 64, 16),
 ]
 
 

@@ -117,6 +117,14 @@ CASES = [
     (257, 512, 32, 16, 8, 1, 0.0, 4, 16, 4),
     (130, 4096, 128, 8, 4, 1, 0.2, 8, 1024, 256),
     (4099, 136, 32, 4, 3, 0, 0.5, 1, 1024, 256),
+    # fp8 rows whose H is a multiple of 128 but not of 512: the last lane
+    # group of a chunk holds a partial row (small and large batches, one and
+    # several chunks per row)
+    (300, 128, 16, 4, 2, 1, 0.1, 2, 64, 16),
+    (3000, 384, 64, 8, 4, 1, 0.0, 4, 1024, 256),
+    (200, 640, 64, 16, 4, 1, 0.0, 3, 1024, 256),
+    (1500, 6400, 256, 32, 8, 1, 0.0, 8, 1024, 256),
+    (700, 8320, 64, 16, 4, 1, 0.05, 8, 1024, 256),
 ]
 
 

@@ -32,6 +32,9 @@ MUTANTS = {
     "quant_max_not_abs": ("float v = fabsf(bf16_to_float(xrow[b * 128 + i]));",
                           "float v = bf16_to_float(xrow[b * 128 + i]);"),
     "quant_scale_inverted": ("float s = a / 448.0f;", "float s = 448.0f / a;"),
+    "quant_divide_by_scale": ("float prod = xv * inv;", "float prod = xv / (a / 448.0f);"),
+    "quant_nan_in_amax": ("if (v > amax) amax = v;", "if (!(v <= amax)) amax = v;"),
+    "quant_nan_sign_dropped": ("(uint8_t)((signbit(xv) ? 0x80 : 0x00) | 0x7F);", "(uint8_t)0x7F;"),
     "row_pitch_unpadded": ("return (payload + 127) / 128 * 128;", "return payload;"),
     "row_pad_short": ("i < pitch; i++) out_row[i] = 0;", "i < pitch - 4; i++) out_row[i] = 0;"),
     "quant_block_64": ("float amax = 0.0f;\n        for (int i = 0; i < 128; i++) {",

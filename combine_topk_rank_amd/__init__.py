@@ -16,6 +16,9 @@ The functions keep the C names:
     ep_dispatch(shape, x, topk_idx, topk_w, rank_offset, send_slot, send_buf,
                 slot_src, slot_local_idx, slot_local_w, ring, workspace,
                 dev_status, stream=None)
+    ep_dispatch_fused_noalloc(shape, x, topk_idx, topk_w, <layout outputs>, send_buf,
+                              slot_src, slot_local_idx, slot_local_w, ring, dev_status,
+                              stream=None, clear_scratch=False)
     ep_combine(shape, y, topk_idx, topk_w, send_slot, out, dev_status, stream=None)
         (y_rows is y.shape[0])
     Ring(depth, channels, max_inflight, timeout_ns)   # ep_ring_* calls
@@ -94,6 +97,9 @@ def _load() -> ctypes.CDLL:
     L.ep_dispatch_fused.argtypes = [S, P, P, P, P, P, P, P, P, P, P, i64, P, P, P, P, P, sz, P,
                                     P]
     L.ep_dispatch_fused.restype = ctypes.c_int
+    L.ep_dispatch_fused_noalloc.argtypes = [S, P, P, P, P, P, P, P, P, P, P, i64, P, P, P, P,
+                                            i32, P, P]
+    L.ep_dispatch_fused_noalloc.restype = ctypes.c_int
     L.ep_combine.argtypes = [S, P, i64, P, P, P, P, P, P]
     L.ep_combine.restype = ctypes.c_int
     L.ep_dispatch_layout_ll.argtypes = [S, P, P, P, P, sz, P, P]
@@ -214,6 +220,21 @@ def ep_dispatch_fused(s, x, topk_idx, topk_w, num_tokens_per_rank, num_tokens_pe
                                workspace.numel() * workspace.element_size(), _ptr(dev_status),
                                _stream(stream))
     _check(st, "ep_dispatch_fused")
+
+
+def ep_dispatch_fused_noalloc(s, x, topk_idx, topk_w, num_tokens_per_rank,
+                              num_tokens_per_expert, rank_offset, expert_offset, is_token_in_rank,
+                              send_slot, send_buf, slot_src, slot_local_idx, slot_local_w, ring,
+                              dev_status, stream=None, capacity_rows: Optional[int] = None,
+                              clear_scratch: bool = False) -> None:
+    cap = send_buf.shape[0] if capacity_rows is None else capacity_rows
+    st = lib.ep_dispatch_fused_noalloc(
+        ctypes.byref(s), _ptr(x), _ptr(topk_idx), _ptr(topk_w), _ptr(num_tokens_per_rank),
+        _ptr(num_tokens_per_expert), _ptr(rank_offset), _ptr(expert_offset),
+        _ptr(is_token_in_rank), _ptr(send_slot), _ptr(send_buf), cap, _ptr(slot_src),
+        _ptr(slot_local_idx), _ptr(slot_local_w), ring.handle if ring is not None else None,
+        1 if clear_scratch else 0, _ptr(dev_status), _stream(stream))
+    _check(st, "ep_dispatch_fused_noalloc")
 
 
 def ep_combine(s, y, topk_idx, topk_w, send_slot, out, dev_status, stream=None) -> None:
@@ -392,6 +413,17 @@ class Buffers:
                           self.is_token_in_rank, self.send_slot, self.send_buf, self.slot_src,
                           self.slot_local_idx, self.slot_local_w, ring, self.workspace,
                           self.dev_status, stream)
+
+    def dispatch_fused_noalloc(self, x, topk_idx, topk_w, ring=None, stream=None,
+                               clear_scratch=False):
+        """layout + dispatch in one call on the library's own device scratch
+        (no workspace; the buffers' own workspace is not used)"""
+        ep_dispatch_fused_noalloc(self.shape, x, topk_idx, topk_w, self.num_tokens_per_rank,
+                                  self.num_tokens_per_expert, self.rank_offset,
+                                  self.expert_offset, self.is_token_in_rank, self.send_slot,
+                                  self.send_buf, self.slot_src, self.slot_local_idx,
+                                  self.slot_local_w, ring, self.dev_status, stream,
+                                  clear_scratch=clear_scratch)
 
     def combine(self, y, topk_idx, topk_w, stream=None):
         ep_combine(self.shape, y, topk_idx, topk_w, self.send_slot, self.out, self.dev_status,

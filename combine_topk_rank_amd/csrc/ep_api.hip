@@ -15,6 +15,8 @@ void record_hip_error(hipError_t e, const char* what) {
     snprintf(g_last_error, sizeof g_last_error, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
 }
 
+void record_error(const char* what) { snprintf(g_last_error, sizeof g_last_error, "%s", what); }
+
 size_t row_bytes(int32_t H, int32_t fmt) {
     if (fmt == EP_FMT_BF16) return (size_t)2 * H;
     // H code bytes, one float scale per 128 elements, then zero bytes up to a

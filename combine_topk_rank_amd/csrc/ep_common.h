@@ -94,6 +94,8 @@ size_t row_bytes(int32_t H, int32_t fmt);
 
 // Remember the last failing HIP call of this thread (ep_last_error).
 void record_hip_error(hipError_t e, const char* what);
+// Remember why a call was rejected on the host (ep_last_error).
+void record_error(const char* what);
 
 #define EP_HIP_CHECK(expr)                                  \
     do {                                                    \

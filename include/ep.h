@@ -200,6 +200,27 @@ int ep_dispatch_fused(const ep_shape_t* shape, const void* x, const int32_t* top
                       ep_ring_t* ring, void* workspace, size_t workspace_bytes,
                       int32_t* dev_status, hipStream_t stream);
 
+/* ep_dispatch_fused for callers that cannot allocate device memory or pass a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  Same arguments (minus the workspace), outputs,
+ * meanings and device errors as ep_dispatch_fused.  Its scratch is a 4 MiB
+ * device array inside the library, one per GPU, held until the process ends;
+ * the call allocates nothing.  Shapes whose ep_workspace_bytes exceed 4 MiB
+ * are rejected with EP_ERR_INVALID_ARG before anything is enqueued
+ * (ep_last_error says why).  The first call on each GPU zero-fills that
+ * GPU's array with a kernel on `stream`; clear_scratch != 0 does it again
+ * (needed only after a call reported EP_ERR_TIMEOUT).  Every call on a GPU
+ * shares its array: calls on one GPU must be ordered (one stream, or
+ * synchronised); calls that overlap in time race. */
+int ep_dispatch_fused_noalloc(const ep_shape_t* shape, const void* x, const int32_t* topk_idx,
+                              const float* topk_w, int32_t* num_tokens_per_rank,
+                              int32_t* num_tokens_per_expert, int32_t* rank_offset,
+                              int32_t* expert_offset, uint8_t* is_token_in_rank,
+                              int32_t* send_slot, void* send_buf, int64_t capacity_rows,
+                              int32_t* slot_src, int32_t* slot_local_idx, float* slot_local_w,
+                              ep_ring_t* ring, int32_t clear_scratch, int32_t* dev_status,
+                              hipStream_t stream);
+
 /* Combine.  UCCL-EP s6 (EP combine), GPU communication notes s5
  * (DeepEP combine).  The returned expert outputs y sit in the dispatch
  * layout: y row send_slot[t,r] is rank r's result for token t.
@@ -363,7 +384,8 @@ int ep_ring_loopback_stats(const ep_ring_t* ring, int64_t* n_done, int64_t* n_er
 const char* ep_status_str(int status);
 
 /* Description of the last HIP runtime failure seen by this library on the
- * calling thread (the call that returned EP_ERR_HIP), or "" if none. */
+ * calling thread (the call that returned EP_ERR_HIP), or of the last host-side
+ * rejection that records a reason, or "" if none. */
 const char* ep_last_error(void);
 
 #ifdef __cplusplus

@@ -143,3 +143,18 @@ def test_oracle_and_hip_path_share_nothing():
     for p in orc:
         text = open(p).read()
         assert "combine_topk_rank_amd" not in text and "ep.h" not in text, p
+
+
+def test_noalloc_rejects_shapes_beyond_its_scratch(ep):
+    """The no-allocation one-call dispatch owns 4 MiB of device scratch per
+    GPU; a shape that needs more is rejected on the host with a reason,
+    before any HIP call."""
+    big = ep.shape(65536, 64, 4096, 64, 8)
+    assert ep.ep_workspace_bytes(big) > (4 << 20)
+    st = ep.lib.ep_dispatch_fused_noalloc(ctypes.byref(big), *([None] * 10), 0, *([None] * 4), 0,
+                                          None, None)
+    assert st == ep.EP_ERR_INVALID_ARG
+    assert b"4 MiB" in ep.lib.ep_last_error()
+    bad = ep.shape(16, 7, 16, 4, 2)
+    assert ep.lib.ep_dispatch_fused_noalloc(ctypes.byref(bad), *([None] * 10), 0, *([None] * 4),
+                                            0, None, None) == ep.EP_ERR_INVALID_ARG

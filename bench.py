@@ -111,7 +111,8 @@ def quantiles(vals) -> dict:
 KERNEL_SOURCES = ["combine_topk_rank_amd/csrc/ep_dispatch.hip",
                   "combine_topk_rank_amd/csrc/ep_combine.hip",
                   "combine_topk_rank_amd/csrc/ep_layout.hip",
-                  "combine_topk_rank_amd/csrc/ep_common.h"]
+                  "combine_topk_rank_amd/csrc/ep_common.h",
+                  "combine_topk_rank_amd/csrc/ep_ring_proto.h"]
 
 
 def measured_traffic(kernel_prefix: str, workload: str):
@@ -344,6 +345,11 @@ class Runner:
         b.combine(st["y"], st["idx"], st["w"], s)
         if ev is not None:
             ev[3].record(s)
+        if self.lb is not None:
+            # loopback copies read the send buffer: the next dispatch may
+            # rewrite it only once every command has completed
+            self.torch.cuda.synchronize()
+            self.ring.wait_complete(60_000_000_000)
 
     def status(self) -> int:
         for st in self.sets:

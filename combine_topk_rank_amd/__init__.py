@@ -130,6 +130,8 @@ def _load() -> ctypes.CDLL:
     L.ep_ring_set_loopback.restype = ctypes.c_int
     L.ep_ring_completed.argtypes = [P, i32]
     L.ep_ring_completed.restype = i64
+    L.ep_ring_check_completion.argtypes = [P, P, P, i32, P, P]
+    L.ep_ring_check_completion.restype = ctypes.c_int
     L.ep_ring_wait_complete.argtypes = [P, i64]
     L.ep_ring_wait_complete.restype = ctypes.c_int
     i64p = ctypes.POINTER(i64)
@@ -349,6 +351,13 @@ class Ring:
 
     def completed(self, channel: int) -> int:
         return int(lib.ep_ring_completed(self.handle, channel))
+
+    def check_completion(self, channels, tickets, done, stream=None) -> None:
+        """ep_ring_check_completion: device tensors channels (int32), tickets
+        (uint64 as int64) and done (uint8), all of length n."""
+        _check(lib.ep_ring_check_completion(self.handle, _ptr(channels), _ptr(tickets),
+                                            int(done.numel()), _ptr(done), _stream(stream)),
+               "ep_ring_check_completion")
 
     def wait_complete(self, timeout_ns: int = 10_000_000_000) -> None:
         _check(lib.ep_ring_wait_complete(self.handle, timeout_ns), "ep_ring_wait_complete")

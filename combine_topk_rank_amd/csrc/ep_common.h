@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include "ep.h"
+#include "ep_ring_proto.h"
 
 namespace ep {
 
@@ -22,26 +23,6 @@ constexpr int kPad = 8;            // 64-byte stride between per-channel counter
 // Bound on a grid-barrier wait, in s_memrealtime ticks (100 MHz): one second.
 constexpr unsigned long long kBarrierTimeoutTicks = 100000000ull;
 
-// One FIFO slot as it sits in the ring: four 64-bit words, each
-//   bits  0..15  tag = low 16 bits of (ticket + 1)
-//   bits 16..63  48 bits of the command:
-//     w0: type (8) | op (8) | num_tokens (16) | 0 (16)
-//     w1: dst_rank (16) | size_or_value (32)
-//     w2: src_offset (48)
-//     w3: dst_offset (48)
-// The GPU writes the words with two plain 16-byte stores followed by a
-// system-scope release, in any order and with no flag write; a consumer that reads the four words (8-byte
-// loads are single-copy atomic) and finds the expected tag in all of them has
-// the whole command.  A stale slot holds the tag of ticket - depth + 1, which
-// differs as long as depth < 65536.  The consumer decodes slots into
-// ep_transfer_cmd_t.
-struct RingSlot {
-    uint64_t w[4];
-};
-static_assert(sizeof(RingSlot) == 32, "ring slot is 32 bytes");
-constexpr uint64_t kMaxRingOffset = (1ull << 48) - 1;
-constexpr int32_t kMaxRingDepth = 65535;
-
 // Device view of a TransferCmd ring.
 struct RingDev {
     RingSlot* slots;                       // host-pinned, [channels][depth]
@@ -49,12 +30,22 @@ struct RingDev {
     unsigned long long* head;              // device, ticket counter, stride kPad
     unsigned long long* tail_cache;        // device, last consumer position seen, stride kPad
     unsigned long long* poll;              // device, 1 while a lane reads host_tail, stride kPad
+    const unsigned long long* completed;   // host-pinned, commands completed, stride kPad
     int32_t depth;
     int32_t channels;
     int32_t max_inflight;
     int32_t pad_;
     unsigned long long timeout_ticks;      // in s_memrealtime ticks
 };
+
+// CheckCompletion (UCCL-EP article s2.2): whether the command with `ticket`
+// on channel c has completed, from the consumer's per-channel count of
+// completed commands (commands of a channel complete in ticket order).
+// Never waits.
+__device__ inline bool ring_check_completion(const RingDev& g, int c, unsigned long long ticket) {
+    return __hip_atomic_load(g.completed + (size_t)c * kPad, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_SYSTEM) > ticket;
+}
 
 // Carved workspace.
 // Workspace header: grid barrier words (256 B), then arrival counters, one

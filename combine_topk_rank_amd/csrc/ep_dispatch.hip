@@ -94,22 +94,18 @@ __device__ inline void ring_write(const RingDev& g, int c, unsigned long long ti
                                   uint32_t op, uint32_t ntok, uint32_t dst_rank, uint32_t size_val,
                                   uint64_t src_off, uint64_t dst_off) {
     RingSlot* slot = g.slots + (size_t)c * g.depth + (size_t)(ticket % (unsigned long long)g.depth);
-    const uint64_t tag = (uint64_t)((ticket + 1) & 0xFFFFull);
-    const uint64_t w0 = tag | ((uint64_t)(type & 0xFF) << 16) | ((uint64_t)(op & 0xFF) << 24) |
-                        ((uint64_t)(ntok & 0xFFFF) << 32);
-    const uint64_t w1 = tag | ((uint64_t)(dst_rank & 0xFFFF) << 16) | ((uint64_t)size_val << 32);
-    const uint64_t w2 = tag | ((src_off & kMaxRingOffset) << 16);
-    const uint64_t w3 = tag | ((dst_off & kMaxRingOffset) << 16);
+    uint64_t w[4];
+    ring_slot_words(ticket, type, op, ntok, dst_rank, size_val, src_off, dst_off, w);
     if (SYS) {
         const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(slot, (int32_t)sizeof(RingSlot));
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, (u64x2{w0, w1})), rs, 0,
-                                               0, kStoreSystem);
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, (u64x2{w2, w3})), rs, 16,
-                                               0, kStoreSystem);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, (u64x2{w[0], w[1]})), rs,
+                                               0, 0, kStoreSystem);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, (u64x2{w[2], w[3]})), rs,
+                                               16, 0, kStoreSystem);
     } else {
         u64x2* p = reinterpret_cast<u64x2*>(slot);
-        p[0] = u64x2{w0, w1};
-        p[1] = u64x2{w2, w3};
+        p[0] = u64x2{w[0], w[1]};
+        p[1] = u64x2{w[2], w[3]};
     }
 }
 
@@ -289,6 +285,18 @@ __device__ void publish_group(const PackArgs& a, const RankView& rv,
             }
         }
     }
+    bool hit[3];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        hit[i] = m0 >= 0 && cnt3[i] > 0;
+        if (hit[i] && mbase + m0 + i >= a.max_msgs) bad = true;   // message table too small
+    }
+    // An inconsistent group is reported before it counts any row or takes
+    // any ticket: none of its messages is ever published.
+    if (__ballot(bad)) {
+        if (bad) set_error(a.st, EP_ERR_INVALID_ARG);
+        return;
+    }
     // the status, the cached consumer positions and the (at most three)
     // arrival atomics go out together: one latency
     const int32_t st0 = read_status(a.st);
@@ -297,16 +305,9 @@ __device__ void publish_group(const PackArgs& a, const RankView& rv,
         tc = __hip_atomic_load(a.ring.tail_cache + (size_t)lane * kPad, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
     int32_t old3[3] = {0, 0, 0};
-    bool hit[3];
 #pragma unroll
-    for (int i = 0; i < 3; ++i) {
-        hit[i] = m0 >= 0 && cnt3[i] > 0;
-        if (hit[i] && mbase + m0 + i >= a.max_msgs) {
-            hit[i] = false;   // message table too small: not from this layout
-            bad = true;
-        }
+    for (int i = 0; i < 3; ++i)
         if (hit[i]) old3[i] = atomicAdd(&a.msg_arrivals[mbase + m0 + i], cnt3[i]);
-    }
     // completed messages, in ascending order, in registers (no indexed
     // private array)
     int32_t done_m[3] = {0, 0, 0};
@@ -324,7 +325,6 @@ __device__ void publish_group(const PackArgs& a, const RankView& rv,
             ++ndone;
         }
     }
-    if (bad) set_error(a.st, EP_ERR_INVALID_ARG);
     if (!__ballot(ndone > 0)) return;
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     const int c = lane % C;
@@ -785,9 +785,15 @@ __global__ __launch_bounds__(WAVES * kWave) void pack_kernel(PackArgs a) {
         if (!cap_ok && lane == 0) set_error(a.st, EP_ERR_CAPACITY);
         if (PUB != kPubNone) refresh_tail_cache(a);
     }
-    // stream publication runs when the ring exists and the rows fit
+    // stream publication runs when the ring exists and the rows fit; every
+    // wavefront hands its slots over after each group, but wavefront 0
+    // publishes only if no error (e.g. a bad expert id found by the layout)
+    // was reported before the kernel started -- then no command goes out,
+    // as in the closed form
     const bool streaming = PUB == kPubStream && cap_ok;
-    if (streaming && blockIdx.x == 0 && wave == 0) publish_empty_ranks(a);
+    bool pub_ok = false;   // wavefront 0 only
+    if (streaming && wave == 0) pub_ok = bcast(read_status(a.st), 0) == 0;
+    if (pub_ok && blockIdx.x == 0) publish_empty_ranks(a);
     __shared__ RankView rv;   // read by wavefront 0 only, which wrote it
     if (streaming && wave == 0) load_rank_view(a, rv);
     // groups of kWaves wavefronts, taken in launch order; a workgroup that
@@ -820,7 +826,7 @@ __global__ __launch_bounds__(WAVES * kWave) void pack_kernel(PackArgs a) {
     // visible to every agent, so no write-back precedes the arrivals.
     wait_vm();
     __syncthreads();
-    if (wave == 0) {
+    if (wave == 0 && pub_ok) {
         // The arrivals and the descriptors of the group.  Meanwhile the
         // other wavefronts go on with the next group, whose slots go to the
         // other buffer; this one is written again only after the next

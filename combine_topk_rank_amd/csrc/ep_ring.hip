@@ -47,6 +47,8 @@ struct ep_ring {
     int device = 0;
     ep::RingSlot* slots = nullptr;             // host-pinned
     unsigned long long* host_tail = nullptr;   // host-pinned, stride kPad
+    unsigned long long* host_completed = nullptr;   // host-pinned, stride kPad: completed[c]
+                                                    // mirrored for the GPU
     unsigned long long* dev_state = nullptr;   // device: head, tail_cache, poll; each [C*kPad]
     unsigned long long timeout_ticks = 0;
     std::vector<unsigned long long> pos;       // consumer position per channel
@@ -85,6 +87,7 @@ RingDev ring_device_view(ep_ring_t* r) {
     d.head = r->dev_state;
     d.tail_cache = r->dev_state + (size_t)r->channels * kPad;
     d.poll = r->dev_state + 2 * (size_t)r->channels * kPad;
+    d.completed = r->host_completed;
     d.depth = r->depth;
     d.channels = r->channels;
     d.max_inflight = r->max_inflight;
@@ -98,50 +101,11 @@ using namespace ep;
 
 namespace {
 
-// Read one slot (four 8-byte loads) and decode it when every word carries
-// the tag of ticket `want - 1`.
-inline bool read_slot(const RingSlot* s, uint32_t want, ep_transfer_cmd_t* out) {
-    const uint64_t tag = want & 0xFFFFu;
-    uint64_t w[4];
-    for (int i = 0; i < 4; ++i) {
-        w[i] = __atomic_load_n(&s->w[i], __ATOMIC_ACQUIRE);
-        if ((w[i] & 0xFFFFu) != tag) return false;
-    }
-    if (out) {
-        out->seq = want;
-        out->type = (uint8_t)(w[0] >> 16);
-        out->op = (uint8_t)(w[0] >> 24);
-        out->num_tokens = (uint16_t)(w[0] >> 32);
-        out->dst_rank = (uint32_t)((w[1] >> 16) & 0xFFFFu);
-        out->size_or_value = (uint32_t)(w[1] >> 32);
-        out->src_offset = w[2] >> 16;
-        out->dst_offset = w[3] >> 16;
-    }
-    return true;
-}
-
-// Pop up to `max` published commands of channel c; returns the number popped.
+// Pop up to `max` published commands of channel c (the slot format and the
+// pop itself: ep_ring_proto.h); returns the number popped.
 int64_t pop_channel(ep_ring_t* r, int c, ep_transfer_cmd_t* out, int64_t max, bool publish) {
-    unsigned long long p = r->pos[c];
-    const RingSlot* base = r->slots + (size_t)c * r->depth;
-    int64_t n = 0;
-    while (n < max) {
-        const RingSlot* s = base + (p % (unsigned long long)r->depth);
-        // Slot lines written by the GPU miss in the CPU caches; touching the
-        // lines a few slots ahead overlaps those misses when a backlog exists.
-        if ((p & 1) == 0) {
-            __builtin_prefetch(base + ((p + 8) % (unsigned long long)r->depth), 0, 0);
-            __builtin_prefetch(base + ((p + 16) % (unsigned long long)r->depth), 0, 0);
-        }
-        if (!read_slot(s, (uint32_t)(p + 1), out ? &out[n] : nullptr)) break;
-        ++p;
-        ++n;
-    }
-    if (n) {
-        r->pos[c] = p;
-        if (publish) __atomic_store_n(&r->host_tail[(size_t)c * kPad], p, __ATOMIC_RELEASE);
-    }
-    return n;
+    return ring_pop(r->slots + (size_t)c * r->depth, (uint32_t)r->depth, &r->pos[c],
+                    publish ? &r->host_tail[(size_t)c * kPad] : nullptr, out, max);
 }
 
 constexpr int kDrainBatch = 32;  // UCCL-EP s5.2 DRAIN_BATCH_SIZE
@@ -175,6 +139,24 @@ __global__ __launch_bounds__(256) void loopback_copy(CopyList l) {
 
 __global__ void loopback_add(AddList l) {
     if ((int)threadIdx.x < l.n) atomicAdd(l.p[threadIdx.x], l.v[threadIdx.x]);
+}
+
+// Count n more commands of channel c as completed, and publish the new
+// count where the GPU can read it (one writer per channel at a time: the
+// proxy thread serving it, or ep_ring_drain while no proxy runs).
+void add_completed(ep_ring_t* r, int c, int64_t n) {
+    const int64_t v = r->completed[c].fetch_add(n, std::memory_order_release) + n;
+    __atomic_store_n(&r->host_completed[(size_t)c * kPad], (unsigned long long)v, __ATOMIC_RELEASE);
+}
+
+// One thread per queried command: 1 if complete, 0 if not, 2 for a channel
+// outside the ring.
+__global__ void check_completion_kernel(RingDev g, const int32_t* channels,
+                                        const uint64_t* tickets, int32_t n, uint8_t* done) {
+    const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+    if (i >= n) return;
+    const int c = channels[i];
+    done[i] = (c < 0 || c >= g.channels) ? 2 : (ring_check_completion(g, c, tickets[i]) ? 1 : 0);
 }
 
 int64_t now_ns() {
@@ -256,7 +238,7 @@ void execute_batch(ep_ring_t* r, const ep_transfer_cmd_t* b, int64_t n, hipStrea
 }
 
 void finish(ep_ring_t* r, const Pending& p) {
-    r->completed[p.c].fetch_add(p.n, std::memory_order_release);
+    add_completed(r, p.c, p.n);
     r->lb_done.fetch_add(p.n);
     const int64_t lat = now_ns() - p.t_pop;
     r->lb_lat_sum_ns.fetch_add(lat * p.n);
@@ -303,7 +285,7 @@ void proxy_loop(ep_ring_t* r, int first, int stride) {
                         if (ev) free_ev.push_back(ev);
                     }
                 } else {
-                    r->completed[c].fetch_add(n, std::memory_order_release);
+                    add_completed(r, c, n);
                 }
             }
         }
@@ -363,10 +345,13 @@ extern "C" ep_ring_t* ep_ring_create(int32_t depth, int32_t channels, int32_t ma
                              hipHostMallocCoherent | hipHostMallocMapped) == hipSuccess;
     ok = ok && hipHostMalloc((void**)&r->host_tail, tail_bytes,
                              hipHostMallocCoherent | hipHostMallocMapped) == hipSuccess;
+    ok = ok && hipHostMalloc((void**)&r->host_completed, tail_bytes,
+                             hipHostMallocCoherent | hipHostMallocMapped) == hipSuccess;
     ok = ok && hipMalloc((void**)&r->dev_state, 3 * tail_bytes) == hipSuccess;
     if (ok) {
         std::memset(r->slots, 0, slot_bytes);
         std::memset(r->host_tail, 0, tail_bytes);
+        std::memset(r->host_completed, 0, tail_bytes);
         ok = hipMemset(r->dev_state, 0, 3 * tail_bytes) == hipSuccess &&
              hipDeviceSynchronize() == hipSuccess;
     }
@@ -383,6 +368,7 @@ extern "C" int ep_ring_destroy(ep_ring_t* r) {
     int st = EP_OK;
     if (r->slots && hipHostFree(r->slots) != hipSuccess) st = EP_ERR_HIP;
     if (r->host_tail && hipHostFree(r->host_tail) != hipSuccess) st = EP_ERR_HIP;
+    if (r->host_completed && hipHostFree(r->host_completed) != hipSuccess) st = EP_ERR_HIP;
     if (r->dev_state && hipFree(r->dev_state) != hipSuccess) st = EP_ERR_HIP;
     delete r;
     return st;
@@ -394,6 +380,7 @@ extern "C" int ep_ring_reset(ep_ring_t* r) {
     if (r->running.load()) return EP_ERR_BUSY;
     std::memset(r->slots, 0, (size_t)r->channels * r->depth * sizeof(RingSlot));
     std::memset(r->host_tail, 0, (size_t)r->channels * kPad * sizeof(unsigned long long));
+    std::memset(r->host_completed, 0, (size_t)r->channels * kPad * sizeof(unsigned long long));
     std::fill(r->pos.begin(), r->pos.end(), 0ull);
     for (int c = 0; c < r->channels; ++c) r->completed[c].store(0);
     EP_HIP_CHECK(hipMemset(r->dev_state, 0, 3 * (size_t)r->channels * kPad * sizeof(unsigned long long)));
@@ -408,7 +395,7 @@ extern "C" int ep_ring_drain(ep_ring_t* r, int32_t channel, ep_transfer_cmd_t* o
     std::lock_guard<std::mutex> g(r->mu);
     if (r->running.load()) return EP_ERR_BUSY;
     *n_out = (int32_t)pop_channel(r, channel, out, max, true);
-    r->completed[channel].fetch_add(*n_out);
+    add_completed(r, channel, *n_out);
     return EP_OK;
 }
 
@@ -495,6 +482,19 @@ extern "C" int ep_ring_set_loopback(ep_ring_t* r, const void* src, uint64_t src_
 extern "C" int64_t ep_ring_completed(const ep_ring_t* r, int32_t channel) {
     if (!r || channel < 0 || channel >= r->channels) return -1;
     return r->completed[channel].load(std::memory_order_acquire);
+}
+
+extern "C" int ep_ring_check_completion(const ep_ring_t* r, const int32_t* channels,
+                                        const uint64_t* tickets, int32_t n, uint8_t* done,
+                                        hipStream_t stream) {
+    if (!r || n < 0 || (n > 0 && (!channels || !tickets || !done))) return EP_ERR_INVALID_ARG;
+    if (n == 0) return EP_OK;
+    clear_hip_error();
+    hipLaunchKernelGGL(check_completion_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0,
+                       stream, ring_device_view(const_cast<ep_ring_t*>(r)), channels, tickets, n,
+                       done);
+    EP_HIP_CHECK(hipGetLastError());
+    return EP_OK;
 }
 
 extern "C" int ep_ring_wait_complete(ep_ring_t* r, int64_t timeout_ns) {

@@ -174,8 +174,13 @@ int ep_dispatch_layout(const ep_shape_t* shape, const int32_t* topk_idx,
  *                  ATOMIC ADD of cnt_r (also for cnt_r = 0).
  * Device errors: EP_ERR_CAPACITY (rows >= capacity_rows are not written and
  * no descriptor is emitted), EP_ERR_RING_TIMEOUT (the ring stayed full for
- * longer than its timeout; the ring must then be reset), EP_ERR_INVALID_ARG
- * (send_slot and rank_offset do not come from the same layout). */
+ * longer than its timeout), EP_ERR_INVALID_ARG (send_slot and rank_offset do
+ * not come from the same layout; a group of rows found inconsistent publishes
+ * nothing).  A status already set when the call starts (e.g. a bad expert id
+ * from the layout) means no descriptor is emitted.  After any device error
+ * on a call with a ring, the ring may hold tickets that were reserved but
+ * never written, where a consumer would wait: stop the proxy threads and call
+ * ep_ring_reset before the ring is used again. */
 int ep_dispatch(const ep_shape_t* shape, const void* x, const int32_t* topk_idx,
                 const float* topk_w, const int32_t* rank_offset, const int32_t* send_slot,
                 void* send_buf, int64_t capacity_rows,
@@ -322,7 +327,8 @@ ep_ring_t* ep_ring_create(int32_t depth, int32_t channels, int32_t max_inflight,
 int ep_ring_destroy(ep_ring_t* ring);
 
 /* Host-only, while no kernel uses the ring and no proxy runs: clear slots,
- * tickets and positions. */
+ * tickets and positions.  Required after a dispatch on the ring reported a
+ * device error. */
 int ep_ring_reset(ep_ring_t* ring);
 
 /* Stand-in for one proxy dequeue: pop up to `max` published commands of
@@ -349,7 +355,11 @@ int64_t ep_ring_proxy_drained(const ep_ring_t* ring);
 /* Loopback execution target (UCCL-EP s2.3: the proxy executes each command it
  * pops; s2.2: completions are tracked per command).  Host-only, while no
  * proxy runs.  With src set, proxy threads started afterwards execute what
- * they pop, each on its own stream, in ticket order per channel:
+ * they pop, each on its own stream, in ticket order per channel.  A popped
+ * command's slot goes back to the producers at once (the in-flight limit
+ * counts published, not yet popped commands), but its copy reads the send
+ * buffer later: the caller must not rewrite the send buffer (e.g. by the
+ * next dispatch into it) before ep_ring_wait_complete has returned.
  *   WRITE       copy size_or_value bytes from src + src_offset to
  *               dst[dst_rank] + dst_offset (device to device); consecutive
  *               WRITEs that continue each other become one copy;
@@ -366,6 +376,19 @@ int ep_ring_set_loopback(ep_ring_t* ring, const void* src, uint64_t src_bytes, i
 /* Commands of `channel` completed so far (-1 on bad arguments); a command
  * with ticket t (its seq - 1) is complete once this exceeds t. */
 int64_t ep_ring_completed(const ep_ring_t* ring, int32_t channel);
+
+/* CheckCompletion on the GPU (UCCL-EP s2.2: a command's completion can be
+ * queried without blocking).  Enqueues on `stream` one kernel that, for
+ * i < n, writes done[i] = 1 if the command with ticket tickets[i] (its seq -
+ * 1) on channel channels[i] has completed, 0 if not yet, 2 if the channel is
+ * not one of the ring's.  The proxy threads (or ep_ring_drain) keep each
+ * channel's completed count in host-pinned memory that the kernel reads; a
+ * channel's commands complete in ticket order.  The kernel never waits.
+ *   channels int32 [n], tickets uint64 [n], done uint8 [n]: device memory.
+ * Returns EP_ERR_INVALID_ARG for a NULL ring or n < 0. */
+int ep_ring_check_completion(const ep_ring_t* ring, const int32_t* channels,
+                             const uint64_t* tickets, int32_t n, uint8_t* done,
+                             hipStream_t stream);
 
 /* Block the calling host thread until every command published so far (the
  * producers' ticket counters, read from the device) is completed.  Call it

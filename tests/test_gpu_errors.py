@@ -108,3 +108,89 @@ def test_inconsistent_slots_rejected():
     lg, nd = ring.proxy_stop(1024)
     assert int(b.dev_status.item()) == ep.EP_ERR_INVALID_ARG
     assert all(d["type"] != 1 or d["dst_rank"] == 0 for d in lg)
+
+
+def _streaming_case():
+    # 2048 one-wavefront rows: the large-batch pack, which publishes as
+    # messages complete
+    rng = np.random.default_rng(34)
+    T, H, E, R, k = 2048, 512, 64, 8, 4
+    return (T, H, E, R, k), W.make_random_case(rng, T, H, E, R, k)
+
+
+def _clean_dispatch_on(ring, shape, inp):
+    """A correct dispatch on a ring that was reset: the exact stream again."""
+    import combine_topk_rank_amd as ep
+    import torch
+    from gpu_helpers import assert_descriptors, dev, dev_bf16
+    T, H, E, R, k = shape
+    s = ep.shape(T, H, E, R, k)
+    b = ep.Buffers(s)
+    L = oracle.layout(inp["topk_idx"], E, R)
+    want = oracle.descriptors(L["num_tokens_per_rank"], L["rank_offset"], oracle.row_bytes(H, 0),
+                              ring.channels)
+    ring.proxy_start(2, 1 << 16)
+    d_idx = dev(inp["topk_idx"])
+    b.layout(d_idx)
+    b.dispatch(dev_bf16(inp["x"]), d_idx, dev(inp["topk_w"]), ring=ring)
+    torch.cuda.synchronize()
+    lg, nd = ring.proxy_stop(1 << 16)
+    assert int(b.dev_status.item()) == 0
+    assert nd == len(want)
+    assert_descriptors(lg, want, ring.channels, first_seq=1)
+
+
+def test_streaming_bad_expert_publishes_nothing():
+    """A bad expert id found by the layout: the large-batch pack still packs
+    every row (the bad choice skipped) but emits no command; after a reset
+    the ring carries a correct dispatch."""
+    import combine_topk_rank_amd as ep
+    (T, H, E, R, k), inp = _streaming_case()
+    idx = inp["topk_idx"].copy()
+    idx[5, 0] = E
+    idx[1700, 2] = -3
+    clean = idx.copy()
+    clean[5, 0] = clean[1700, 2] = -1
+    L = oracle.layout(clean, E, R)
+    pk = oracle.pack(inp["x"], clean, inp["topk_w"], L["send_slot"], E, R, 0,
+                     capacity_rows=T * min(k, R))
+    log("[errors] streaming pack after a bad expert id")
+    g = run_hip(T, H, E, R, k, 0, inp["x"], idx, inp["topk_w"],
+                ring_cfg=(1024, 4, 256, 5_000_000_000))
+    assert g["status"] == ep.EP_ERR_BAD_EXPERT
+    assert_layout_equal(g, L)
+    assert_pack_equal(g, pk, L["P"])
+    lg, nd = g["logs"][0]
+    assert nd == 0
+    ring = g["ring"]
+    ring.reset()
+    _clean_dispatch_on(ring, (T, H, E, R, k), inp)
+    ring.destroy()
+
+
+def test_streaming_inconsistent_slots():
+    """send_slot with the rank_offset of another layout on the large-batch
+    pack: reported, no WRITE escapes, and the ring works after a reset."""
+    import combine_topk_rank_amd as ep
+    import torch
+    from gpu_helpers import dev, dev_bf16
+    (T, H, E, R, k), inp = _streaming_case()
+    s = ep.shape(T, H, E, R, k)
+    b = ep.Buffers(s)
+    d_idx, d_w, d_x = dev(inp["topk_idx"]), dev(inp["topk_w"]), dev_bf16(inp["x"])
+    log("[errors] streaming pack, inconsistent rank_offset")
+    b.layout(d_idx)
+    torch.cuda.synchronize()
+    bad_off = torch.zeros_like(b.rank_offset)
+    bad_off[-1] = b.rank_offset[-1]           # every rank starts at 0
+    ring = ep.Ring(1024, 4, 256, 5_000_000_000)
+    ring.proxy_start(2, 1 << 16)
+    ep.ep_dispatch(s, d_x, d_idx, d_w, bad_off, b.send_slot, b.send_buf, b.slot_src,
+                   b.slot_local_idx, b.slot_local_w, ring, b.workspace, b.dev_status)
+    torch.cuda.synchronize()
+    lg, nd = ring.proxy_stop(1 << 16)
+    assert int(b.dev_status.item()) == ep.EP_ERR_INVALID_ARG
+    assert all(int(d["type"]) != 1 for d in lg)
+    ring.reset()
+    _clean_dispatch_on(ring, (T, H, E, R, k), inp)
+    ring.destroy()

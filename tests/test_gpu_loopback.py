@@ -64,7 +64,8 @@ def test_loopback_receive_regions(name, mode):
         b.dispatch(d_x, d_idx, d_w, ring=ring)
         torch.cuda.synchronize()
         assert int(b.dev_status.item()) == 0
-    ring.wait_complete(10_000_000_000)
+        # the copies read the send buffer: it is rewritten only after they end
+        ring.wait_complete(10_000_000_000)
     st = ring.loopback_stats()
     lg, nd = ring.proxy_stop(0)
     log(f"[loopback] {st}")
@@ -107,3 +108,57 @@ def test_loopback_reports_commands_outside_the_regions():
     # the other ranks are still delivered
     for r in range(1, w.R):
         assert np.array_equal(recv[r].cpu().numpy(), want[r])
+
+
+def _query(ring, channels, tickets):
+    """done flags of ep_ring_check_completion for (channel, ticket) pairs."""
+    import torch
+    ch = torch.tensor(channels, dtype=torch.int32, device="cuda")
+    tk = torch.tensor(tickets, dtype=torch.int64, device="cuda")
+    done = torch.full((len(channels),), 9, dtype=torch.uint8, device="cuda")
+    ring.check_completion(ch, tk, done)
+    torch.cuda.synchronize()
+    return done.cpu().numpy()
+
+
+@pytest.mark.parametrize("name,loopback", [("decode", True), ("train", False)])
+def test_check_completion_on_the_gpu(name, loopback):
+    """The GPU's CheckCompletion query: nothing reads complete on a fresh
+    ring; once ep_ring_wait_complete has returned, every published ticket of
+    every channel reads complete and tickets beyond a channel's last read
+    incomplete; a channel outside the ring reads 2."""
+    import combine_topk_rank_amd as ep
+    import torch
+    w = W.WORKLOADS[name]
+    inp = pins.workload_inputs(name)
+    s = ep.shape(w.T, w.H, w.E, w.R, w.k, w.fmt)
+    b = ep.Buffers(s)
+    ring = ep.Ring(w.depth, w.channels, w.max_inflight, 5_000_000_000)
+    C = w.channels
+    assert list(_query(ring, list(range(C)) + [C, -1], [0] * C + [0, 0])) == [0] * C + [2, 2]
+    if loopback:
+        want, counts, rb = _expected(w, inp, "rank")
+        recv = [torch.empty(max(want[r].size, 1), dtype=torch.uint8, device="cuda")
+                for r in range(w.R)]
+        cnt = [torch.zeros(1, dtype=torch.int32, device="cuda") for _ in range(w.R)]
+        ring.set_loopback(b.send_buf, recv, cnt)
+    ring.proxy_start(4, 0)
+    log(f"[completion] {name} loopback={loopback}")
+    d_idx = dev(inp["topk_idx"])
+    b.layout(d_idx)
+    b.dispatch(dev_bf16(inp["x"]), d_idx, dev(inp["topk_w"]), ring=ring)
+    torch.cuda.synchronize()
+    assert int(b.dev_status.item()) == 0
+    ring.wait_complete(10_000_000_000)
+    heads = [ring.completed(c) for c in range(C)]
+    lg, nd = ring.proxy_stop(0)
+    assert sum(heads) == nd > 0
+    chans, tks, exp = [], [], []
+    for c in range(C):
+        for t in range(heads[c]):
+            chans.append(c), tks.append(t), exp.append(1)
+        for t in (heads[c], heads[c] + 1, heads[c] + 1000):
+            chans.append(c), tks.append(t), exp.append(0)
+    got = _query(ring, chans, tks)
+    assert np.array_equal(got, np.array(exp, np.uint8))
+    ring.destroy()

@@ -428,6 +428,44 @@ def flushed_steps(run: Runner, n: int, scratch, sink):
     return [e[0].elapsed_time(e[3]) for e in evs], evs
 
 
+PRE_STEPS = ("none", "gpu_spin", "read64m", "read256m", "read1g", "write1g", "other_set")
+
+
+def pre_step_times(run: Runner, names, reps: int, scratch, sink) -> dict:
+    """Median layout / dispatch / combine times of a step on buffer set 0
+    right after a given other piece of work (what the memory system holds
+    when the step starts): nothing, a 1 ms GPU spin without memory traffic,
+    a read of 64 MB / 256 MB / 1 GiB or a write of 1 GiB of other memory, or
+    a step on buffer set 1."""
+    import numpy as np
+    torch = run.torch
+    acts = {
+        "none": lambda: None,
+        "gpu_spin": lambda: torch.cuda._sleep(2_000_000),
+        "read64m": lambda: sink.add_(scratch[: (64 << 20) // 4].sum()),
+        "read256m": lambda: sink.add_(scratch[: (256 << 20) // 4].sum()),
+        "read1g": lambda: sink.add_(scratch.sum()),
+        "write1g": lambda: scratch.fill_(1),
+        "other_set": lambda: run.step(1),
+    }
+    out = {}
+    for n in names:
+        if n == "other_set" and len(run.sets) < 2:
+            continue
+        evs = [new_events(4) for _ in range(reps)]
+        for r in range(reps):
+            acts[n]()
+            run.step(0, evs[r])
+        torch.cuda.synchronize()
+        d = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])]
+                      for e in evs]) * 1e3
+        med = np.median(d, axis=0)
+        out[n] = {"layout": round(float(med[0]), 1), "dispatch": round(float(med[1]), 1),
+                  "combine": round(float(med[2]), 1)}
+        eprint(f"bench: {run.w.name} after {n}: layout/dispatch/combine us {out[n]}")
+    return out
+
+
 def dominant(run: Runner, ops: dict):
     """The longer of the pack (inside dispatch) and the combine kernel."""
     ab = run.ab
@@ -534,6 +572,13 @@ def bench_workload(w, args, scratch, sink, dev) -> dict:
         if evs_w:
             entry["warm"]["per_op_us"] = per_op(evs_w, run.fused, ll, K)
 
+    if args.pre_steps and run.graphs is None:
+        entry["pre_steps"] = dict(
+            pre_step_times(run, [n for n in args.pre_steps.split(",") if n], args.pre_reps,
+                           scratch, sink),
+            note="median per-op us (HIP events) of a step on one buffer set right after the "
+                 "named work")
+
     st = run.status()
     if st:
         raise RuntimeError(f"{w.name}: device status after the timed steps: "
@@ -609,6 +654,10 @@ def main() -> int:
                     help="steps each after a 1 GiB read (0: skip)")
     ap.add_argument("--no-warm", dest="warm", action="store_false",
                     help="skip the warm back-to-back phase")
+    ap.add_argument("--pre-steps", default="",
+                    help="comma-separated work to run right before each of --pre-reps steps, "
+                         "timed per op: " + ",".join(PRE_STEPS) + " (empty: skip)")
+    ap.add_argument("--pre-reps", type=int, default=12)
     ap.add_argument("--loopback", action="store_true",
                     help="proxy threads execute every command against per-rank receive regions "
                          "and count words (one buffer set); the timed region then ends when "
@@ -650,10 +699,15 @@ def main() -> int:
         if n not in W.WORKLOADS:
             print(f"unknown workload {n}; known: {', '.join(W.WORKLOADS)}", file=sys.stderr)
             return 2
+    for n in [n for n in args.pre_steps.split(",") if n]:
+        if n not in PRE_STEPS:
+            print(f"unknown pre-step {n}; known: {', '.join(PRE_STEPS)}", file=sys.stderr)
+            return 2
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
     ceil = ceilings(dev) if args.ceilings else None
-    scratch = torch.ones((1 << 30) // 4, dtype=torch.int32, device=dev) if args.flush_reps else None
+    need_scratch = args.flush_reps > 0 or bool(args.pre_steps)
+    scratch = torch.ones((1 << 30) // 4, dtype=torch.int32, device=dev) if need_scratch else None
     sink = torch.zeros((), dtype=torch.int64, device=dev)
 
     entries = {}

@@ -46,7 +46,7 @@ def _check_case(T, H, E, R, k, fmt, inp, C, depth, mif, cap_extra=3, repeat=1, y
     return g
 
 
-@pytest.mark.parametrize("name", ["tiny", "decode", "train", "fp8"])
+@pytest.mark.parametrize("name", ["tiny", "decode", "train", "fp8", "skewed"])
 def test_ll_workload_parity(name):
     w = W.WORKLOADS[name]
     inp = pins.workload_inputs(name)

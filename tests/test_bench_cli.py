@@ -48,3 +48,32 @@ def test_row_pitch_is_whole_lines_for_fp8():
     import bench
     assert bench.row_pitch(7168, 1) == 7424 and bench.row_bytes(7168, 1) == 7392
     assert bench.row_pitch(7168, 0) == bench.row_bytes(7168, 0) == 14336
+
+
+def test_rotation_sets_and_quantiles():
+    import bench
+    mall = bench.MALL_BYTES
+    # enough sets that a set's data was last touched >= 2x the MALL of traffic ago
+    for step_bytes in (800_000, 30_000_000, 976_000_000, 3_200_000_000):
+        n = bench.rotation_sets(step_bytes)
+        assert 2 <= n <= 16
+        assert n == 16 or (n - 1) * step_bytes >= 2 * mall
+    q = bench.quantiles(list(range(1, 101)))
+    assert q["p10"] < q["p50"] < q["p90"] and abs(q["p50"] - 50.5) < 1e-9
+
+
+def test_cpu_threads_follow_omp_num_threads(monkeypatch):
+    import bench
+    info = {"nproc": 16, "cpu_count": 64, "model": "x"}
+    monkeypatch.setenv("OMP_NUM_THREADS", "4")
+    assert bench.cpu_threads_all(info) == 4
+    monkeypatch.setenv("OMP_NUM_THREADS", "64")
+    assert bench.cpu_threads_all(info) == 16
+    monkeypatch.delenv("OMP_NUM_THREADS")
+    assert bench.cpu_threads_all(info) == 16
+
+
+def test_unknown_pre_step_rejected_before_the_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--pre-steps", "bogus"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "unknown pre-step" in r.stderr

@@ -239,9 +239,15 @@ class Runner:
         if self.ll:
             self.fused = args.fused == "on" or (args.fused == "auto" and w.T <= 256 and w.E <= 1024)
         else:
-            self.fused = args.fused == "on" or (args.fused == "auto" and w.T <= 256)
+            # the one call when it is one kernel (small batches; large bf16
+            # batches, through a grid barrier), else the two calls, whose
+            # per-op events then time the layout on its own
+            self.fused = args.fused == "on" or (
+                args.fused == "auto" and ep.ep_dispatch_fused_plan(
+                    ep.shape(w.T, w.H, w.E, w.R, w.k, w.fmt)) != ep.EP_FUSED_TWO_CALLS)
         s = ep.shape(w.T, w.H, w.E, w.R, w.k, w.fmt)
         self.shape = s
+        self.plan = ep.ep_dispatch_fused_plan(s) if (self.fused and not self.ll) else None
         self.stream = torch.cuda.current_stream()
         x0 = torch.from_numpy(inp["x"].view(np.int16)).to(dev).view(torch.bfloat16)
         i0 = torch.from_numpy(inp["topk_idx"]).to(dev)
@@ -479,10 +485,13 @@ def dominant(run: Runner, ops: dict):
             name, prefix = "ll_fused_small_kernel (ep_dispatch_ll_fused)", "ll_fused_small_kernel"
         elif run.ll:
             name, prefix = "ll_pack_kernel (ep_dispatch_ll)", "ll_pack_kernel"
-        elif run.fused:
+        elif run.fused and run.plan == run.ep.EP_FUSED_ONE_KERNEL_SMALL:
             name, prefix = "fused_small_kernel (ep_dispatch_fused)", "fused_small_kernel"
+        elif run.fused and run.plan == run.ep.EP_FUSED_ONE_KERNEL_LARGE:
+            name, prefix = "fused_large_kernel (ep_dispatch_fused)", "fused_large_kernel"
         else:
             name, prefix = "pack_kernel (ep_dispatch)", "pack_kernel"
+        # the one call's layout and pack are one kernel (or two back to back)
         return name, prefix, ops["dispatch"], ab["dispatch"] + (ab["layout"] if run.fused else 0)
     name = "combine_kernel (ep_combine_ll)" if run.ll else "combine_kernel (ep_combine)"
     return name, "combine_kernel", ops["combine"], ab["combine"]
@@ -521,6 +530,10 @@ def bench_workload(w, args, scratch, sink, dev) -> dict:
              ("rows_Q" if ll else "pairs_P"): P, "bytes_per_step": ab["total"],
              "algorithmic_bytes_per_step": ab, "buffer_sets": nsets,
              "fused_layout_dispatch": run.fused, "graph": run.graphs is not None}
+    if run.plan is not None:
+        entry["fused_plan"] = {run.ep.EP_FUSED_ONE_KERNEL_SMALL: "one kernel (small batch)",
+                               run.ep.EP_FUSED_ONE_KERNEL_LARGE: "one kernel (grid barrier)",
+                               run.ep.EP_FUSED_TWO_CALLS: "layout call, then dispatch call"}[run.plan]
 
     # cold (headline): K rotating steps by wall clock
     el, evs, cmds = timed_steps(run, K, args.warmup, rotate=nsets > 1, every=every)
@@ -605,12 +618,13 @@ def bench_workload(w, args, scratch, sink, dev) -> dict:
 
 def ceilings(dev) -> dict:
     """Read, write and copy rates of torch's own kernels over 1 GiB on this
-    GPU: practical reference points next to the 8 TB/s peak."""
+    GPU: practical reference points next to the 8 TB/s peak.  The read rate
+    is the best of a few whole-tensor reductions (torch has no plain read)."""
     import torch
     n = 1 << 30
     a = torch.ones(n // 4, dtype=torch.int32, device=dev)
     b = torch.empty_like(a)
-    sink = torch.zeros((), dtype=torch.int64, device=dev)
+    sink = torch.zeros((), dtype=torch.float32, device=dev)
     s = torch.cuda.current_stream()
 
     def rate(fn, nbytes, reps=5):
@@ -623,14 +637,20 @@ def ceilings(dev) -> dict:
         torch.cuda.synchronize()
         return round(reps * nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
 
-    def rd():
-        sink.add_(a.sum())
-
-    out = {"read_GBps": rate(rd, n), "write_GBps": rate(lambda: b.fill_(3), n),
+    f = a.view(torch.float32)
+    m = a.view(torch.bfloat16).view(-1, 8192)
+    v = torch.ones(8192, dtype=torch.bfloat16, device=dev)
+    reads = {"sum of int32": lambda: sink.add_(a.sum()),
+             "amax of float32": lambda: sink.add_(f.amax()),
+             "bf16 matrix-vector product": lambda: sink.add_(torch.mv(m, v)[0].float())}
+    rr = {k: rate(fn, n) for k, fn in reads.items()}
+    best = max(rr, key=rr.get)
+    out = {"read_GBps": rr[best], "read_kernel": best, "reads_GBps": rr,
+           "write_GBps": rate(lambda: b.fill_(3), n),
            "copy_GBps": rate(lambda: b.copy_(a), 2 * n),
-           "note": "torch kernels over 1 GiB (sum for read, fill for write, copy counts read + "
-                   "write bytes)"}
-    del a, b
+           "note": "torch kernels over 1 GiB (read: the best of the reductions listed; fill for "
+                   "write; copy counts read + write bytes)"}
+    del a, b, f, m
     torch.cuda.empty_cache()
     return out
 
@@ -647,9 +667,10 @@ def main() -> int:
                     help="rank: one row per (token, rank) pair; ll: the per-expert "
                          "(low-latency) mode, one row per kept choice")
     ap.add_argument("--fused", choices=("auto", "on", "off"), default="auto",
-                    help="layout + dispatch in one call (ep_dispatch_fused, one kernel for "
-                         "T <= 256; per-expert mode: ep_dispatch_ll_fused, T <= 256 and "
-                         "E <= 1024); auto: for batches of at most 256 tokens")
+                    help="layout + dispatch in one call (ep_dispatch_fused: one kernel for "
+                         "T <= 256 and for large bf16 batches whose rows take one wavefront; "
+                         "per-expert mode: ep_dispatch_ll_fused, T <= 256 and E <= 1024); "
+                         "auto: where the call is one kernel")
     ap.add_argument("--cold-sets", type=int, default=0,
                     help="buffer sets the cold steps rotate over (0: enough to exceed twice the "
                          "MALL; 1: no rotation)")

@@ -16,6 +16,7 @@ The functions keep the C names:
     ep_dispatch(shape, x, topk_idx, topk_w, rank_offset, send_slot, send_buf,
                 slot_src, slot_local_idx, slot_local_w, ring, workspace,
                 dev_status, stream=None)
+    ep_dispatch_fused_plan(shape, with_ring=True) -> int
     ep_dispatch_fused_noalloc(shape, x, topk_idx, topk_w, <layout outputs>, send_buf,
                               slot_src, slot_local_idx, slot_local_w, ring, dev_status,
                               stream=None, clear_scratch=False)
@@ -46,6 +47,9 @@ EP_ERR_RING_TIMEOUT = 4
 EP_ERR_HIP = 5
 EP_ERR_BUSY = 6
 EP_ERR_TIMEOUT = 7
+EP_FUSED_ONE_KERNEL_SMALL = 101
+EP_FUSED_ONE_KERNEL_LARGE = 102
+EP_FUSED_TWO_CALLS = 103
 EP_FMT_BF16 = 0
 EP_FMT_FP8_E4M3_B128 = 1
 EP_CMD_WRITE = 1
@@ -97,6 +101,8 @@ def _load() -> ctypes.CDLL:
     L.ep_dispatch_fused.argtypes = [S, P, P, P, P, P, P, P, P, P, P, i64, P, P, P, P, P, sz, P,
                                     P]
     L.ep_dispatch_fused.restype = ctypes.c_int
+    L.ep_dispatch_fused_plan.argtypes = [S, i32]
+    L.ep_dispatch_fused_plan.restype = ctypes.c_int
     L.ep_dispatch_fused_noalloc.argtypes = [S, P, P, P, P, P, P, P, P, P, P, i64, P, P, P, P,
                                             i32, P, P]
     L.ep_dispatch_fused_noalloc.restype = ctypes.c_int
@@ -222,6 +228,15 @@ def ep_dispatch_fused(s, x, topk_idx, topk_w, num_tokens_per_rank, num_tokens_pe
                                workspace.numel() * workspace.element_size(), _ptr(dev_status),
                                _stream(stream))
     _check(st, "ep_dispatch_fused")
+
+
+def ep_dispatch_fused_plan(s, with_ring: bool = True) -> int:
+    """EP_FUSED_ONE_KERNEL_SMALL, EP_FUSED_ONE_KERNEL_LARGE or
+    EP_FUSED_TWO_CALLS: the path ep_dispatch_fused takes for shape s."""
+    st = lib.ep_dispatch_fused_plan(ctypes.byref(s), 1 if with_ring else 0)
+    if st not in (EP_FUSED_ONE_KERNEL_SMALL, EP_FUSED_ONE_KERNEL_LARGE, EP_FUSED_TWO_CALLS):
+        _check(st, "ep_dispatch_fused_plan")
+    return st
 
 
 def ep_dispatch_fused_noalloc(s, x, topk_idx, topk_w, num_tokens_per_rank,

@@ -44,9 +44,10 @@ inline size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 size_t workspace_bytes(const ep_shape_t& s) {
     const int64_t nb = layout_blocks(s.T);
-    size_t b = kWsHeader;                      // barrier words, channel ticket bases
+    size_t b = kWsHeader;                      // barrier words, arrival counters
     b += align256((size_t)nb * s.R * 4);       // blk_rank_cnt
     b += align256((size_t)nb * s.E * 4);       // blk_exp_cnt
+    b += align256((size_t)wave_blocks(s.T) * s.R * 4);   // wave_rank_cnt
     b += align256((size_t)(s.R + 1) * 4);      // msg_base
     b += align256((size_t)(max_messages(s) + s.R) * 4);   // msg_arrivals + rank_msgs_done
     return b;
@@ -58,12 +59,14 @@ Workspace carve_workspace(const ep_shape_t& s, void* base) {
     const int64_t nb = layout_blocks(s.T);
     w.layout_blocks = (int32_t)nb;
     w.barrier = reinterpret_cast<uint32_t*>(p);
-    w.arrive = reinterpret_cast<uint32_t*>(p + 256);
+    w.arrive = reinterpret_cast<uint32_t*>(p + kBarrierBytes);
     p += kWsHeader;
     w.blk_rank_cnt = reinterpret_cast<int32_t*>(p);
     p += align256((size_t)nb * s.R * 4);
     w.blk_exp_cnt = reinterpret_cast<int32_t*>(p);
     p += align256((size_t)nb * s.E * 4);
+    w.wave_rank_cnt = reinterpret_cast<int32_t*>(p);
+    p += align256((size_t)wave_blocks(s.T) * s.R * 4);
     w.msg_base = reinterpret_cast<int32_t*>(p);
     p += align256((size_t)(s.R + 1) * 4);
     w.max_msgs = max_messages(s);

@@ -48,17 +48,25 @@ __device__ inline bool ring_check_completion(const RingDev& g, int c, unsigned l
 }
 
 // Carved workspace.
-// Workspace header: grid barrier words (256 B), then arrival counters, one
-// per 128-byte line (a top counter and 8 group counters).
+// Workspace header: grid barrier words, one per 128-byte line (the top
+// arrival count, kBarGroups group counts, the generation), then the
+// dispatch's arrival counters, also one per line (a top counter and 8 group
+// counters).
 constexpr size_t kArriveStride = 32;   // words
-constexpr size_t kWsHeader = 256 + 16 * kArriveStride * 4;
-static_assert(kWsHeader % 256 == 0, "workspace sections stay 256-byte aligned");
+constexpr int kBarGroups = 8;
+constexpr size_t kBarGen = (1 + kBarGroups) * kArriveStride;   // word of the generation
+constexpr size_t kBarrierBytes = 10 * kArriveStride * 4;
+constexpr size_t kWsHeader = kBarrierBytes + 16 * kArriveStride * 4;
+static_assert((kBarGen + 1) * 4 <= kBarrierBytes, "barrier words fit their section");
+static_assert(kBarrierBytes % 256 == 0 && kWsHeader % 256 == 0,
+              "workspace sections stay 256-byte aligned");
 
 struct Workspace {
-    uint32_t* barrier;        // [2] grid barrier: arrivals, generation (zero at first use)
+    uint32_t* barrier;        // grid barrier words (zero at first use)
     uint32_t* arrive;         // [9 lines] dispatch arrival counters (zero between calls)
     int32_t* blk_rank_cnt;    // [NB, R] per-layout-block rank counts
     int32_t* blk_exp_cnt;     // [NB, E] per-layout-block expert counts
+    int32_t* wave_rank_cnt;   // [ceil(T/64), R] per-64-token rank counts (one-kernel dispatch)
     int32_t* msg_base;        // [R+1]   first message index of each rank
     int32_t* msg_arrivals;    // [max_msgs] rows (x chunks) written per message
     int32_t* rank_msgs_done;  // [R]     messages of a rank published
@@ -72,6 +80,8 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int32_t layout_blocks(int32_t T) {
     return (int32_t)(T <= 0 ? 1 : ceil_div(T, kLayoutTile));
 }
+
+inline int64_t wave_blocks(int32_t T) { return T <= 0 ? 1 : ceil_div(T, kWave); }
 
 inline int64_t max_messages(const ep_shape_t& s) {
     int64_t kr = s.k < s.R ? s.k : s.R;
@@ -150,19 +160,22 @@ constexpr int kStoreSystem = kCacheSc0 | kCacheSc1;
 // covers another wavefront's stores only if that wavefront waited first.
 __device__ inline void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// Grid-wide barrier for a grid whose workgroups are all resident: bar[0]
-// counts arrivals, bar[1] is a generation number.  Each workgroup reads the
-// generation before it arrives (thread 0 passes what it loaded with
-// grid_barrier_generation, as early as it likes: the generation cannot move
-// before this workgroup arrives); the last arrival resets the count and
-// bumps the generation, which releases the others.  The words stay consistent from
-// one call to the next for any grid size (they start at zero).  The wait is
-// bounded by about a second of wall clock; on timeout the status is set and
-// false is returned.  Stores made before the barrier by any workgroup are
-// visible to loads made after it by every workgroup; with SYSTEM they are
-// also released at system scope (visible to other agents, e.g. a CPU or NIC).
+// Grid-wide barrier for a grid whose workgroups are all resident.  Arrivals
+// are counted in two levels so that no single word takes every atomic:
+// workgroup b counts into group counter b % kBarGroups, the last of a group
+// into the top counter, and the last of all bumps the generation, which
+// releases the others.  Each workgroup reads the generation before it
+// arrives (thread 0 passes what it loaded with grid_barrier_generation, as
+// early as it likes: the generation cannot move before this workgroup
+// arrives).  Every counter is reset by the arrival that completes it, so the
+// words stay consistent from one call to the next for any grid size (they
+// start at zero).  The wait is bounded by about a second of wall clock; on
+// timeout the status is set and false is returned.  Stores made before the
+// barrier by any workgroup are visible to loads made after it by every
+// workgroup; with SYSTEM they are also released at system scope (visible to
+// other agents, e.g. a CPU or NIC).
 __device__ inline uint32_t grid_barrier_generation(const uint32_t* bar) {
-    return __hip_atomic_load(&bar[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __hip_atomic_load(&bar[kBarGen], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <bool SYSTEM>
@@ -176,13 +189,28 @@ __device__ bool grid_barrier(uint32_t* bar, uint32_t nblocks, int32_t* st, uint3
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "");
         else
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        const uint32_t old = atomicAdd(&bar[0], 1u);
-        if (old == nblocks - 1) {
-            atomicExch(&bar[0], 0u);
-            __hip_atomic_store(&bar[1], gen + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t g = blockIdx.x % kBarGroups;
+        const uint32_t ng = nblocks < (uint32_t)kBarGroups ? nblocks : (uint32_t)kBarGroups;
+        const uint32_t in_g = (nblocks - g + kBarGroups - 1) / kBarGroups;
+        uint32_t* cg = bar + (size_t)(1 + g) * kArriveStride;
+        bool last = false;
+        if (__hip_atomic_fetch_add(cg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == in_g - 1) {
+            __hip_atomic_store(cg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            // what the group's workgroups released goes on with the top arrival
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");
+            if (__hip_atomic_fetch_add(&bar[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                ng - 1) {
+                __hip_atomic_store(&bar[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");
+                last = true;
+            }
+        }
+        if (last) {
+            __hip_atomic_store(&bar[kBarGen], gen + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
         } else {
             const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
-            while (__hip_atomic_load(&bar[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gen) {
+            while (__hip_atomic_load(&bar[kBarGen], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                   gen) {
                 if (__builtin_amdgcn_s_memrealtime() - t0 > kBarrierTimeoutTicks) {
                     set_error(st, EP_ERR_TIMEOUT);
                     ok = 0;

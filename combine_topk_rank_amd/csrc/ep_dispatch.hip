@@ -79,6 +79,10 @@ struct PackArgs {
     int32_t* send_slot_out;       // [T, R]
     int32_t* msg_base_out;        // [R+1] (workspace)
     int64_t counters_n;           // msg_arrivals .. rank_msgs_done
+    // one-kernel large batches
+    uint32_t* bar;                // grid barrier words (workspace)
+    int32_t* wave_cnt;            // [ceil(T/64), R] per-64-token rank counts (workspace)
+    int32_t npass;                // groups per pack workgroup, at most
 };
 
 // ------------------------------------------------------------------ ring
@@ -213,21 +217,6 @@ __device__ inline void ring_publish(const RingDev& g, bool have, int c, unsigned
     ring_publish_n<1, SYS>(g, have ? 1 : 0, c, &ticket, &cmd, st);
 }
 
-// ATOMIC{ADD, cnt} for ranks that receive no rows (nothing to order after).
-__device__ void publish_empty_ranks(const PackArgs& a) {
-    const int lane = lane_id();
-    bool have = false;
-    int c = 0;
-    unsigned long long tk = 0;
-    if (lane < a.R && a.rank_off[lane + 1] == a.rank_off[lane]) {
-        have = true;
-        c = lane % a.ring.channels;
-        tk = ring_reserve(a.ring, c, 1);
-    }
-    ring_publish<true>(a.ring, have, c, tk, EP_CMD_ATOMIC, EP_ATOMIC_ADD, 0, (uint32_t)lane, 0, 0,
-                       0, a.st);
-}
-
 // Wavefront 0 of a workgroup, after the rows of its current group (kWaves
 // consecutive wavefronts, hence consecutive tokens) are released: lane r
 // takes rank r.  slot[w][r] is the slot of rank r written by wavefront w of
@@ -255,6 +244,21 @@ __device__ inline void load_rank_view(const PackArgs& a, RankView& v) {
         v.cnt[lane] = a.rank_off[lane + 1] - o;
         v.mbase[lane] = a.msg_base[lane];
     }
+}
+
+// ATOMIC{ADD, cnt} for ranks that receive no rows (nothing to order after).
+__device__ void publish_empty_ranks(const PackArgs& a, const RankView& rv) {
+    const int lane = lane_id();
+    bool have = false;
+    int c = 0;
+    unsigned long long tk = 0;
+    if (lane < a.R && rv.cnt[lane] == 0) {
+        have = true;
+        c = lane % a.ring.channels;
+        tk = ring_reserve(a.ring, c, 1);
+    }
+    ring_publish<true>(a.ring, have, c, tk, EP_CMD_ATOMIC, EP_ATOMIC_ADD, 0, (uint32_t)lane, 0, 0,
+                       0, a.st);
 }
 
 template <int W>
@@ -793,9 +797,9 @@ __global__ __launch_bounds__(WAVES * kWave) void pack_kernel(PackArgs a) {
     const bool streaming = PUB == kPubStream && cap_ok;
     bool pub_ok = false;   // wavefront 0 only
     if (streaming && wave == 0) pub_ok = bcast(read_status(a.st), 0) == 0;
-    if (pub_ok && blockIdx.x == 0) publish_empty_ranks(a);
     __shared__ RankView rv;   // read by wavefront 0 only, which wrote it
     if (streaming && wave == 0) load_rank_view(a, rv);
+    if (pub_ok && blockIdx.x == 0) publish_empty_ranks(a, rv);
     // groups of kWaves wavefronts, taken in launch order; a workgroup that
     // finishes a group (rows, then descriptors) moves on to the next one
     int pass = 0;
@@ -999,6 +1003,252 @@ __global__ __launch_bounds__(kPackWavesSmall* kWave) void fused_small_kernel(Pac
     if (wave == 0) closed_reserve(a, z, s_base, s_cstart, s_cnum);
     __syncthreads();
     closed_publish_all<kWaves * kWave>(a, z, s_base, s_cstart, s_cnum);
+}
+
+// ------------------------------------------------- one-kernel large batches
+// Routing layout and pack of a large batch in one launch, for chunkings with
+// one wavefront per token.  The pack's work order is kept (workgroup b takes
+// groups b, b + G, ... of kWaves consecutive tokens, so messages complete all
+// through the copy and publication overlaps it); only the layout moves into
+// the kernel, split so that no workgroup does more than a few ballots:
+//   1. for each of its groups, the workgroup takes the 64-token block the
+//      group lies in and computes its per-rank ballots (one wavefront per
+//      block); the block's first group also stores the block's rank counts
+//      to a [ceil(T/64), R] table;
+//   2. grid barrier (the G pack workgroups are resident at once);
+//   3. every workgroup sums the table: the rank totals (hence the offsets,
+//      identical everywhere) and, per group, the rows of each rank in the
+//      blocks before the group's block; a token's slot is then
+//        o_r + (rows of r in earlier blocks) + popcount(ballot_r below it);
+//   4. the pack of the two-kernel path, reading slots from LDS; each token's
+//      first wavefront also writes its send_slot and is_token_in_rank rows.
+// Each wavefront loads its row chunk of pass 0 before the barrier, so the
+// copy's first reads overlap the layout.
+// One workgroup more than the pack's computes the per-expert counts and
+// their scan from topk_idx meanwhile; it takes no part in the barrier.  The
+// slots are those of the layout kernel: integer counts and prefix sums, no
+// atomic decides an order.
+constexpr int kFusedLargeMaxPasses = 16;
+
+// Per-expert counts of all T * k choices and their exclusive scan (one
+// workgroup of NT >= kBlock threads).
+template <int NT>
+__device__ void expert_counts(const PackArgs& a, int32_t* s_hist, int32_t* s_part) {
+    const int tid = threadIdx.x;
+    for (int e = tid; e < a.E; e += NT) s_hist[e] = 0;
+    __syncthreads();
+    const int64_t n = (int64_t)a.T * a.k;
+    constexpr int kBatch = 8;
+    for (int64_t i0 = tid; i0 < n; i0 += (int64_t)NT * kBatch) {
+        int32_t v[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int64_t i = i0 + (int64_t)u * NT;
+            v[u] = i < n ? a.idx[i] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+            if (v[u] >= 0 && v[u] < a.E) atomicAdd(&s_hist[v[u]], 1);
+    }
+    __syncthreads();
+    for (int e = tid; e < a.E; e += NT) a.cnt_exp_out[e] = s_hist[e];
+    block_exclusive_scan_store(s_hist, a.E, a.exp_off_out, s_part);
+}
+
+// The rows of one pass of the one-kernel large batch: this wavefront's
+// token of group b + p*G (its row chunk in *v when already loaded), its
+// slots from the block's ballots, its rows and metadata.  Returns the slot
+// of rank `lane` (or -1).
+template <int VPL, int FMT, int WAVES>
+__device__ __forceinline__ int32_t fused_rows(const PackArgs& a, int p, int64_t b, int64_t G,
+                                              const uint64_t (*s_ball)[kMaxR],
+                                              const int32_t (*s_base)[kMaxR],
+                                              const u32x4 (*v)[VPL]) {
+    const int lane = lane_id(), wave = (int)(threadIdx.x / kWave), R = a.R;
+    const int64_t t = (b + (int64_t)p * G) * WAVES + wave;
+    int32_t s_lane = -1;
+    if (t < a.T) {   // wavefront-uniform
+        if (lane < R) {
+            const uint64_t bb = s_ball[p][lane];
+            const int tl = (int)(t % kWave);
+            const bool in = (bb >> tl) & 1ull;
+            if (in) s_lane = s_base[p][lane] + (int32_t)__popcll(bb & ((1ull << tl) - 1ull));
+            a.send_slot_out[t * R + lane] = s_lane;
+            a.in_rank_out[t * R + lane] = (uint8_t)in;
+        }
+        const uint64_t dmask = __ballot(s_lane >= 0);
+        if (v)
+            store_row_chunk_v<VPL, FMT>(a, 0, s_lane, dmask, *v);
+        else
+            store_row_chunk<VPL, FMT>(a, t, 0, s_lane, dmask);
+        store_slot_metadata(a, t, s_lane, dmask);
+    }
+    return s_lane;
+}
+
+// Four wavefronts per SIMD (at most 128 registers a lane), so that the pack
+// workgroups and the expert one are resident at once.
+template <int VPL, int FMT, int WAVES, int PUB>
+__global__ __launch_bounds__(WAVES * kWave, 4) void fused_large_kernel(PackArgs a) {
+    constexpr int kWaves = WAVES;
+    constexpr int kT = WAVES * kWave;
+    constexpr int kPass = kFusedLargeMaxPasses;
+    static_assert(kWave % kWaves == 0, "a group lies inside one 64-token block");
+    static_assert(kT >= kBlock, "the expert scan takes at least kBlock threads");
+    __shared__ uint64_t s_ball[kPass][kMaxR];   // pass p: ballots of its group's block
+    __shared__ int32_t s_base[kPass][kMaxR];    // pass p: slot of the block's first row of r
+    __shared__ int32_t s_tot[kMaxR];            // rows of rank r
+    __shared__ int32_t s_slot[2][kWaves][kMaxR];
+    __shared__ RankView rv;
+    __shared__ int32_t s_hist[kMaxE];           // the expert workgroup
+    __shared__ int32_t s_part[kT];
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+    const int R = a.R;
+    const int64_t G = (int64_t)gridDim.x - 1;   // pack workgroups
+    const int64_t b = blockIdx.x;
+    if (b == G) {
+        expert_counts<kT>(a, s_hist, s_part);
+        return;
+    }
+    // 1. ballots of each pass's block (wavefront p % kWaves takes pass p).
+    // The ids of a wavefront's first ballot block are loaded first, then its
+    // row chunk of pass 0, which stays in registers through the layout: its
+    // latency overlaps the ballots and the barrier instead of following them.
+    int32_t ids[kMaxK];
+    if (wave < a.npass && b + (int64_t)wave * G < a.ngroups)
+        load_token_ids(a.idx, (b + (int64_t)wave * G) * kWaves / kWave * kWave + lane, a.T, a.k,
+                       ids);
+    u32x4 v0[VPL];
+    const int64_t t0 = b * kWaves + wave;   // this wavefront's token in pass 0
+    if (t0 < a.T) load_row_chunk<VPL>(a, t0, 0, v0);
+    // the barrier's generation, loaded after the ids so that they do not
+    // wait behind it
+    uint32_t gen = 0;
+    if (tid == 0) gen = grid_barrier_generation(a.bar);
+    for (int p = wave; p < a.npass; p += kWaves) {
+        const int64_t g = b + (int64_t)p * G;
+        uint64_t mine = 0;
+        if (g < a.ngroups) {
+            const int64_t blk = g * kWaves / kWave;
+            if (p != wave) load_token_ids(a.idx, blk * kWave + lane, a.T, a.k, ids);
+            const uint64_t mask = rank_mask_of(ids, a.E, a.k, a.epr, a.st, nullptr);
+            for (int r = 0; r < R; ++r) {
+                const uint64_t bb = __ballot((mask >> r) & 1ull);
+                if (lane == r) mine = bb;
+            }
+            if ((g * kWaves) % kWave == 0 && lane < R)
+                a.wave_cnt[blk * R + lane] = (int32_t)__popcll(mine);
+        }
+        if (lane < R) s_ball[p][lane] = mine;
+    }
+    for (int p = tid; p < kPass * kMaxR; p += kT) (&s_base[0][0])[p] = 0;
+    if (tid < kMaxR) s_tot[tid] = 0;
+    // the streaming pack's message counters start at zero
+    for (int64_t i = b * kT + tid; i < a.counters_n; i += G * kT) a.msg_arrivals[i] = 0;
+
+    // 2. every block's counts are in the table after this
+    if (!grid_barrier<false>(a.bar, (uint32_t)G, a.st, gen)) return;
+
+    // 3. rank totals and, per pass, the rows in earlier blocks.  Thread
+    // (seg, r) walks rows [lo, hi) of column r in order; pass p, whose group
+    // lies in block f_p (ascending in p), takes the rows of the range below
+    // f_p: the running sum when the walk reaches f_p, the whole range when
+    // f_p >= hi.
+    {
+        const int nseg = kT / R;
+        const int r = tid % R, seg = tid / R;
+        const int32_t nblk = (a.T + kWave - 1) / kWave;
+        const int32_t len = (nblk + nseg - 1) / nseg;
+        const int32_t lo = seg * len, hi = min(lo + len, nblk);
+        auto first_blk = [&](int p) {
+            return (int32_t)((b + (int64_t)p * G) * kWaves / kWave);
+        };
+        if (seg < nseg) {
+            int32_t run = 0;
+            int p = 0;
+            while (p < a.npass && first_blk(p) <= lo) ++p;   // nothing of this range
+            constexpr int kBatch = 8;
+            for (int32_t k0 = lo; k0 < hi; k0 += kBatch) {
+                int32_t v[kBatch];
+#pragma unroll
+                for (int u = 0; u < kBatch; ++u)
+                    v[u] = k0 + u < hi ? a.wave_cnt[(int64_t)(k0 + u) * R + r] : 0;
+#pragma unroll
+                for (int u = 0; u < kBatch; ++u) {
+                    while (p < a.npass && first_blk(p) <= k0 + u) {
+                        if (run) atomicAdd(&s_base[p][r], run);
+                        ++p;
+                    }
+                    run += v[u];
+                }
+            }
+            for (; p < a.npass; ++p)
+                if (run) atomicAdd(&s_base[p][r], run);
+            atomicAdd(&s_tot[r], run);
+        }
+    }
+    __syncthreads();
+    if (wave == 0) {
+        // offsets and message bases (exclusive scans across lanes, R <= 64)
+        const int32_t tot = lane < R ? s_tot[lane] : 0;
+        const int32_t msgs = (tot + kMsgRows - 1) / kMsgRows;
+        int32_t incl = tot, mincl = msgs;
+        for (int d = 1; d < kWave; d <<= 1) {
+            const int32_t o = __shfl_up(incl, d);
+            const int32_t mo = __shfl_up(mincl, d);
+            if (lane >= d) {
+                incl += o;
+                mincl += mo;
+            }
+        }
+        const int32_t off = incl - tot;
+        if (lane < R) {
+            rv.o[lane] = off;
+            rv.cnt[lane] = tot;
+            rv.mbase[lane] = mincl - msgs;
+            for (int p = 0; p < a.npass; ++p) s_base[p][lane] += off;
+        }
+        if (b == 0) {
+            if (lane < R) {
+                a.cnt_rank_out[lane] = tot;
+                a.rank_off_out[lane] = off;
+                a.msg_base_out[lane] = mincl - msgs;
+            }
+            if (lane == R - 1) {
+                a.rank_off_out[R] = incl;
+                a.msg_base_out[R] = mincl;
+            }
+        }
+        if (lane == R - 1) s_tot[0] = incl;   // P, read after the barrier below
+    }
+    __syncthreads();
+
+    // 4. the pack
+    const int64_t P = s_tot[0];
+    const bool cap_ok = P <= a.cap;
+    if (b == 0 && wave == 0) {
+        if (!cap_ok && lane == 0) set_error(a.st, EP_ERR_CAPACITY);
+        if (PUB != kPubNone) refresh_tail_cache(a);
+    }
+    // as in the two-kernel pack: no command goes out once an error (e.g. a
+    // bad expert id found in step 1) has been reported
+    const bool streaming = PUB == kPubStream && cap_ok;
+    bool pub_ok = false;   // wavefront 0 only
+    if (streaming && wave == 0) pub_ok = bcast(read_status(a.st), 0) == 0;
+    if (pub_ok && b == 0) publish_empty_ranks(a, rv);
+    // pass 0's rows come from the registers loaded before the barrier; every
+    // pack workgroup has a pass 0 (b < G <= ngroups)
+    int32_t s_lane = fused_rows<VPL, FMT, kWaves>(a, 0, b, G, s_ball, s_base, &v0);
+    for (int p = 0;;) {
+        if (streaming) {   // uniform over the workgroup
+            if (lane < R) s_slot[p & 1][wave][lane] = s_lane;
+            wait_vm();
+            __syncthreads();
+            if (wave == 0 && pub_ok) publish_group<kWaves>(a, rv, s_slot[p & 1]);
+        }
+        if (++p >= a.npass || b + (int64_t)p * G >= a.ngroups) break;
+        s_lane = fused_rows<VPL, FMT, kWaves>(a, p, b, G, s_ball, s_base, nullptr);
+    }
 }
 
 // ------------------------------------------------------------ per-expert mode
@@ -1493,6 +1743,78 @@ int launch_fused(PackArgs& a, int fmt, hipStream_t stream) {
                     : launch_fused_fmt<2, EP_FMT_FP8_E4M3_B128>(a, waves, stream);
 }
 
+// One-kernel large batch: the work order of the two-kernel pack (same
+// group size and grid), when it has one wavefront per token, at most
+// kFusedLargeMaxPasses groups per workgroup, and room for every workgroup
+// (plus the expert one) at once.  kNotTaken when the batch does not qualify;
+// nothing is launched then.
+constexpr int kNotTaken = 1;
+
+template <typename K>
+int64_t resident_blocks(K kernel, int threads) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kernel),
+                                                     threads, 0) != hipSuccess)
+        return 0;
+    return (int64_t)cus * per_cu;
+}
+
+template <int VPL, int FMT, int WAVES>
+int launch_fused_large_fmt(PackArgs a, hipStream_t stream, bool dry) {
+    a.ngroups = ceil_div(a.T, WAVES);
+    const int64_t cap = pack_grid_cap() * kPackWaves / WAVES;
+    const int64_t passes = ceil_div(a.ngroups, cap);
+    const int64_t blocks = ceil_div(a.ngroups, passes);
+    if (passes > kFusedLargeMaxPasses) return kNotTaken;
+    static int64_t room[2] = {-1, -1};   // per process and ring mode; one GPU model
+    const int pub = a.has_ring ? kPubStream : kPubNone;
+    int64_t& rm = room[a.has_ring ? 1 : 0];
+    if (rm < 0)
+        rm = a.has_ring ? resident_blocks(fused_large_kernel<VPL, FMT, WAVES, kPubStream>,
+                                          WAVES * kWave)
+                        : resident_blocks(fused_large_kernel<VPL, FMT, WAVES, kPubNone>,
+                                          WAVES * kWave);
+    if (blocks + 1 > rm) return kNotTaken;
+    if (dry) return EP_OK;
+    a.npass = (int32_t)passes;
+    a.nchunks = 1;
+    const dim3 grid((unsigned)(blocks + 1)), block(WAVES * kWave);
+    clear_hip_error();
+    if (pub == kPubStream)
+        hipLaunchKernelGGL((fused_large_kernel<VPL, FMT, WAVES, kPubStream>), grid, block, 0,
+                           stream, a);
+    else
+        hipLaunchKernelGGL((fused_large_kernel<VPL, FMT, WAVES, kPubNone>), grid, block, 0, stream,
+                           a);
+    EP_HIP_CHECK(hipGetLastError());
+    return EP_OK;
+}
+
+// The vectors per lane of the two-kernel pack for this row size, if one
+// wavefront covers a row and the batch is large enough for the streaming
+// pack (smaller batches and rows take the two-kernel path).  dry: only
+// whether the batch would take the path.
+int launch_fused_large(PackArgs& a, int fmt, hipStream_t stream, bool dry = false) {
+    if ((int64_t)a.T < kPackSmallWaves) return kNotTaken;
+    const int nv = a.nv;
+    if (fmt == EP_FMT_BF16) {
+        if (nv <= 128) return kNotTaken;
+        if (nv <= 256) return launch_fused_large_fmt<4, EP_FMT_BF16, kPackWaves>(a, stream, dry);
+        if (nv <= 512) return launch_fused_large_fmt<8, EP_FMT_BF16, kPackWaves>(a, stream, dry);
+        if (nv <= 896)
+            return launch_fused_large_fmt<kPackVplH7168, EP_FMT_BF16, kPackWaves>(a, stream, dry);
+        if (nv <= 1024) return launch_fused_large_fmt<16, EP_FMT_BF16, kPackWaves>(a, stream, dry);
+        return kNotTaken;
+    }
+    // fp8 rows stay with the two calls: its pack runs 8-wavefront workgroups
+    // at more than 128 registers a lane, one per compute unit, and the
+    // one-kernel version (capped at 128 so that the expert workgroup fits
+    // too) measured slower
+    return kNotTaken;
+}
+
 // One-kernel per-expert small batch: the chunking of the small-batch pack.
 template <int VPL, int FMT>
 int launch_ll_fused_fmt(PackArgs a, int64_t waves, hipStream_t stream) {
@@ -1583,16 +1905,6 @@ extern "C" int ep_dispatch_fused(const ep_shape_t* shape, const void* x, const i
     int v = validate_shape(shape);
     if (v != EP_OK) return v;
     const ep_shape_t s = *shape;
-    if (s.T > kFusedMaxT) {
-        // the two-kernel path: layout, then pack
-        v = ep_dispatch_layout(shape, topk_idx, num_tokens_per_rank, num_tokens_per_expert,
-                               rank_offset, expert_offset, is_token_in_rank, send_slot, workspace,
-                               ws_bytes, dev_status, stream);
-        if (v != EP_OK) return v;
-        return ep_dispatch(shape, x, topk_idx, topk_w, rank_offset, send_slot, send_buf,
-                           capacity_rows, slot_src, slot_local_idx, slot_local_w, ring, workspace,
-                           ws_bytes, dev_status, stream);
-    }
     if (!num_tokens_per_rank || !num_tokens_per_expert || !rank_offset || !expert_offset ||
         !dev_status || !workspace || capacity_rows < 0)
         return EP_ERR_INVALID_ARG;
@@ -1601,6 +1913,10 @@ extern "C" int ep_dispatch_fused(const ep_shape_t* shape, const void* x, const i
     if (capacity_rows > 0 && (!send_buf || !slot_src || !slot_local_idx || !slot_local_w))
         return EP_ERR_INVALID_ARG;
     if (((uintptr_t)x | (uintptr_t)send_buf) & 15) return EP_ERR_INVALID_ARG;
+    // the two-kernel fallback of large batches stores send_slot and
+    // is_token_in_rank in 16- and 4-byte pieces
+    if (s.T > kFusedMaxT && (((uintptr_t)send_slot & 15) || ((uintptr_t)is_token_in_rank & 3)))
+        return EP_ERR_INVALID_ARG;
     if (ws_bytes < workspace_bytes(s)) return EP_ERR_INVALID_ARG;
     if (ring && (uint64_t)capacity_rows * row_bytes(s.H, s.fmt) > kMaxRingOffset)
         return EP_ERR_INVALID_ARG;   // descriptor offsets are 48-bit
@@ -1641,7 +1957,32 @@ extern "C" int ep_dispatch_fused(const ep_shape_t* shape, const void* x, const i
     a.send_slot_out = send_slot;
     a.msg_base_out = w.msg_base;
     a.counters_n = w.counters_n;
-    return launch_fused(a, s.fmt, stream);
+    a.bar = w.barrier;
+    a.wave_cnt = w.wave_rank_cnt;
+    if (s.T <= kFusedMaxT) return launch_fused(a, s.fmt, stream);
+    v = launch_fused_large(a, s.fmt, stream);
+    if (v != kNotTaken) return v;
+    // the two-kernel path: layout, then pack
+    v = ep_dispatch_layout(shape, topk_idx, num_tokens_per_rank, num_tokens_per_expert,
+                           rank_offset, expert_offset, is_token_in_rank, send_slot, workspace,
+                           ws_bytes, dev_status, stream);
+    if (v != EP_OK) return v;
+    return ep_dispatch(shape, x, topk_idx, topk_w, rank_offset, send_slot, send_buf,
+                       capacity_rows, slot_src, slot_local_idx, slot_local_w, ring, workspace,
+                       ws_bytes, dev_status, stream);
+}
+
+extern "C" int ep_dispatch_fused_plan(const ep_shape_t* shape, int32_t with_ring) {
+    int v = validate_shape(shape);
+    if (v != EP_OK) return v;
+    const ep_shape_t s = *shape;
+    if (s.T <= kFusedMaxT) return EP_FUSED_ONE_KERNEL_SMALL;
+    PackArgs a{};
+    a.T = s.T;
+    a.nv = s.H / 8;
+    a.has_ring = with_ring != 0;
+    return launch_fused_large(a, s.fmt, nullptr, true) == EP_OK ? EP_FUSED_ONE_KERNEL_LARGE
+                                                                 : EP_FUSED_TWO_CALLS;
 }
 
 extern "C" int ep_dispatch(const ep_shape_t* shape, const void* x, const int32_t* topk_idx,

@@ -253,7 +253,7 @@ void proxy_loop(ep_ring_t* r, int first, int stride) {
     std::vector<hipEvent_t> free_ev;
     std::deque<Pending> pending;
     if (r->loopback) {
-        hipSetDevice(r->device);
+        (void)hipSetDevice(r->device);
         if (hipStreamCreateWithFlags(&stream, hipStreamNonBlocking) != hipSuccess) stream = nullptr;
     }
     int idle = 0;
@@ -280,7 +280,7 @@ void proxy_loop(ep_ring_t* r, int first, int stride) {
                     if (ev && hipEventRecord(ev, stream) == hipSuccess) {
                         pending.push_back({ev, c, n, t_pop});
                     } else {
-                        hipStreamSynchronize(stream);
+                        (void)hipStreamSynchronize(stream);
                         finish(r, Pending{nullptr, c, n, t_pop});
                         if (ev) free_ev.push_back(ev);
                     }
@@ -306,8 +306,8 @@ void proxy_loop(ep_ring_t* r, int first, int stride) {
             std::this_thread::yield();
         }
     }
-    for (hipEvent_t ev : free_ev) hipEventDestroy(ev);
-    if (stream) hipStreamDestroy(stream);
+    for (hipEvent_t ev : free_ev) (void)hipEventDestroy(ev);
+    if (stream) (void)hipStreamDestroy(stream);
 }
 
 }  // namespace

@@ -7,30 +7,40 @@
 
 namespace ep {
 
-// Rank mask of token t; bad ids are reported and skipped.  When `hist` is
-// given, the token's valid experts are counted in it (LDS).
-__device__ inline uint64_t token_rank_mask(const int32_t* __restrict__ idx, int64_t t, int T,
-                                           int E, int k, int epr, int32_t* st, int32_t* hist) {
+// The k expert ids of token t (-1 past k, and for t >= T), all loads
+// issued before any is used (one memory latency, not k).
+__device__ inline void load_token_ids(const int32_t* __restrict__ idx, int64_t t, int T, int k,
+                                      int32_t (&ids)[kMaxK]) {
+    const int32_t* row = idx + t * k;
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) ids[j] = (t < T && j < k) ? row[j] : -1;
+}
+
+// Rank mask of a token from its ids; bad ids are reported and skipped.  When
+// `hist` is given, the token's valid experts are counted in it (LDS).
+__device__ inline uint64_t rank_mask_of(const int32_t (&ids)[kMaxK], int E, int k, int epr,
+                                        int32_t* st, int32_t* hist) {
     uint64_t m = 0;
-    if (t < T) {
-        // issue all k loads before using any (one memory latency, not k)
-        const int32_t* row = idx + t * k;
-        int32_t ids[kMaxK];
 #pragma unroll
-        for (int j = 0; j < kMaxK; ++j) ids[j] = j < k ? row[j] : -1;
-#pragma unroll
-        for (int j = 0; j < kMaxK; ++j) {
-            const int e = ids[j];
-            if (j >= k || e == -1) continue;
-            if (e < -1 || e >= E) {
-                set_error(st, EP_ERR_BAD_EXPERT);
-                continue;
-            }
-            m |= 1ull << (e / epr);
-            if (hist) atomicAdd(&hist[e], 1);
+    for (int j = 0; j < kMaxK; ++j) {
+        const int e = ids[j];
+        if (j >= k || e == -1) continue;
+        if (e < -1 || e >= E) {
+            set_error(st, EP_ERR_BAD_EXPERT);
+            continue;
         }
+        m |= 1ull << (e / epr);
+        if (hist) atomicAdd(&hist[e], 1);
     }
     return m;
+}
+
+// Rank mask of token t (0 for t >= T), as above.
+__device__ inline uint64_t token_rank_mask(const int32_t* __restrict__ idx, int64_t t, int T,
+                                           int E, int k, int epr, int32_t* st, int32_t* hist) {
+    int32_t ids[kMaxK];
+    load_token_ids(idx, t, T, k, ids);
+    return rank_mask_of(ids, E, k, epr, st, hist);
 }
 
 // Per-wave rank ballots: bit i of ball_r = the wave's token i goes to rank r.

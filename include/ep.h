@@ -120,7 +120,7 @@ typedef struct ep_ring ep_ring_t;
 size_t ep_row_bytes(int32_t H, int32_t fmt);
 
 /* Bytes of device workspace that ep_dispatch_layout and ep_dispatch need for
- * `shape` (a grid-barrier word pair, per-tile partial counts, per-message
+ * `shape` (grid-barrier words, per-tile partial counts, per-message
  * arrival counters).  One workspace serves a layout call and the dispatch
  * calls that follow it on the same stream.  It must be zero-filled once
  * before its first use (e.g. hipMemset); the library leaves it consistent
@@ -189,13 +189,22 @@ int ep_dispatch(const ep_shape_t* shape, const void* x, const int32_t* topk_idx,
                 int32_t* dev_status, hipStream_t stream);
 
 /* Layout and pack in one call: the outputs of ep_dispatch_layout followed by
- * ep_dispatch, with the same arguments, meanings and device errors.  UCCL-EP
- * s4.1 (the low-latency path serves small decode batches, where latency, not
- * bandwidth, is the cost).  For T <= 256 it is one kernel: every workgroup
- * derives the whole (small) layout from topk_idx on chip and starts copying
- * rows at once, and the descriptors are published in closed form by the last
- * workgroup to finish its rows.  For larger T it makes the two calls.
- * Leaves the workspace as the two calls would. */
+ * ep_dispatch, with the same arguments, meanings and device errors (and
+ * EP_ERR_TIMEOUT as for ep_dispatch_layout).  UCCL-EP s4.1 (the dispatch
+ * prepares the token data, synchronises, then posts the transfers; for small
+ * decode batches latency, not bandwidth, is the cost).  For T <= 256 it is
+ * one kernel: every workgroup derives the whole (small) layout from topk_idx
+ * on chip and starts copying rows at once, and the descriptors are published
+ * in closed form by the last workgroup to finish its rows.  For T >= 1024
+ * with bf16 rows that one wavefront covers (H in (1024, 8192]) it is one
+ * kernel too, when its workgroups can all be
+ * resident: each computes the rank ballots of its own tokens' 64-token
+ * blocks, they meet at a grid barrier, and each derives its slots from a
+ * per-block count table, then packs and publishes as ep_dispatch does.
+ * Otherwise it makes the two calls.  ep_dispatch_fused_plan says which.
+ * send_slot must be 16-byte and is_token_in_rank 4-byte aligned when
+ * T > 256.  Leaves in the workspace what a following ep_dispatch with the
+ * same layout needs. */
 int ep_dispatch_fused(const ep_shape_t* shape, const void* x, const int32_t* topk_idx,
                       const float* topk_w, int32_t* num_tokens_per_rank,
                       int32_t* num_tokens_per_expert, int32_t* rank_offset,
@@ -204,6 +213,17 @@ int ep_dispatch_fused(const ep_shape_t* shape, const void* x, const int32_t* top
                       int32_t* slot_src, int32_t* slot_local_idx, float* slot_local_w,
                       ep_ring_t* ring, void* workspace, size_t workspace_bytes,
                       int32_t* dev_status, hipStream_t stream);
+
+/* Which path ep_dispatch_fused takes for `shape` on the current device, for
+ * a call with a ring (with_ring != 0) or without: EP_FUSED_ONE_KERNEL_SMALL,
+ * EP_FUSED_ONE_KERNEL_LARGE or EP_FUSED_TWO_CALLS; EP_ERR_INVALID_ARG for an
+ * invalid shape.  Launches nothing. */
+enum {   /* distinct from every status code */
+    EP_FUSED_ONE_KERNEL_SMALL = 101,
+    EP_FUSED_ONE_KERNEL_LARGE = 102,
+    EP_FUSED_TWO_CALLS = 103
+};
+int ep_dispatch_fused_plan(const ep_shape_t* shape, int32_t with_ring);
 
 /* ep_dispatch_fused for callers that cannot allocate device memory or pass a
  * workspace: code under HIP graph capture, tight serving loops, harnesses

@@ -64,6 +64,25 @@ def test_workspace_bytes(ep):
         assert ep.ep_workspace_bytes(bad) == 0
 
 
+def test_fused_plan_on_the_host(ep):
+    """The path ep_dispatch_fused takes: one kernel up to 256 tokens; the
+    two calls for shapes the one-kernel large path never takes (fewer than
+    1024 tokens, rows of at most 1024 elements, rows that take more than one
+    wavefront); an invalid shape is rejected."""
+    L = ep.lib
+    for s in [ep.shape(1, 64, 16, 4, 2), ep.shape(256, 7168, 256, 32, 8),
+              ep.shape(256, 7168, 256, 32, 8, 1)]:
+        assert ep.ep_dispatch_fused_plan(s) == ep.EP_FUSED_ONE_KERNEL_SMALL
+    for s in [ep.shape(1000, 7168, 256, 32, 8), ep.shape(4096, 1024, 256, 32, 8),
+              ep.shape(4096, 16384, 256, 32, 8), ep.shape(4096, 8192, 256, 32, 8, 1)]:
+        assert ep.ep_dispatch_fused_plan(s) == ep.EP_FUSED_TWO_CALLS
+        assert ep.ep_dispatch_fused_plan(s, with_ring=False) == ep.EP_FUSED_TWO_CALLS
+    assert L.ep_dispatch_fused_plan(ctypes.byref(ep.shape(16, 7, 16, 4, 2)), 1) == 1
+    assert len({ep.EP_FUSED_ONE_KERNEL_SMALL, ep.EP_FUSED_ONE_KERNEL_LARGE, ep.EP_FUSED_TWO_CALLS,
+                ep.EP_OK, ep.EP_ERR_INVALID_ARG, ep.EP_ERR_BAD_EXPERT, ep.EP_ERR_CAPACITY,
+                ep.EP_ERR_RING_TIMEOUT, ep.EP_ERR_HIP, ep.EP_ERR_BUSY, ep.EP_ERR_TIMEOUT}) == 11
+
+
 def test_host_validation_rejects_without_launch(ep):
     L = ep.lib
     bad = ep.shape(16, 7, 16, 4, 2)

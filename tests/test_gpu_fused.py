@@ -1,6 +1,7 @@
 """GPU parity of ep_dispatch_fused (routing layout and pack in one call: one
-kernel for T <= 256, else the two calls) against the CPU oracle, through the
-C ABI.
+kernel for T <= 256; one kernel with a grid barrier for larger bf16 batches
+whose rows take one wavefront; else the two calls) against the CPU oracle,
+through the C ABI.
 
 Bit-exact: counts, offsets, membership, send slots, packed bytes (poisoned
 buffers, rows past P untouched), metadata and fp8 codes.  The closed-form
@@ -42,7 +43,7 @@ def _check_stream(g, L, pk, want, channels):
     assert_descriptors(lg, want, channels, first_seq=1)
 
 
-@pytest.mark.parametrize("name", ["tiny", "decode", "train", "fp8"])
+@pytest.mark.parametrize("name", ["tiny", "decode", "train", "fp8", "skewed"])
 def test_fused_workload_parity(name):
     w = W.WORKLOADS[name]
     inp = pins.workload_inputs(name)
@@ -52,6 +53,10 @@ def test_fused_workload_parity(name):
                      capacity_rows=P + 8)
     want = oracle.descriptors(L["num_tokens_per_rank"], L["rank_offset"],
                               oracle.row_bytes(w.H, w.fmt), w.channels)
+    import combine_topk_rank_amd as ep
+    plan = ep.ep_dispatch_fused_plan(ep.shape(w.T, w.H, w.E, w.R, w.k, w.fmt))
+    assert plan == (ep.EP_FUSED_ONE_KERNEL_SMALL if w.T <= 256 else
+                    ep.EP_FUSED_ONE_KERNEL_LARGE if w.fmt == 0 else ep.EP_FUSED_TWO_CALLS)
     log(f"[fused] workload {name}: T={w.T} H={w.H} R={w.R} k={w.k}, P={P}; one-kernel dispatch")
     g = run_hip(w.T, w.H, w.E, w.R, w.k, w.fmt, inp["x"], inp["topk_idx"], inp["topk_w"],
                 capacity_rows=P + 8,
@@ -85,6 +90,14 @@ CASES = [
     (300, 7168, 256, 32, 8, 0, 0.0, 8, 1024, 256),
     (1100, 7168, 64, 64, 8, 1, 0.1, 8, 64, 16),
     (2000, 2304, 6, 3, 2, 0, 0.3, 2, 1024, 256),
+    # bf16: one kernel with a grid barrier (1024 tokens and more, one wavefront
+    # a row); fp8: the two calls
+    (1024, 7168, 256, 32, 8, 0, 0.0, 8, 1024, 256),
+    (4099, 2048, 64, 16, 4, 0, 0.1, 4, 256, 64),
+    (3000, 8192, 96, 48, 6, 0, 0.05, 8, 1024, 256),
+    (2500, 2048, 128, 8, 8, 1, 0.0, 8, 1024, 256),
+    (5000, 4096, 64, 64, 2, 1, 0.2, 8, 1024, 256),
+    (20000, 4096, 32, 32, 1, 0, 0.0, 16, 2048, 256),
 ]
 
 
@@ -115,11 +128,12 @@ def test_fused_random_case_parity(case):
         combine_tolerance_check(got, ref, f"fused case {case}")
 
 
-def test_fused_matches_two_calls_without_ring():
+@pytest.mark.parametrize("name", ["decode", "train", "fp8"])
+def test_fused_matches_two_calls_without_ring(name):
     """No ring: the one-kernel call and layout + dispatch give the same bytes."""
-    w = W.WORKLOADS["decode"]
-    inp = pins.workload_inputs("decode")
-    log("[fused] decode without a ring: one call vs two calls")
+    w = W.WORKLOADS[name]
+    inp = pins.workload_inputs(name)
+    log(f"[fused] {name} without a ring: one call vs two calls")
     a = run_hip(w.T, w.H, w.E, w.R, w.k, w.fmt, inp["x"], inp["topk_idx"], inp["topk_w"],
                 fused=True)
     b = run_hip(w.T, w.H, w.E, w.R, w.k, w.fmt, inp["x"], inp["topk_idx"], inp["topk_w"])
@@ -145,7 +159,7 @@ def test_fused_repeated_calls_on_one_ring():
     _check(g, L, pk, want, C, calls=3)
 
 
-@pytest.mark.parametrize("name", ["decode", "train"])
+@pytest.mark.parametrize("name", ["decode", "train", "fp8"])
 def test_fused_errors(name):
     """A bad expert id and a capacity shortfall are reported; no descriptor
     goes out, and the rows below the capacity are still written."""

@@ -49,7 +49,7 @@ size_t workspace_bytes(const ep_shape_t& s) {
     b += align256((size_t)nb * s.E * 4);       // blk_exp_cnt
     b += align256((size_t)wave_blocks(s.T) * s.R * 4);   // wave_rank_cnt
     b += align256((size_t)(s.R + 1) * 4);      // msg_base
-    b += align256((size_t)(max_messages(s) + s.R) * 4);   // msg_arrivals + rank_msgs_done
+    b += align256((size_t)(max_messages(s) + s.E) * 4);   // msg_arrivals + msgs_done
     return b;
 }
 
@@ -71,8 +71,8 @@ Workspace carve_workspace(const ep_shape_t& s, void* base) {
     p += align256((size_t)(s.R + 1) * 4);
     w.max_msgs = max_messages(s);
     w.msg_arrivals = reinterpret_cast<int32_t*>(p);
-    w.rank_msgs_done = w.msg_arrivals + w.max_msgs;
-    w.counters_n = w.max_msgs + s.R;
+    w.msgs_done = w.msg_arrivals + w.max_msgs;
+    w.counters_n = w.max_msgs + s.E;
     return w;
 }
 

@@ -69,9 +69,9 @@ struct Workspace {
     int32_t* wave_rank_cnt;   // [ceil(T/64), R] per-64-token rank counts (one-kernel dispatch)
     int32_t* msg_base;        // [R+1]   first message index of each rank
     int32_t* msg_arrivals;    // [max_msgs] rows (x chunks) written per message
-    int32_t* rank_msgs_done;  // [R]     messages of a rank published
+    int32_t* msgs_done;       // [E]     messages of a rank (or, per-expert mode, an expert) published
     int64_t max_msgs;
-    int64_t counters_n;       // msg_arrivals .. rank_msgs_done, contiguous
+    int64_t counters_n;       // msg_arrivals .. msgs_done, contiguous
     int32_t layout_blocks;
 };
 
@@ -83,9 +83,11 @@ inline int32_t layout_blocks(int32_t T) {
 
 inline int64_t wave_blocks(int32_t T) { return T <= 0 ? 1 : ceil_div(T, kWave); }
 
+// Messages of one call, at most: per rank, ceil(rows / 8) with at most
+// min(k, R) rows a token; per expert (per-expert mode), ceil(rows / 8) with k
+// rows a token.  Both are below ceil(T * k / 8) + E.
 inline int64_t max_messages(const ep_shape_t& s) {
-    int64_t kr = s.k < s.R ? s.k : s.R;
-    return ceil_div((int64_t)s.T * kr, kMsgRows) + s.R;
+    return ceil_div((int64_t)s.T * s.k, kMsgRows) + s.E;
 }
 
 size_t workspace_bytes(const ep_shape_t& s);

@@ -54,7 +54,7 @@ struct PackArgs {
     float* slot_local_w;          // [cap, k]
     const int32_t* msg_base;      // [R+1]
     int32_t* msg_arrivals;        // [max_msgs]
-    int32_t* rank_msgs_done;      // [R]
+    int32_t* msgs_done;           // [E] messages of a rank / an expert published
     int32_t* st;
     RingDev ring;
     int64_t max_msgs;             // entries of msg_arrivals
@@ -78,7 +78,7 @@ struct PackArgs {
     uint8_t* in_rank_out;         // [T, R]
     int32_t* send_slot_out;       // [T, R]
     int32_t* msg_base_out;        // [R+1] (workspace)
-    int64_t counters_n;           // msg_arrivals .. rank_msgs_done
+    int64_t counters_n;           // msg_arrivals .. msgs_done
     // one-kernel large batches
     uint32_t* bar;                // grid barrier words (workspace)
     int32_t* wave_cnt;            // [ceil(T/64), R] per-64-token rank counts (workspace)
@@ -246,6 +246,74 @@ __device__ inline void load_rank_view(const PackArgs& a, RankView& v) {
     }
 }
 
+// Up to N commands per lane, command i on its own channel c[i] (those with
+// bit i of `have`): as ring_publish_n, each command written as soon as its ticket is
+// inside its channel's window, so no command of the wavefront waits for
+// another of the same wavefront.  System-scope slot stores.
+template <int N>
+__device__ void ring_publish_v(const RingDev& g, uint32_t have, const int* c,
+                               const unsigned long long* ticket, const RingCmd* cmd, int32_t* st) {
+    if (!__ballot(have != 0)) return;
+    const unsigned long long lim = (unsigned long long)g.max_inflight;
+    unsigned long long seen[N];
+    uint32_t pending = have;
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        seen[i] = ((pending >> i) & 1u) ? __hip_atomic_load(g.tail_cache + (size_t)c[i] * kPad,
+                                                            __ATOMIC_RELAXED,
+                                                            __HIP_MEMORY_SCOPE_AGENT)
+                                        : 0ull;
+    bool polled = false;
+    unsigned long long t0 = 0;
+    while (__ballot(pending != 0)) {
+        bool progress = false;
+        if (pending) {
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+                if (!((pending >> i) & 1u) || ticket[i] < seen[i] + lim) continue;
+                // the cached consumer position says full: one lane per channel
+                // at a time reads the real one over PCIe and refreshes the cache
+                unsigned long long* poll = g.poll + (size_t)c[i] * kPad;
+                unsigned long long* cache = g.tail_cache + (size_t)c[i] * kPad;
+                if (atomicCAS(poll, 0ull, 1ull) == 0ull) {
+                    const unsigned long long h = __hip_atomic_load(
+                        g.host_tail + (size_t)c[i] * kPad, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+                    atomicMax(cache, h);
+                    atomicExch(poll, 0ull);
+                }
+                const unsigned long long cv =
+                    __hip_atomic_load(cache, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (cv > seen[i]) seen[i] = cv;
+            }
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+                if (((pending >> i) & 1u) && ticket[i] < seen[i] + lim) {
+                    ring_write<true>(g, c[i], ticket[i], cmd[i].type, cmd[i].op, cmd[i].ntok,
+                                     cmd[i].dst_rank, cmd[i].size_val, cmd[i].src_off,
+                                     cmd[i].dst_off);
+                    pending &= ~(1u << i);
+                    progress = true;
+                }
+            }
+            if (pending && !progress) {
+                if (read_status(st) != 0) {
+                    pending = 0;
+                } else {
+                    const unsigned long long now = __builtin_amdgcn_s_memrealtime();
+                    if (!polled) {
+                        polled = true;
+                        t0 = now;
+                    } else if (now - t0 > g.timeout_ticks) {
+                        set_error(st, EP_ERR_RING_TIMEOUT);
+                        pending = 0;
+                    }
+                }
+            }
+        }
+        if (!__ballot(progress) && __ballot(pending != 0)) __builtin_amdgcn_s_sleep(16);
+    }
+}
+
 // ATOMIC{ADD, cnt} for ranks that receive no rows (nothing to order after).
 __device__ void publish_empty_ranks(const PackArgs& a, const RankView& rv) {
     const int lane = lane_id();
@@ -346,7 +414,7 @@ __device__ void publish_group(const PackArgs& a, const RankView& rv,
         // reserve the ATOMIC's ticket, which then follows every WRITE ticket
         // of the rank.
         const int32_t add = ndone + (int32_t)(t0 >> 62);
-        done = atomicAdd(&a.rank_msgs_done[lane], add);
+        done = atomicAdd(&a.msgs_done[lane], add);
     }
     const uint64_t rb = (uint64_t)a.row_bytes;
     RingCmd cmd[3];
@@ -361,7 +429,7 @@ __device__ void publish_group(const PackArgs& a, const RankView& rv,
     bool atom = false;
     unsigned long long ta = 0;
     if (nw > 0 && done + ndone == (cnt + kMsgRows - 1) / kMsgRows) {
-        a.rank_msgs_done[lane] = 0;
+        a.msgs_done[lane] = 0;
         ta = ring_reserve(a.ring, c, 1);
         atom = true;
     }
@@ -1376,43 +1444,230 @@ __device__ void ll_closed_publish(const PackArgs& a, const int32_t* exp_off) {
     }
 }
 
+// Per-expert streaming publication (large batches): as in the rank pack,
+// each message -- the <= 8 consecutive rows [eo_e + 8m, ...) of expert e --
+// is published by the arrival that completes it, and the expert's ATOMIC by
+// the wavefront whose WRITE completes the expert's message count, with a
+// ticket taken after every WRITE ticket of the expert.  Wavefront 0 of each
+// workgroup stages the expert offsets and the experts' first message indices
+// in LDS once per launch.
+__device__ void ll_stage_experts(const PackArgs& a, int32_t* eo, int32_t* mb) {
+    const int lane = lane_id(), E = a.E;
+    for (int e = lane; e <= E; e += kWave) eo[e] = a.exp_off[e];
+    // messages per expert, then their exclusive scan (lane l sums a run)
+    const int per = (E + kWave - 1) / kWave;
+    const int e0 = lane * per;
+    int32_t sum = 0;
+    for (int i = 0; i < per; ++i) {
+        const int e = e0 + i;
+        if (e < E) sum += (eo[e + 1] - eo[e] + kMsgRows - 1) / kMsgRows;
+    }
+    int32_t incl = sum;
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int32_t v = __shfl_up(incl, d);
+        if (lane >= d) incl += v;
+    }
+    int32_t run = incl - sum;
+    for (int i = 0; i < per; ++i) {
+        const int e = e0 + i;
+        if (e < E) {
+            mb[e] = run;
+            run += (eo[e + 1] - eo[e] + kMsgRows - 1) / kMsgRows;
+        }
+    }
+    if (lane == kWave - 1) mb[E] = incl;
+}
+
+// ATOMIC{ADD, 0} of every expert with no rows (nothing to order after), by
+// wavefront 0 of one workgroup, 64 experts a round.
+__device__ void ll_publish_empty(const PackArgs& a, const int32_t* eo) {
+    const int lane = lane_id();
+    for (int e0 = 0; e0 < a.E; e0 += kWave) {
+        const int e = e0 + lane;
+        int n = 0, c = 0;
+        unsigned long long tk = 0;
+        RingCmd cmd{};
+        if (e < a.E && eo[e + 1] == eo[e]) {
+            const int r = e / a.epr;
+            c = r % a.ring.channels;
+            tk = ring_reserve(a.ring, c, 1);
+            cmd = RingCmd{EP_CMD_ATOMIC, EP_ATOMIC_ADD, 0, (uint32_t)r, 0, 0,
+                          (uint64_t)(4 * (e - r * a.epr))};
+            n = 1;
+        }
+        ring_publish_v<1>(a.ring, n ? 1u : 0u, &c, &tk, &cmd, a.st);
+    }
+}
+
+// Wavefront 0, after the rows of its group are released: row[w][j] and
+// ex[w][j] are the row and expert of wavefront w's choice j (-1 for none).
+// The W * k pairs go in rounds of 128, two per lane; a pair adds one arrival
+// (one chunk of one row) to its message.  Within a round every step is
+// issued for both of a lane's pairs at once: one round trip each for the
+// arrivals (with the status word), the WRITE tickets, the experts' message
+// counts and the ATOMIC tickets.  A round's tickets are all written before
+// the next round takes any.
+template <int W>
+__device__ void ll_publish_group(const PackArgs& a, const int32_t* eo, const int32_t* mb,
+                                 const int32_t (*row)[kMaxK], const int32_t (*ex)[kMaxK]) {
+    constexpr int P = 2;
+    const int lane = lane_id();
+    const int k = a.k, C = a.ring.channels;
+    const int npairs = W * k;
+    // an inconsistent group is reported before it counts any row or takes
+    // any ticket
+    bool bad = false;
+    for (int f = lane; f < npairs; f += kWave) {
+        const int sf = row[f / k][f % k], ef = ex[f / k][f % k];
+        if (sf >= 0 && (ef < 0 || ef >= a.E || sf < eo[ef] || sf >= eo[ef + 1] ||
+                        mb[ef] + (sf - eo[ef]) / kMsgRows >= a.max_msgs))
+            bad = true;   // expert_slot not from this expert_offset, or the message table too small
+    }
+    if (__ballot(bad)) {
+        if (bad) set_error(a.st, EP_ERR_INVALID_ARG);
+        return;
+    }
+    const uint64_t rb = (uint64_t)a.row_bytes;
+    for (int f0 = 0; f0 < npairs; f0 += P * kWave) {
+        int32_t s[P], e[P];
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            const int f = f0 + lane + i * kWave;
+            s[i] = f < npairs ? row[f / k][f % k] : -1;
+            e[i] = f < npairs ? ex[f / k][f % k] : -1;
+        }
+        // arrivals, with the status word
+        const int32_t st0 = read_status(a.st);
+        int32_t old[P];
+#pragma unroll
+        for (int i = 0; i < P; ++i)
+            old[i] = s[i] >= 0
+                         ? atomicAdd(&a.msg_arrivals[mb[e[i]] + (s[i] - eo[e[i]]) / kMsgRows], 1)
+                         : 0;
+        uint32_t done = 0;
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            if (s[i] < 0) continue;
+            const int32_t m = (s[i] - eo[e[i]]) / kMsgRows;
+            const int32_t nrows = min(kMsgRows, eo[e[i] + 1] - eo[e[i]] - m * kMsgRows);
+            if (old[i] + 1 == nrows * a.nchunks) {
+                a.msg_arrivals[mb[e[i]] + m] = 0;   // every arrival is in: leave it clean
+                if (st0 == 0) done |= 1u << i;
+            }
+        }
+        if (!__ballot(done != 0)) continue;
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        // WRITE tickets, then (once they exist) the experts' message counts;
+        // an expert's last message takes the ATOMIC's ticket after them all
+        int c[2 * P];
+        unsigned long long tk[2 * P];
+        RingCmd cmd[2 * P];
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            c[i] = c[P + i] = 0;
+            tk[i] = tk[P + i] = 0;
+            cmd[i] = cmd[P + i] = RingCmd{};
+            if (!((done >> i) & 1u)) continue;
+            const int r = e[i] / a.epr;
+            const int32_t eo_e = eo[e[i]];
+            const int32_t m = (s[i] - eo_e) / kMsgRows;
+            const int32_t nrows = min(kMsgRows, eo[e[i] + 1] - eo_e - m * kMsgRows);
+            c[i] = c[P + i] = r % C;
+            tk[i] = ring_reserve(a.ring, c[i], 1);
+            cmd[i] = RingCmd{EP_CMD_WRITE, 0, (uint32_t)nrows, (uint32_t)r, (uint32_t)(nrows * rb),
+                             (uint64_t)(eo_e + m * kMsgRows) * rb,
+                             (uint64_t)(eo_e - eo[r * a.epr] + m * kMsgRows) * rb};
+        }
+        int32_t dn[P];
+#pragma unroll
+        for (int i = 0; i < P; ++i)
+            dn[i] = ((done >> i) & 1u) ? atomicAdd(&a.msgs_done[e[i]], 1 + (int32_t)(tk[i] >> 62))
+                                       : 0;
+        uint32_t have = done;
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            if (!((done >> i) & 1u)) continue;
+            const int32_t cnt = eo[e[i] + 1] - eo[e[i]];
+            if (dn[i] + 1 == (cnt + kMsgRows - 1) / kMsgRows) {
+                a.msgs_done[e[i]] = 0;
+                const int r = e[i] / a.epr;
+                tk[P + i] = ring_reserve(a.ring, c[P + i], 1);
+                cmd[P + i] = RingCmd{EP_CMD_ATOMIC, EP_ATOMIC_ADD, 0, (uint32_t)r, (uint32_t)cnt,
+                                     0, (uint64_t)(4 * (e[i] - r * a.epr))};
+                have |= 1u << (P + i);
+            }
+        }
+        ring_publish_v<2 * P>(a.ring, have, c, tk, cmd, a.st);
+    }
+}
+
 // Per-expert pack: wavefront g takes chunk g % nchunks of token g / nchunks
 // and stores it to the row of every kept choice of the token (no dedup by
 // rank: a token naming an expert twice sends two rows); the token's first
-// chunk also writes each row's source token and gate.  With a ring, the last
-// workgroup to finish publishes every command in closed form.
+// chunk also writes each row's source token and gate.  With a ring, large
+// batches publish as messages complete (ll_publish_group); small ones in
+// closed form, by the last workgroup to finish.
 template <int VPL, int FMT, int WAVES, int PUB>
 __global__ __launch_bounds__(WAVES * kWave) void ll_pack_kernel(PackArgs a) {
+    constexpr bool STREAM = PUB == kPubStream;
+    // streaming: the group's rows and experts, per wavefront and choice, two
+    // buffers by pass parity; the staged expert offsets and message bases
+    __shared__ int32_t s_row[STREAM ? 2 : 1][STREAM ? WAVES : 1][kMaxK];
+    __shared__ int32_t s_ex[STREAM ? 2 : 1][STREAM ? WAVES : 1][kMaxK];
+    __shared__ int32_t s_eo[STREAM ? kMaxE + 1 : 1];
+    __shared__ int32_t s_mb[STREAM ? kMaxE + 1 : 1];
     const int lane = lane_id();
     const int wave = (int)(threadIdx.x / kWave);
     const int64_t Q = a.exp_off[a.E];
     const bool cap_ok = Q <= a.cap;
     if (blockIdx.x == 0 && wave == 0) {
         if (!cap_ok && lane == 0) set_error(a.st, EP_ERR_CAPACITY);
-        if (PUB == kPubClosed) refresh_tail_cache(a);
+        if (PUB != kPubNone) refresh_tail_cache(a);
     }
-    for (int64_t grp = blockIdx.x; grp < a.ngroups; grp += gridDim.x) {
+    // streaming publication runs when the ring exists and the rows fit;
+    // wavefront 0 publishes only if no error was reported before the kernel
+    // started (then no command goes out)
+    const bool streaming = STREAM && cap_ok;
+    bool pub_ok = false;   // wavefront 0 only
+    if (streaming && wave == 0) {
+        pub_ok = bcast(read_status(a.st), 0) == 0;
+        ll_stage_experts(a, s_eo, s_mb);
+        if (pub_ok && blockIdx.x == 0) ll_publish_empty(a, s_eo);
+    }
+    int pass = 0;
+    for (int64_t grp = blockIdx.x; grp < a.ngroups; grp += gridDim.x, pass ^= 1) {
         const int64_t gw = grp * WAVES + wave;
         const int64_t t = gw / a.nchunks;
         const int chunk = (int)(gw - t * a.nchunks);
-        if (t >= a.T) continue;   // wavefront-uniform
-        int32_t s_lane = -1;
-        float w_lane = 0.0f;
-        if (lane < a.k) {
-            const int e = a.idx[t * a.k + lane];
-            if (e >= 0 && e < a.E) {
-                s_lane = a.expert_slot[t * a.k + lane];
-                w_lane = a.w[t * a.k + lane];
-                if (s_lane < a.exp_off[e] || s_lane >= a.exp_off[e + 1])
-                    set_error(a.st, EP_ERR_INVALID_ARG);   // expert_slot not from this layout
+        int32_t s_lane = -1, e_lane = -1;
+        if (t < a.T) {   // wavefront-uniform
+            float w_lane = 0.0f;
+            if (lane < a.k) {
+                const int e = a.idx[t * a.k + lane];
+                if (e >= 0 && e < a.E) {
+                    s_lane = a.expert_slot[t * a.k + lane];
+                    e_lane = e;
+                    w_lane = a.w[t * a.k + lane];
+                    if (s_lane < a.exp_off[e] || s_lane >= a.exp_off[e + 1])
+                        set_error(a.st, EP_ERR_INVALID_ARG);   // expert_slot not from this layout
+                }
+            }
+            const uint64_t dmask = __ballot(s_lane >= 0);
+            store_row_chunk<VPL, FMT>(a, t, chunk, s_lane, dmask);
+            if (chunk == 0 && s_lane >= 0 && s_lane < a.cap) {
+                a.slot_src[s_lane] = (int32_t)t;
+                a.slot_w[s_lane] = w_lane;
             }
         }
-        const uint64_t dmask = __ballot(s_lane >= 0);
-        store_row_chunk<VPL, FMT>(a, t, chunk, s_lane, dmask);
-        if (chunk == 0 && s_lane >= 0 && s_lane < a.cap) {
-            a.slot_src[s_lane] = (int32_t)t;
-            a.slot_w[s_lane] = w_lane;
+        if (!streaming) continue;   // uniform over the workgroup
+        if (lane < kMaxK) {
+            s_row[pass][wave][lane] = s_lane;
+            s_ex[pass][wave][lane] = e_lane;
         }
+        // rows went out with system-scope stores: complete means visible
+        wait_vm();
+        __syncthreads();
+        if (wave == 0 && pub_ok) ll_publish_group<WAVES>(a, s_eo, s_mb, s_row[pass], s_ex[pass]);
     }
     if (PUB == kPubClosed) {
         __shared__ int s_last;
@@ -1624,11 +1879,11 @@ int64_t pack_grid_cap() {
     return cap;
 }
 
-// SMALL: the small-batch configuration (closed-form publication).  LL: the
-// per-expert pack (always closed-form publication with a ring).
+// SMALL: the small-batch configuration (closed-form publication; otherwise
+// streaming with a ring).  LL: the per-expert pack.
 template <int VPL, int FMT, int WAVES, bool SMALL, bool LL>
 int launch_pack_fmt(PackArgs a, int64_t waves, hipStream_t stream) {
-    const int pub = !a.has_ring ? kPubNone : (SMALL || LL) ? kPubClosed : kPubStream;
+    const int pub = !a.has_ring ? kPubNone : SMALL ? kPubClosed : kPubStream;
     a.ngroups = ceil_div(waves, WAVES);
     // keep about the same number of wavefronts resident whatever WAVES is,
     // and give every workgroup the same number of passes (+-1 group), so no
@@ -1642,8 +1897,11 @@ int launch_pack_fmt(PackArgs a, int64_t waves, hipStream_t stream) {
         if (pub == kPubNone)
             hipLaunchKernelGGL((ll_pack_kernel<VPL, FMT, WAVES, kPubNone>), grid, block, 0, stream,
                                a);
-        else
+        else if (pub == kPubClosed)
             hipLaunchKernelGGL((ll_pack_kernel<VPL, FMT, WAVES, kPubClosed>), grid, block, 0,
+                               stream, a);
+        else
+            hipLaunchKernelGGL((ll_pack_kernel<VPL, FMT, WAVES, kPubStream>), grid, block, 0,
                                stream, a);
     } else if (pub == kPubNone)
         hipLaunchKernelGGL((pack_kernel<VPL, FMT, WAVES, kPubNone>), grid, block, 0, stream, a);
@@ -1876,6 +2134,9 @@ extern "C" int ep_dispatch_ll_fused(const ep_shape_t* shape, const void* x,
     a.slot_src = slot_src;
     a.slot_w = slot_w;
     a.arrive = w.arrive;
+    a.msg_arrivals = w.msg_arrivals;
+    a.msgs_done = w.msgs_done;
+    a.max_msgs = w.max_msgs;
     a.st = dev_status;
     a.ring = ring_device_view(ring);
     a.has_ring = ring != nullptr;
@@ -1934,7 +2195,7 @@ extern "C" int ep_dispatch_fused(const ep_shape_t* shape, const void* x, const i
     a.slot_local_w = slot_local_w;
     a.msg_base = w.msg_base;
     a.msg_arrivals = w.msg_arrivals;
-    a.rank_msgs_done = w.rank_msgs_done;
+    a.msgs_done = w.msgs_done;
     a.max_msgs = w.max_msgs;
     a.arrive = w.arrive;
     a.st = dev_status;
@@ -2016,7 +2277,7 @@ extern "C" int ep_dispatch(const ep_shape_t* shape, const void* x, const int32_t
     a.slot_local_w = slot_local_w;
     a.msg_base = w.msg_base;
     a.msg_arrivals = w.msg_arrivals;
-    a.rank_msgs_done = w.rank_msgs_done;
+    a.msgs_done = w.msgs_done;
     a.max_msgs = w.max_msgs;
     a.arrive = w.arrive;
     a.st = dev_status;
@@ -2063,6 +2324,9 @@ extern "C" int ep_dispatch_ll(const ep_shape_t* shape, const void* x, const int3
     a.slot_src = slot_src;
     a.slot_w = slot_w;
     a.arrive = w.arrive;
+    a.msg_arrivals = w.msg_arrivals;
+    a.msgs_done = w.msgs_done;
+    a.max_msgs = w.max_msgs;
     a.st = dev_status;
     a.ring = ring_device_view(ring);
     a.has_ring = ring != nullptr;

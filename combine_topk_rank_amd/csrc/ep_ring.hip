@@ -51,7 +51,13 @@ struct ep_ring {
                                                     // mirrored for the GPU
     unsigned long long* dev_state = nullptr;   // device: head, tail_cache, poll; each [C*kPad]
     unsigned long long timeout_ticks = 0;
-    std::vector<unsigned long long> pos;       // consumer position per channel
+    // per channel, each on its own 64-byte line: proxy threads that serve
+    // different channels never write the same line
+    struct alignas(64) ChannelState {
+        unsigned long long pos = 0;              // consumer position
+        std::atomic<int64_t> completed{0};       // commands completed
+    };
+    std::unique_ptr<ChannelState[]> ch;
     std::mutex mu;                             // serialises host-side calls
     // proxy
     std::vector<std::thread> threads;
@@ -69,7 +75,6 @@ struct ep_ring {
     std::vector<uint64_t> lb_dst_bytes;
     std::vector<uint8_t*> lb_cnt;
     std::vector<uint64_t> lb_cnt_bytes;
-    std::unique_ptr<std::atomic<int64_t>[]> completed;   // per channel
     std::atomic<int64_t> lb_errors{0};
     std::atomic<int64_t> lb_done{0};
     std::atomic<int64_t> lb_lat_sum_ns{0};
@@ -104,7 +109,7 @@ namespace {
 // Pop up to `max` published commands of channel c (the slot format and the
 // pop itself: ep_ring_proto.h); returns the number popped.
 int64_t pop_channel(ep_ring_t* r, int c, ep_transfer_cmd_t* out, int64_t max, bool publish) {
-    return ring_pop(r->slots + (size_t)c * r->depth, (uint32_t)r->depth, &r->pos[c],
+    return ring_pop(r->slots + (size_t)c * r->depth, (uint32_t)r->depth, &r->ch[c].pos,
                     publish ? &r->host_tail[(size_t)c * kPad] : nullptr, out, max);
 }
 
@@ -145,7 +150,7 @@ __global__ void loopback_add(AddList l) {
 // count where the GPU can read it (one writer per channel at a time: the
 // proxy thread serving it, or ep_ring_drain while no proxy runs).
 void add_completed(ep_ring_t* r, int c, int64_t n) {
-    const int64_t v = r->completed[c].fetch_add(n, std::memory_order_release) + n;
+    const int64_t v = r->ch[c].completed.fetch_add(n, std::memory_order_release) + n;
     __atomic_store_n(&r->host_completed[(size_t)c * kPad], (unsigned long long)v, __ATOMIC_RELEASE);
 }
 
@@ -266,8 +271,11 @@ void proxy_loop(ep_ring_t* r, int first, int stride) {
                 const int64_t t_pop = now_ns();
                 got += n;
                 r->drained.fetch_add(n, std::memory_order_relaxed);
-                int64_t at = r->log_n.fetch_add(n, std::memory_order_relaxed);
-                for (int64_t i = 0; i < n && at + i < r->log_capacity; ++i) r->log[at + i] = batch[i];
+                if (r->log_capacity > 0) {
+                    const int64_t at = r->log_n.fetch_add(n, std::memory_order_relaxed);
+                    for (int64_t i = 0; i < n && at + i < r->log_capacity; ++i)
+                        r->log[at + i] = batch[i];
+                }
                 if (stream) {
                     execute_batch(r, batch, n, stream);
                     hipEvent_t ev = nullptr;
@@ -323,13 +331,11 @@ extern "C" ep_ring_t* ep_ring_create(int32_t depth, int32_t channels, int32_t ma
     r->channels = channels;
     r->max_inflight = max_inflight;
     r->timeout_ns = timeout_ns;
-    r->pos.assign(channels, 0);
-    r->completed.reset(new (std::nothrow) std::atomic<int64_t>[channels]);
-    if (!r->completed) {
+    r->ch.reset(new (std::nothrow) ep_ring::ChannelState[channels]);
+    if (!r->ch) {
         delete r;
         return nullptr;
     }
-    for (int c = 0; c < channels; ++c) r->completed[c].store(0);
     bool ok = hipGetDevice(&r->device) == hipSuccess;
     int rate_khz = 0;
     ok = ok && hipDeviceGetAttribute(&rate_khz, hipDeviceAttributeWallClockRate, r->device) ==
@@ -381,8 +387,10 @@ extern "C" int ep_ring_reset(ep_ring_t* r) {
     std::memset(r->slots, 0, (size_t)r->channels * r->depth * sizeof(RingSlot));
     std::memset(r->host_tail, 0, (size_t)r->channels * kPad * sizeof(unsigned long long));
     std::memset(r->host_completed, 0, (size_t)r->channels * kPad * sizeof(unsigned long long));
-    std::fill(r->pos.begin(), r->pos.end(), 0ull);
-    for (int c = 0; c < r->channels; ++c) r->completed[c].store(0);
+    for (int c = 0; c < r->channels; ++c) {
+        r->ch[c].pos = 0;
+        r->ch[c].completed.store(0);
+    }
     EP_HIP_CHECK(hipMemset(r->dev_state, 0, 3 * (size_t)r->channels * kPad * sizeof(unsigned long long)));
     EP_HIP_CHECK(hipDeviceSynchronize());
     return EP_OK;
@@ -481,7 +489,7 @@ extern "C" int ep_ring_set_loopback(ep_ring_t* r, const void* src, uint64_t src_
 
 extern "C" int64_t ep_ring_completed(const ep_ring_t* r, int32_t channel) {
     if (!r || channel < 0 || channel >= r->channels) return -1;
-    return r->completed[channel].load(std::memory_order_acquire);
+    return r->ch[channel].completed.load(std::memory_order_acquire);
 }
 
 extern "C" int ep_ring_check_completion(const ep_ring_t* r, const int32_t* channels,
@@ -507,7 +515,7 @@ extern "C" int ep_ring_wait_complete(ep_ring_t* r, int64_t timeout_ns) {
     for (;;) {
         bool done = true;
         for (int c = 0; c < r->channels && done; ++c)
-            done = r->completed[c].load(std::memory_order_acquire) >=
+            done = r->ch[c].completed.load(std::memory_order_acquire) >=
                    (int64_t)head[(size_t)c * kPad];
         if (done) break;
         if (now_ns() - t0 > timeout_ns) return EP_ERR_RING_TIMEOUT;

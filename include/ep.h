@@ -293,9 +293,12 @@ int ep_dispatch_layout_ll(const ep_shape_t* shape, const int32_t* topk_idx,
  *            (expert_offset[e] - expert_offset[r*E/R] + 8m) * row bytes}, then
  *            ATOMIC{ADD, value cnt_e, dst_offset 4 * (e - r*E/R)} (the
  *            receiver's count word of that expert; also for cnt_e = 0).  Rank
- *            r uses channel r % channels; per channel, ranks ascending, a
- *            rank's experts ascending.  The commands are published once every
- *            row is written (they are visible to other agents first).
+ *            r uses channel r % channels.  A WRITE is published only after
+ *            its rows are written (visible to other agents), an expert's
+ *            ATOMIC after all of its WRITEs.  Small batches (fewer than 1024
+ *            row chunks) publish in closed form once every row is written:
+ *            per channel, ranks ascending, a rank's experts ascending; larger
+ *            ones as each message's rows complete.
  * Device errors: EP_ERR_CAPACITY (rows >= capacity_rows are not written, no
  * descriptor is emitted), EP_ERR_RING_TIMEOUT, EP_ERR_INVALID_ARG
  * (expert_slot and expert_offset do not come from the same layout; no

@@ -170,6 +170,58 @@ def assert_descriptors(log_, want, channels, first_seq=None):
             assert sa > last_write[r], f"rank {r}: ATOMIC before a WRITE"
 
 
+def pack_streams(T, H, fmt):
+    """Whether a pack of T tokens publishes as messages complete (1024 or
+    more whole-chunk wavefronts) rather than in closed form: the chunking of
+    the pack kernels (vectors per lane by row size)."""
+    nv = H // 8
+    if nv <= 64:
+        vpl = 1
+    elif nv <= 128:
+        vpl = 2
+    elif nv <= 256:
+        vpl = 4
+    elif nv <= 512:
+        vpl = 8
+    elif fmt != 0:
+        vpl = 14 if nv <= 896 else 8
+    else:
+        vpl = 14 if nv <= 896 else 16
+    return T * -(-nv // (vpl * 64)) >= 1024
+
+
+def assert_ll_descriptors(log_, want, channels, expert_offset, E, R, row_bytes_):
+    """Per-expert streaming publication: the same multiset of commands; per
+    channel consecutive tickets from 1; each expert's ATOMIC after all of
+    its WRITEs."""
+    got = sorted(cmd_key(d) for d in log_)
+    exp = sorted(cmd_key(d) for d in want)
+    if got != exp:
+        cg, ce = collections.Counter(got), collections.Counter(exp)
+        raise AssertionError(f"descriptor multisets differ: missing {list((ce - cg).items())[:4]} "
+                             f"extra {list((cg - ce).items())[:4]} ({len(got)} vs {len(exp)})")
+    epr = E // R
+    eo = np.asarray(expert_offset, np.int64)
+    by_ch = collections.defaultdict(list)
+    for d in log_:
+        by_ch[int(d["dst_rank"]) % channels].append(d)
+    for c, ds in by_ch.items():
+        seqs = np.sort(np.array([int(d["seq"]) for d in ds], np.int64))
+        assert seqs[0] == 1 and np.all(np.diff(seqs) == 1), f"channel {c}: tickets not 1, 2, ..."
+        last_write, atomic_seq = {}, {}
+        for d in ds:
+            r = int(d["dst_rank"])
+            if d["type"] == 1:
+                rel = int(d["dst_offset"]) // row_bytes_ + int(eo[r * epr])
+                e = int(np.searchsorted(eo[r * epr:(r + 1) * epr + 1], rel, side="right")) - 1 + r * epr
+                last_write[e] = max(last_write.get(e, -1), int(d["seq"]))
+            else:
+                atomic_seq[r * epr + int(d["dst_offset"]) // 4] = int(d["seq"])
+        for e, sa in atomic_seq.items():
+            assert sa > last_write.get(e, -1), f"expert {e}: ATOMIC before a WRITE"
+        assert set(last_write) <= set(atomic_seq), "an expert's WRITEs without its ATOMIC"
+
+
 def combine_tolerance_check(got, ref, what=""):
     """|gpu - ref| <= 1e-2 * max(1, |ref|) element by element."""
     err = np.abs(got - ref)

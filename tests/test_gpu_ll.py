@@ -1,7 +1,10 @@
 """Per-expert (low-latency) mode on the GPU against the oracle, through the C
-ABI: row table, packed rows and metadata bit-exact, the closed-form command
-stream command for command, combine within 1e-2 * max(1, |ref|).  The same
-checks run on the one-call ep_dispatch_ll_fused (T <= 256, E <= 1024)."""
+ABI: row table, packed rows and metadata bit-exact; the command stream
+command for command where it is published in closed form (small batches),
+else the same multiset with consecutive tickets per channel and each
+expert's ATOMIC after its WRITEs (streaming publication); combine within
+1e-2 * max(1, |ref|).  The same checks run on the one-call
+ep_dispatch_ll_fused (T <= 256, E <= 1024)."""
 
 import numpy as np
 import pytest
@@ -9,8 +12,8 @@ import pytest
 import oracle
 import oracle_pins as pins
 import workloads as W
-from gpu_helpers import (assert_ll_equal, assert_stream_in_order, combine_tolerance_check, log,
-                         run_hip_combine_ll, run_hip_ll)
+from gpu_helpers import (assert_ll_descriptors, assert_ll_equal, assert_stream_in_order,
+                         combine_tolerance_check, log, pack_streams, run_hip_combine_ll, run_hip_ll)
 
 pytestmark = pytest.mark.gpu
 
@@ -31,7 +34,11 @@ def _check_case(T, H, E, R, k, fmt, inp, C, depth, mif, cap_extra=3, repeat=1, y
     assert_ll_equal(g, L, pk, Q)
     lg, nd = g["logs"][0]
     assert nd == repeat * len(want)
-    assert_stream_in_order(lg, want, C, calls=repeat)
+    if fused or not pack_streams(T, H, fmt):
+        assert_stream_in_order(lg, want, C, calls=repeat)
+    else:
+        assert repeat == 1
+        assert_ll_descriptors(lg, want, C, L["expert_offset"], E, R, oracle.row_bytes(H, fmt))
     if fmt == 0:
         y = W.make_expert_outputs(Q, H, y_seed)
         ref = oracle.ll_combine(y, idx, w, L["expert_slot"], H=H)
@@ -89,6 +96,70 @@ def test_ll_repeated_experts_and_repeat_calls():
     inp = dict(inp, topk_idx=idx)
     log("[ll] repeated experts, three calls")
     _check_case(T, H, E, R, k, 0, inp, 3, 16, 4, repeat=3)
+
+
+def test_ll_streaming_errors():
+    """Large-batch per-expert pack (streaming publication): a bad expert id
+    and a capacity shortfall publish nothing; expert_slot from another
+    layout is reported and no WRITE escapes; after a reset the ring carries a
+    correct dispatch."""
+    import combine_topk_rank_amd as ep
+    import torch
+    from gpu_helpers import dev, dev_bf16
+    rng = np.random.default_rng(41)
+    T, H, E, R, k, C = 2048, 512, 64, 8, 4, 4
+    assert pack_streams(T, H, 0)
+    inp = W.make_random_case(rng, T, H, E, R, k, drop_prob=0.1)
+    idx = inp["topk_idx"].copy()
+    idx[5, 0] = E
+    clean = idx.copy()
+    clean[5, 0] = -1
+    L = oracle.ll_layout(clean, E)
+    pk = oracle.ll_pack(inp["x"], inp["topk_w"], L["expert_slot"], 0, capacity_rows=T * k)
+    log("[ll] streaming pack after a bad expert id")
+    g = run_hip_ll(T, H, E, R, k, 0, inp["x"], idx, inp["topk_w"],
+                   ring_cfg=(1024, C, 256, RING_TIMEOUT_NS))
+    assert g["status"] == ep.EP_ERR_BAD_EXPERT
+    assert g["logs"][0][1] == 0
+    assert_ll_equal(g, L, pk, L["Q"])
+    L = oracle.ll_layout(inp["topk_idx"], E)
+    Q = L["Q"]
+    log("[ll] streaming pack, capacity shortfall")
+    g = run_hip_ll(T, H, E, R, k, 0, inp["x"], inp["topk_idx"], inp["topk_w"], capacity_rows=Q - 9,
+                   ring_cfg=(1024, C, 256, RING_TIMEOUT_NS))
+    assert g["status"] == ep.EP_ERR_CAPACITY
+    assert g["logs"][0][1] == 0
+    pk = oracle.ll_pack(inp["x"], inp["topk_w"], L["expert_slot"], 0, capacity_rows=Q - 9)
+    assert np.array_equal(g["send_buf"], pk["send_buf"])
+    log("[ll] streaming pack, expert_slot from another layout")
+    s = ep.shape(T, H, E, R, k)
+    b = ep.BuffersLL(s)
+    d_idx, d_w, d_x = dev(inp["topk_idx"]), dev(inp["topk_w"]), dev_bf16(inp["x"])
+    b.layout(d_idx)
+    torch.cuda.synchronize()
+    bad_slot = torch.flip(b.expert_slot, dims=[0]).contiguous()
+    ring = ep.Ring(1024, C, 256, RING_TIMEOUT_NS)
+    ring.proxy_start(2, 1 << 16)
+    ep.ep_dispatch_ll(s, d_x, d_idx, d_w, b.expert_offset, bad_slot, b.send_buf, b.slot_src,
+                      b.slot_w, ring, b.workspace, b.dev_status)
+    torch.cuda.synchronize()
+    lg, nd = ring.proxy_stop(1 << 16)
+    assert int(b.dev_status.item()) == ep.EP_ERR_INVALID_ARG
+    assert all(int(d["type"]) != 1 for d in lg)
+    log("[ll] reset, then a clean streaming dispatch on the same ring")
+    ring.reset()
+    ring.proxy_start(2, 1 << 16)
+    b.dev_status.zero_()
+    ep.ep_dispatch_ll(s, d_x, d_idx, d_w, b.expert_offset, b.expert_slot, b.send_buf, b.slot_src,
+                      b.slot_w, ring, b.workspace, b.dev_status)
+    torch.cuda.synchronize()
+    lg, nd = ring.proxy_stop(1 << 16)
+    assert int(b.dev_status.item()) == 0
+    want = oracle.ll_descriptors(L["num_tokens_per_expert"], L["expert_offset"], R,
+                                 oracle.row_bytes(H, 0), C)
+    assert nd == len(want)
+    assert_ll_descriptors(lg, want, C, L["expert_offset"], E, R, oracle.row_bytes(H, 0))
+    ring.destroy()
 
 
 def test_ll_capacity_and_inconsistent_rows():

@@ -178,14 +178,16 @@ int launch_combine(const CombineArgs& a, int64_t waves, hipStream_t stream) {
     return EP_OK;
 }
 
-// Large batches: 7 vectors per lane (two wavefronts per 7168-wide row), one
-// row in flight per wavefront (occupancy hides the latency; a second row's
-// registers would halve it).  Small batches (few wavefronts): 1-2 vectors per
-// lane and eight rows in flight, so each wavefront does not wait on its
-// token's rows one after another.
+// Large batches: rows wider than 512 vectors take 4 vectors per lane (four
+// wavefronts per 7168-wide row) with four rows in flight per wavefront; 7
+// vectors and one row in flight, 7 and two, 8 and one, 2 and four all
+// measured the same or slower (train 86-88 us, skewed 275 against 280-286 us).
+// Small batches (few wavefronts): 1-2 vectors per lane and eight rows in
+// flight, so each wavefront does not wait on its token's rows one after
+// another.
 template <bool LL>
 int launch_combine_any(CombineArgs& a, hipStream_t stream) {
-    const int vpl_big = a.nv <= 64 ? 1 : a.nv <= 128 ? 2 : a.nv <= 256 ? 4 : a.nv <= 512 ? 8 : 7;
+    const int vpl_big = a.nv <= 64 ? 1 : a.nv <= 128 ? 2 : a.nv <= 256 ? 4 : a.nv <= 512 ? 8 : 4;
     const int64_t waves_big = (int64_t)a.T * ceil_div(a.nv, (int64_t)vpl_big * kWave);
     if (waves_big < kCombineSmallWaves) {
         const int vpl = a.nv <= 64 ? 1 : 2;
@@ -199,9 +201,8 @@ int launch_combine_any(CombineArgs& a, hipStream_t stream) {
     switch (vpl_big) {
         case 1: return launch_combine<1, 4, LL>(a, waves, stream);
         case 2: return launch_combine<2, 4, LL>(a, waves, stream);
-        case 4: return launch_combine<4, 2, LL>(a, waves, stream);
-        case 8: return launch_combine<8, 1, LL>(a, waves, stream);
-        default: return launch_combine<7, 1, LL>(a, waves, stream);
+        case 4: return launch_combine<4, 4, LL>(a, waves, stream);
+        default: return launch_combine<8, 1, LL>(a, waves, stream);
     }
 }
 }  // namespace

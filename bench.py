@@ -572,6 +572,12 @@ def bench_workload(w, args, scratch, sink, dev) -> dict:
                              "traffic_source": traffic[1] if traffic else None,
                              "note": "algorithmic bytes of one launch / its mean duration from "
                                      "HIP events on the launch stream in the cold timed steps"}
+        if run.plan == run.ep.EP_FUSED_ONE_KERNEL_LARGE and prefix == "fused_large_kernel":
+            entry["roofline"]["note"] += (
+                "; this kernel is the routing layout and the pack in one launch, so its time "
+                "includes the layout's latency (about 14 us of id loads, ballots, a grid barrier "
+                "and a table read before the first row store): algorithmic bytes are the "
+                "layout's and the pack's")
 
     if run.graphs is None and args.flush_reps > 0:
         d, fevs = flushed_steps(run, args.flush_reps, scratch, sink)

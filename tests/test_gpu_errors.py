@@ -194,3 +194,45 @@ def test_streaming_inconsistent_slots():
     ring.reset()
     _clean_dispatch_on(ring, (T, H, E, R, k), inp)
     ring.destroy()
+
+
+@pytest.mark.parametrize("mode", ["rank-one-kernel", "per-expert-streaming"])
+def test_streaming_ring_timeout_without_consumer(mode):
+    """Large batches publish as messages complete; with no proxy and 4
+    commands in flight per channel, each channel takes exactly its first 4
+    commands, the other producers give up after the 2 ms timeout and report
+    it, and every row is still packed."""
+    import combine_topk_rank_amd as ep
+    from gpu_helpers import assert_ll_equal, pack_streams, run_hip_ll
+    rng = np.random.default_rng(61)
+    if mode == "rank-one-kernel":
+        T, H, E, R, k = 2048, 2048, 64, 8, 4
+        assert ep.ep_dispatch_fused_plan(ep.shape(T, H, E, R, k)) == ep.EP_FUSED_ONE_KERNEL_LARGE
+    else:
+        T, H, E, R, k = 2048, 512, 64, 8, 4
+        assert pack_streams(T, H, 0)
+    inp = W.make_random_case(rng, T, H, E, R, k)
+    log(f"[errors] {mode}: ring timeout (no consumer, 2 ms)")
+    if mode == "rank-one-kernel":
+        L = oracle.layout(inp["topk_idx"], E, R)
+        pk = oracle.pack(inp["x"], inp["topk_idx"], inp["topk_w"], L["send_slot"], E, R, 0,
+                         capacity_rows=T * min(k, R))
+        g = run_hip(T, H, E, R, k, 0, inp["x"], inp["topk_idx"], inp["topk_w"],
+                    ring_cfg=(64, 2, 4, 2_000_000), proxy_threads=0, fused=True)
+        assert_layout_equal(g, L)
+        assert_pack_equal(g, pk, L["P"])
+    else:
+        L = oracle.ll_layout(inp["topk_idx"], E)
+        pk = oracle.ll_pack(inp["x"], inp["topk_w"], L["expert_slot"], 0, capacity_rows=T * k)
+        g = run_hip_ll(T, H, E, R, k, 0, inp["x"], inp["topk_idx"], inp["topk_w"],
+                       ring_cfg=(64, 2, 4, 2_000_000), proxy_threads=0)
+        assert_ll_equal(g, L, pk, L["Q"])
+    assert g["status"] == ep.EP_ERR_RING_TIMEOUT
+    ring = g["ring"]
+    for c in range(2):
+        got = ring.drain(c)
+        assert len(got) == 4, (c, len(got))
+        assert [int(d["seq"]) for d in got] == [1, 2, 3, 4]
+    ring.reset()
+    assert len(ring.drain(0)) == 0 and len(ring.drain(1)) == 0
+    ring.destroy()

@@ -185,3 +185,35 @@ def test_fused_errors(name):
     assert g["logs"][0][1] == 0
     assert_layout_equal(g, L)
     assert_pack_equal(g, pk, cap)
+
+
+# one-kernel large path at its edges: (T, H, E, R, k, drop_prob, channels)
+LARGE_EDGES = [
+    (32768, 1032, 4, 2, 1, 0.0, 2),     # 2048 groups on 128 workgroups: 16 passes, the maximum
+    (4095, 4104, 7, 7, 3, 0.2, 3),      # one expert per rank, R not a power of two, ragged T
+    (1025, 2048, 1, 1, 1, 0.5, 1),      # one rank, half the choices dropped, one token past 1024
+    (6000, 7168, 64, 64, 1, 0.0, 8),    # k = 1, 64 ranks
+]
+
+
+@pytest.mark.parametrize("case", LARGE_EDGES, ids=lambda c: "T%d_H%d_E%d_R%d_k%d" % c[:5])
+def test_fused_large_edges(case):
+    import combine_topk_rank_amd as ep
+    T, H, E, R, k, drop, C = case
+    assert ep.ep_dispatch_fused_plan(ep.shape(T, H, E, R, k)) == ep.EP_FUSED_ONE_KERNEL_LARGE
+    rng = np.random.default_rng(7000 + LARGE_EDGES.index(case))
+    inp = W.make_random_case(rng, T, H, E, R, k, drop_prob=drop)
+    L = oracle.layout(inp["topk_idx"], E, R)
+    P = L["P"]
+    pk = oracle.pack(inp["x"], inp["topk_idx"], inp["topk_w"], L["send_slot"], E, R, 0,
+                     capacity_rows=P + 3)
+    want = oracle.descriptors(L["num_tokens_per_rank"], L["rank_offset"], oracle.row_bytes(H, 0), C)
+    log(f"[fused] one-kernel large edge case {case}: P={P}")
+    g = run_hip(T, H, E, R, k, 0, inp["x"], inp["topk_idx"], inp["topk_w"], capacity_rows=P + 3,
+                ring_cfg=(1024, C, 256, RING_TIMEOUT_NS), fused=True)
+    _check_stream(g, L, pk, want, C)
+    y = W.make_expert_outputs(P, H, 5)
+    ref = oracle.combine(y, inp["topk_idx"], inp["topk_w"], L["send_slot"], E, R, H=H)
+    got, st = run_hip_combine(g["buffers"], y, g["d_idx"], g["d_w"])
+    assert st == 0
+    combine_tolerance_check(got, ref, f"one-kernel large edge {case}")

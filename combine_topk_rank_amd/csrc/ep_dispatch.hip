@@ -31,6 +31,8 @@
 // in closed form: the last workgroup to finish emits every command from the
 // per-rank counts.
 
+#include <atomic>
+
 #include "ep_common.h"
 #include "ep_route.h"
 
@@ -1866,7 +1868,10 @@ using namespace ep;
 namespace {
 
 int64_t pack_grid_cap() {
-    static int64_t cap = 0;   // per process; the library targets one GPU model
+    // per process (the library targets one GPU model); threads that race to
+    // fill it compute the same value
+    static std::atomic<int64_t> cached{0};
+    int64_t cap = cached.load(std::memory_order_relaxed);
     if (cap == 0) {
         int dev = 0, cus = 0;
         if (hipGetDevice(&dev) != hipSuccess ||
@@ -1875,6 +1880,7 @@ int64_t pack_grid_cap() {
             cus = 256;
         cap = (int64_t)cus * kPackGridPerCuNum / kPackGridPerCuDen;
         if (cap < 1) cap = 1;
+        cached.store(cap, std::memory_order_relaxed);
     }
     return cap;
 }
@@ -2010,7 +2016,7 @@ int launch_fused(PackArgs& a, int fmt, hipStream_t stream) {
 // kFusedLargeMaxPasses groups per workgroup, and room for every workgroup
 // (plus the expert one) at once.  kNotTaken when the batch does not qualify;
 // nothing is launched then.
-constexpr int kNotTaken = 1;
+constexpr int kNotTaken = -1;   // no status code is negative
 
 template <typename K>
 int64_t resident_blocks(K kernel, int threads) {
@@ -2030,14 +2036,18 @@ int launch_fused_large_fmt(PackArgs a, hipStream_t stream, bool dry) {
     const int64_t passes = ceil_div(a.ngroups, cap);
     const int64_t blocks = ceil_div(a.ngroups, passes);
     if (passes > kFusedLargeMaxPasses) return kNotTaken;
-    static int64_t room[2] = {-1, -1};   // per process and ring mode; one GPU model
+    // per process and ring mode (one GPU model); racing threads compute the
+    // same value
+    static std::atomic<int64_t> room[2] = {{-1}, {-1}};
     const int pub = a.has_ring ? kPubStream : kPubNone;
-    int64_t& rm = room[a.has_ring ? 1 : 0];
-    if (rm < 0)
+    int64_t rm = room[a.has_ring ? 1 : 0].load(std::memory_order_relaxed);
+    if (rm < 0) {
         rm = a.has_ring ? resident_blocks(fused_large_kernel<VPL, FMT, WAVES, kPubStream>,
                                           WAVES * kWave)
                         : resident_blocks(fused_large_kernel<VPL, FMT, WAVES, kPubNone>,
                                           WAVES * kWave);
+        room[a.has_ring ? 1 : 0].store(rm, std::memory_order_relaxed);
+    }
     if (blocks + 1 > rm) return kNotTaken;
     if (dry) return EP_OK;
     a.npass = (int32_t)passes;

@@ -22,6 +22,8 @@
 // tiles: it sums the tiles' expert histograms and scans them, in parallel
 // with the tiles' slot stores, so no tile carries the expert work.
 
+#include <atomic>
+
 #include "ep_common.h"
 #include "ep_route.h"
 
@@ -458,19 +460,23 @@ __global__ __launch_bounds__(kWave) void ll_slot_kernel(
 // Tiles of the one-kernel layout that can be resident at once on the current
 // device (workgroups per CU from the occupancy calculator x CUs), or 0.
 int64_t max_resident_layout_tiles() {
-    static int64_t cached = -1;   // per process; the library targets one GPU model
-    if (cached < 0) {
+    // per process (the library targets one GPU model); threads that race to
+    // fill it compute the same value
+    static std::atomic<int64_t> cached{-1};
+    int64_t v = cached.load(std::memory_order_relaxed);
+    if (v < 0) {
         int dev = 0, cus = 0, per_cu = 0;
         if (hipGetDevice(&dev) == hipSuccess &&
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
             hipOccupancyMaxActiveBlocksPerMultiprocessor(
                 &per_cu, reinterpret_cast<const void*>(layout_main_kernel<2>), kBlock, 0) ==
                 hipSuccess)
-            cached = (int64_t)cus * per_cu;
+            v = (int64_t)cus * per_cu;
         else
-            cached = 0;
+            v = 0;
+        cached.store(v, std::memory_order_relaxed);
     }
-    return cached;
+    return v;
 }
 
 }  // namespace ep

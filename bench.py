@@ -81,11 +81,11 @@ def algorithmic_bytes(w, P: int) -> dict:
 
 def algorithmic_bytes_ll(w, Q: int) -> dict:
     """Per-expert mode: one row per kept choice (Q rows), each input read
-    once and each output written once."""
+    once and each output written once.  Its layout needs no rank outputs:
+    read the ids, write the expert counts and offsets and the row table."""
     T, H, E, R, k = w.T, w.H, w.E, w.R, w.k
     rb = row_bytes(H, w.fmt)
-    base = algorithmic_bytes(w, 0)
-    layout = base["layout"] + 4 * T * k + 4 * T * k    # + row table: read idx, write slots
+    layout = 4 * T * k + 4 * (2 * E + 1) + 4 * T * k
     pack_r = 2 * T * H + 8 * T * k + 4 * T * k + 4 * (E + 1)
     pack_w = Q * rb + Q * 8
     comb_r = 2 * Q * H + 8 * T * k + 4 * T * k
@@ -248,6 +248,9 @@ class Runner:
         s = ep.shape(w.T, w.H, w.E, w.R, w.k, w.fmt)
         self.shape = s
         self.plan = ep.ep_dispatch_fused_plan(s) if (self.fused and not self.ll) else None
+        # per-expert layout in one kernel (ep_dispatch_ll_layout) where it takes
+        # the shape (E <= 1024, every tile resident); the first call finds out
+        self.ll_one = self.ll and not self.fused and w.E <= 1024
         self.stream = torch.cuda.current_stream()
         x0 = torch.from_numpy(inp["x"].view(np.int16)).to(dev).view(torch.bfloat16)
         i0 = torch.from_numpy(inp["topk_idx"]).to(dev)
@@ -285,8 +288,17 @@ class Runner:
         if self.fused:
             b.dispatch_fused(st["x"], st["idx"], st["w"], ring=ring, stream=stream)
         else:
-            b.layout(st["idx"], stream)
+            self._layout(st, stream)
             b.dispatch(st["x"], st["idx"], st["w"], ring=ring, stream=stream)
+
+    def _layout(self, st, stream):
+        if self.ll_one:
+            try:
+                st["b"].layout_one_call(st["idx"], stream)
+                return
+            except self.ep.EpError:
+                self.ll_one = False   # rejected on the host, nothing enqueued
+        st["b"].layout(st["idx"], stream)
 
     def _set_loopback(self):
         """Receive regions per rank for set 0 (loopback runs on one set)."""
@@ -344,7 +356,7 @@ class Runner:
         if ev is not None:
             ev[0].record(s)
         if not self.fused:
-            b.layout(st["idx"], s)
+            self._layout(st, s)
         if ev is not None:
             ev[1].record(s)
         if self.fused:

@@ -20,6 +20,8 @@ The functions keep the C names:
     ep_dispatch_fused_noalloc(shape, x, topk_idx, topk_w, <layout outputs>, send_buf,
                               slot_src, slot_local_idx, slot_local_w, ring, dev_status,
                               stream=None, clear_scratch=False)
+    ep_dispatch_ll_layout(shape, topk_idx, num_tokens_per_expert, expert_offset, expert_slot,
+                          workspace, dev_status, stream=None)
     ep_combine(shape, y, topk_idx, topk_w, send_slot, out, dev_status, stream=None)
         (y_rows is y.shape[0])
     Ring(depth, channels, max_inflight, timeout_ns)   # ep_ring_* calls
@@ -110,6 +112,8 @@ def _load() -> ctypes.CDLL:
     L.ep_combine.restype = ctypes.c_int
     L.ep_dispatch_layout_ll.argtypes = [S, P, P, P, P, sz, P, P]
     L.ep_dispatch_layout_ll.restype = ctypes.c_int
+    L.ep_dispatch_ll_layout.argtypes = [S, P, P, P, P, P, sz, P, P]
+    L.ep_dispatch_ll_layout.restype = ctypes.c_int
     L.ep_dispatch_ll.argtypes = [S, P, P, P, P, P, P, i64, P, P, P, P, sz, P, P]
     L.ep_dispatch_ll.restype = ctypes.c_int
     L.ep_dispatch_ll_fused.argtypes = [S, P, P, P, P, P, P, P, i64, P, P, P, P, sz, P, P]
@@ -267,6 +271,15 @@ def ep_dispatch_layout_ll(s, topk_idx, expert_offset, expert_slot, workspace, de
                                    workspace.numel() * workspace.element_size(),
                                    _ptr(dev_status), _stream(stream))
     _check(st, "ep_dispatch_layout_ll")
+
+
+def ep_dispatch_ll_layout(s, topk_idx, num_tokens_per_expert, expert_offset, expert_slot,
+                          workspace, dev_status, stream=None) -> None:
+    st = lib.ep_dispatch_ll_layout(ctypes.byref(s), _ptr(topk_idx), _ptr(num_tokens_per_expert),
+                                   _ptr(expert_offset), _ptr(expert_slot), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(),
+                                   _ptr(dev_status), _stream(stream))
+    _check(st, "ep_dispatch_ll_layout")
 
 
 def ep_dispatch_ll(s, x, topk_idx, topk_w, expert_offset, expert_slot, send_buf, slot_src,
@@ -474,6 +487,13 @@ class BuffersLL(Buffers):
         super().layout(topk_idx, stream)
         ep_dispatch_layout_ll(self.shape, topk_idx, self.expert_offset, self.expert_slot,
                               self.workspace, self.dev_status, stream)
+
+    def layout_one_call(self, topk_idx, stream=None):
+        """the per-expert layout in one kernel (ep_dispatch_ll_layout; E <=
+        1024); the rank-layout buffers are left untouched"""
+        ep_dispatch_ll_layout(self.shape, topk_idx, self.num_tokens_per_expert,
+                              self.expert_offset, self.expert_slot, self.workspace,
+                              self.dev_status, stream)
 
     def dispatch(self, x, topk_idx, topk_w, ring=None, stream=None):
         ep_dispatch_ll(self.shape, x, topk_idx, topk_w, self.expert_offset, self.expert_slot,

@@ -457,6 +457,194 @@ __global__ __launch_bounds__(kWave) void ll_slot_kernel(
     }
 }
 
+// ------------------------------------------------ per-expert layout, one kernel
+// Counts, offsets and the row table of the per-expert mode in one launch
+// (the rank layout is not needed there).  Tiles of 256 tokens, one wavefront
+// per 64 tokens, E <= kLLLayoutMaxE:
+//   1. each wavefront counts its choices per expert in LDS; the tile stores
+//      its histogram to a [NB, E] table;
+//   2. grid barrier (every tile resident);
+//   3. every tile sums the table's columns: the expert totals (their
+//      exclusive scan is expert_offset) and the rows of each expert in the
+//      earlier tiles;
+//   4. a choice's row is expert_offset[e] + (earlier tiles) + (earlier
+//      wavefronts of the tile) + (earlier choices of e in its wavefront, in
+//      (t, j) order), the last from per-wavefront LDS masks as in
+//      ll_slot_kernel.
+// Integer counts only: the rows do not depend on scheduling order.
+constexpr int kLLLayoutMaxE = 1024;
+
+template <int KMAX>
+__global__ __launch_bounds__(kBlock) void ll_layout_kernel(
+    const int32_t* __restrict__ idx, int T, int E, int k, int nblocks,
+    int32_t* __restrict__ blk_exp_cnt, int32_t* __restrict__ cnt_exp,
+    int32_t* __restrict__ exp_off, int32_t* __restrict__ expert_slot,
+    int32_t* __restrict__ counters, int64_t counters_n, uint32_t* __restrict__ bar,
+    int32_t* st) {
+    constexpr int kW = kBlock / kWave;
+    __shared__ int32_t s_whist[kW][kLLLayoutMaxE];             // choices per expert, per wavefront
+    __shared__ unsigned long long s_mask[kW][kLLLayoutMaxE];   // one round's lanes per expert
+    __shared__ int32_t s_base[kLLLayoutMaxE];                  // offset + earlier tiles
+    __shared__ int32_t s_tot[kLLLayoutMaxE];
+    __shared__ int32_t s_wsum[kW];
+    __shared__ int s_rounds;
+    const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+    const int b = blockIdx.x;
+    uint32_t gen = 0;
+    if (tid == 0) gen = grid_barrier_generation(bar);
+    // this lane's token: its choices, all loads issued first
+    const int64_t t = (int64_t)b * kLayoutTile + tid;
+    int32_t ids[KMAX];
+    {
+        const int32_t* row = idx + t * k;
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) ids[j] = (j < k && t < T) ? row[j] : -1;
+    }
+    for (int e = lane; e < E; e += kWave) {
+        s_whist[wave][e] = 0;
+        s_mask[wave][e] = 0ull;
+    }
+    if (tid == 0) s_rounds = 0;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+        if (ids[j] < -1 || ids[j] >= E) {
+            set_error(st, EP_ERR_BAD_EXPERT);
+            ids[j] = -1;
+        }
+    // occurrence of each choice among the token's earlier choices
+    int32_t occ[KMAX];
+    int my_rounds = 0;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+        int o = 0;
+#pragma unroll
+        for (int i = 0; i < j; ++i) o += (ids[i] == ids[j]) ? 1 : 0;
+        occ[j] = o;
+        if (ids[j] >= 0 && o + 1 > my_rounds) my_rounds = o + 1;
+    }
+    __syncthreads();
+    if (my_rounds) atomicMax(&s_rounds, my_rounds);
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+        if (ids[j] >= 0) atomicAdd(&s_whist[wave][ids[j]], 1);
+    __syncthreads();
+    // 1. the tile's histogram for the others; the dispatch's counters start at zero
+    for (int e = tid; e < E; e += kBlock) {
+        int32_t c = 0;
+#pragma unroll
+        for (int w = 0; w < kW; ++w) c += s_whist[w][e];
+        blk_exp_cnt[(int64_t)b * E + e] = c;
+    }
+    zero_counters(counters, counters_n, (int64_t)b * kBlock + tid, (int64_t)gridDim.x * kBlock);
+    // 2. every tile's histogram is in the table after this
+    if (!grid_barrier<false>(bar, (uint32_t)gridDim.x, st, gen)) return;
+    // 3. column sums: totals, and the rows in earlier tiles
+    constexpr int kRows = 16;
+    for (int e = tid; e < E; e += kBlock) {
+        int32_t tot = 0, pre = 0;
+        for (int r0 = 0; r0 < nblocks; r0 += kRows) {
+            int32_t q[kRows];
+#pragma unroll
+            for (int u = 0; u < kRows; ++u)
+                q[u] = r0 + u < nblocks ? blk_exp_cnt[(int64_t)(r0 + u) * E + e] : 0;
+#pragma unroll
+            for (int u = 0; u < kRows; ++u) {
+                tot += q[u];
+                pre += r0 + u < b ? q[u] : 0;
+            }
+        }
+        s_tot[e] = tot;
+        s_base[e] = pre;
+    }
+    __syncthreads();
+    // exclusive scan of the totals: thread tid takes a run of `per` experts
+    {
+        const int per = (E + kBlock - 1) / kBlock;
+        const int e0 = tid * per;
+        int32_t sum = 0;
+        for (int i = 0; i < per; ++i)
+            if (e0 + i < E) sum += s_tot[e0 + i];
+        int32_t incl = sum;
+        for (int d = 1; d < kWave; d <<= 1) {
+            const int32_t v = __shfl_up(incl, d);
+            if (lane >= d) incl += v;
+        }
+        if (lane == kWave - 1) s_wsum[wave] = incl;
+        __syncthreads();
+        int32_t run = incl - sum;
+        for (int w = 0; w < wave; ++w) run += s_wsum[w];
+        for (int i = 0; i < per; ++i) {
+            const int e = e0 + i;
+            if (e < E) {
+                if (b == 0) {
+                    cnt_exp[e] = s_tot[e];
+                    exp_off[e] = run;
+                }
+                s_base[e] += run;
+                run += s_tot[e];
+            }
+        }
+        if (b == 0 && tid == kBlock - 1) exp_off[E] = run;
+    }
+    __syncthreads();
+    // 4. rows: base + earlier wavefronts of the tile + earlier lanes (rounds
+    // by occurrence, as in ll_slot_kernel) + earlier choices of the token
+    int32_t pos[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+        pos[j] = occ[j];
+        if (ids[j] >= 0) {
+            int32_t p = s_base[ids[j]];
+            for (int w = 0; w < wave; ++w) p += s_whist[w][ids[j]];
+            pos[j] += p;
+        }
+    }
+    const unsigned long long below = (1ull << lane) - 1ull;
+    const int rounds = s_rounds;
+    for (int o = 0; o < rounds; ++o) {
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j)
+            if (ids[j] >= 0 && occ[j] == o) atomicOr(&s_mask[wave][ids[j]], 1ull << lane);
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j)
+            if (ids[j] >= 0) pos[j] += __popcll(s_mask[wave][ids[j]] & below);
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j)
+            if (ids[j] >= 0) s_mask[wave][ids[j]] = 0ull;
+        __syncthreads();
+    }
+    if (t < T) {
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) {
+            if (j >= k) break;
+            expert_slot[t * k + j] = ids[j] >= 0 ? pos[j] : -1;
+        }
+    }
+}
+
+// Tiles of the one-kernel per-expert layout that can be resident at once (per
+// process; threads that race to fill it compute the same value), or 0.
+template <int KMAX>
+int64_t max_resident_ll_tiles() {
+    static std::atomic<int64_t> cached{-1};
+    int64_t v = cached.load(std::memory_order_relaxed);
+    if (v < 0) {
+        int dev = 0, cus = 0, per_cu = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &per_cu, reinterpret_cast<const void*>(ll_layout_kernel<KMAX>), kBlock, 0) ==
+                hipSuccess)
+            v = (int64_t)cus * per_cu;
+        else
+            v = 0;
+        cached.store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
 // Tiles of the one-kernel layout that can be resident at once on the current
 // device (workgroups per CU from the occupancy calculator x CUs), or 0.
 int64_t max_resident_layout_tiles() {
@@ -544,6 +732,43 @@ extern "C" int ep_dispatch_layout_ll(const ep_shape_t* shape, const int32_t* top
     hipLaunchKernelGGL(ll_slot_kernel, dim3((unsigned)ceil_div(s.T, kWave)), dim3(kWave), 0, stream,
                        topk_idx, s.T, s.E, s.k, w.blk_exp_cnt, expert_offset, expert_slot,
                        dev_status);
+    EP_HIP_CHECK(hipGetLastError());
+    return EP_OK;
+}
+
+extern "C" int ep_dispatch_ll_layout(const ep_shape_t* shape, const int32_t* topk_idx,
+                                     int32_t* num_tokens_per_expert, int32_t* expert_offset,
+                                     int32_t* expert_slot, void* workspace, size_t ws_bytes,
+                                     int32_t* dev_status, hipStream_t stream) {
+    int v = validate_shape(shape);
+    if (v != EP_OK) return v;
+    const ep_shape_t s = *shape;
+    if (!num_tokens_per_expert || !expert_offset || !dev_status || !workspace)
+        return EP_ERR_INVALID_ARG;
+    if (s.T > 0 && (!topk_idx || !expert_slot)) return EP_ERR_INVALID_ARG;
+    if (ws_bytes < workspace_bytes(s)) return EP_ERR_INVALID_ARG;
+    if (s.E > kLLLayoutMaxE) {
+        record_error("ep_dispatch_ll_layout: E > 1024 (use ep_dispatch_layout + ep_dispatch_layout_ll)");
+        return EP_ERR_INVALID_ARG;
+    }
+    Workspace w = carve_workspace(s, workspace);
+    const int nb = w.layout_blocks;
+    const bool small_k = s.k <= 8;
+    const int64_t room = small_k ? max_resident_ll_tiles<8>() : max_resident_ll_tiles<kMaxK>();
+    if (nb > room) {
+        record_error("ep_dispatch_ll_layout: more tiles than the device holds at once (use "
+                     "ep_dispatch_layout + ep_dispatch_layout_ll)");
+        return EP_ERR_INVALID_ARG;
+    }
+    clear_hip_error();
+    if (small_k)
+        hipLaunchKernelGGL(ll_layout_kernel<8>, dim3(nb), dim3(kBlock), 0, stream, topk_idx, s.T,
+                           s.E, s.k, nb, w.blk_exp_cnt, num_tokens_per_expert, expert_offset,
+                           expert_slot, w.msg_arrivals, w.counters_n, w.barrier, dev_status);
+    else
+        hipLaunchKernelGGL(ll_layout_kernel<kMaxK>, dim3(nb), dim3(kBlock), 0, stream, topk_idx,
+                           s.T, s.E, s.k, nb, w.blk_exp_cnt, num_tokens_per_expert, expert_offset,
+                           expert_slot, w.msg_arrivals, w.counters_n, w.barrier, dev_status);
     EP_HIP_CHECK(hipGetLastError());
     return EP_OK;
 }

@@ -282,9 +282,28 @@ int ep_dispatch_layout_ll(const ep_shape_t* shape, const int32_t* topk_idx,
                           void* workspace, size_t workspace_bytes,
                           int32_t* dev_status, hipStream_t stream);
 
+/* The whole per-expert layout in one call, without the rank layout: the
+ * outputs num_tokens_per_expert [E] and expert_offset [E+1] of
+ * ep_dispatch_layout and expert_slot [T,k] of ep_dispatch_layout_ll, with the
+ * same meanings and device errors (EP_ERR_BAD_EXPERT: the entry is treated as
+ * dropped; EP_ERR_TIMEOUT: the tiles did not all become resident within a
+ * second).  One kernel: tiles of 256 tokens count their choices per expert,
+ * meet at a grid barrier, and each derives its rows from the tiles' counts.
+ * UCCL-EP s4.1 (low-latency mode: tokens go per expert).  Only for
+ * E <= 1024 and as many tiles as the device holds at once (ceil(T/256) up to a
+ * few hundred on MI355X); otherwise EP_ERR_INVALID_ARG with nothing enqueued
+ * (ep_last_error says why) and ep_dispatch_layout + ep_dispatch_layout_ll
+ * serve.  Leaves the workspace ready for ep_dispatch_ll. */
+int ep_dispatch_ll_layout(const ep_shape_t* shape, const int32_t* topk_idx,
+                          int32_t* num_tokens_per_expert, int32_t* expert_offset,
+                          int32_t* expert_slot, void* workspace, size_t workspace_bytes,
+                          int32_t* dev_status, hipStream_t stream);
+
 /* Per-expert pack and descriptors.  Row expert_slot[t,j] of send_buf gets
  * x[t] (bf16, or its fp8 row as in ep_dispatch); metadata slot_src[s] = t and
- * slot_w[s] = w[t,j] (the gate of that choice).
+ * slot_w[s] = w[t,j] (the gate of that choice).  Must follow the per-expert
+ * layout (ep_dispatch_layout + ep_dispatch_layout_ll, or
+ * ep_dispatch_ll_layout) on the same stream with the same workspace.
  *   send_buf [capacity_rows, row bytes], 16-byte aligned; capacity_rows >= Q
  *   slot_src int32 [capacity_rows], slot_w float [capacity_rows]
  *   ring     may be NULL.  Otherwise, per expert e on rank r = e / (E/R), its

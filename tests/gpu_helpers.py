@@ -235,10 +235,12 @@ def combine_tolerance_check(got, ref, what=""):
 
 
 def run_hip_ll(T, H, E, R, k, fmt, x, idx, w, capacity_rows=None, ring_cfg=None,
-               proxy_threads=4, poison=POISON, log_capacity=1 << 20, repeat=1, fused=False):
+               proxy_threads=4, poison=POISON, log_capacity=1 << 20, repeat=1, fused=False,
+               one_call_layout=False):
     """Per-expert mode through the C ABI: rank layout + per-expert row table +
     per-expert pack (and descriptors when ring_cfg is given); fused: the
-    one-call ep_dispatch_ll_fused."""
+    one-call ep_dispatch_ll_fused; one_call_layout: the layout by
+    ep_dispatch_ll_layout, then the pack."""
     import combine_topk_rank_amd as ep
     torch = torch_mod()
     s = ep.shape(T, H, E, R, k, fmt)
@@ -261,7 +263,10 @@ def run_hip_ll(T, H, E, R, k, fmt, x, idx, w, capacity_rows=None, ring_cfg=None,
         if fused:
             buf.dispatch_fused(d_x, d_idx, d_w, ring=ring)
         else:
-            buf.layout(d_idx)
+            if one_call_layout:
+                buf.layout_one_call(d_idx)
+            else:
+                buf.layout(d_idx)
             buf.dispatch(d_x, d_idx, d_w, ring=ring)
         torch.cuda.synchronize()
     if ring is not None and proxy_threads:

@@ -113,6 +113,14 @@ def test_host_validation_rejects_without_launch(ep):
                                       1 << 30, 16, None) == 1
     assert L.ep_dispatch_ll_fused(ctypes.byref(good), *([None] * 6), None, 0, None, None, None,
                                   None, 0, None, None) == 1
+    # one-call per-expert layout: bad shape, E beyond its bound, null outputs, short workspace
+    assert L.ep_dispatch_ll_layout(ctypes.byref(bad), 16, 16, 16, 16, 16, 1 << 20, 16, None) == 1
+    assert L.ep_dispatch_ll_layout(ctypes.byref(ep.shape(16, 64, 2048, 4, 2)), 16, 16, 16, 16, 16,
+                                   1 << 30, 16, None) == 1
+    assert b"E > 1024" in L.ep_last_error()
+    assert L.ep_dispatch_ll_layout(ctypes.byref(good), 16, None, 16, 16, 16, 1 << 20, 16,
+                                   None) == 1
+    assert L.ep_dispatch_ll_layout(ctypes.byref(good), 16, 16, 16, 16, 16, 0, 16, None) == 1
     # T = 0 combine is a no-op
     zero = ep.shape(0, 64, 16, 4, 2)
     assert L.ep_combine(ctypes.byref(zero), None, 0, None, None, None, None, 16, None) == 0

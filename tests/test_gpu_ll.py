@@ -21,7 +21,7 @@ RING_TIMEOUT_NS = 5_000_000_000
 
 
 def _check_case(T, H, E, R, k, fmt, inp, C, depth, mif, cap_extra=3, repeat=1, y_seed=7,
-                fused=False):
+                fused=False, one_call_layout=False):
     idx, w, x = inp["topk_idx"], inp["topk_w"], inp["x"]
     L = oracle.ll_layout(idx, E)
     Q = L["Q"]
@@ -29,7 +29,8 @@ def _check_case(T, H, E, R, k, fmt, inp, C, depth, mif, cap_extra=3, repeat=1, y
     want = oracle.ll_descriptors(L["num_tokens_per_expert"], L["expert_offset"], R,
                                  oracle.row_bytes(H, fmt), C)
     g = run_hip_ll(T, H, E, R, k, fmt, x, idx, w, capacity_rows=Q + cap_extra,
-                   ring_cfg=(depth, C, mif, RING_TIMEOUT_NS), repeat=repeat, fused=fused)
+                   ring_cfg=(depth, C, mif, RING_TIMEOUT_NS), repeat=repeat, fused=fused,
+                   one_call_layout=one_call_layout)
     assert g["status"] == 0, g["status"]
     assert_ll_equal(g, L, pk, Q)
     lg, nd = g["logs"][0]
@@ -82,6 +83,59 @@ def test_ll_random_case_parity(case):
     inp = W.make_random_case(rng, T, H, E, R, k, drop_prob=drop)
     log(f"[ll] case {case}")
     _check_case(T, H, E, R, k, fmt, inp, C, depth, mif)
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "train", "fp8", "skewed"])
+def test_ll_one_call_layout_workloads(name):
+    """ep_dispatch_ll_layout (counts, offsets and row table in one kernel),
+    then the per-expert pack: the same checks as the three-call path."""
+    w = W.WORKLOADS[name]
+    inp = pins.workload_inputs(name)
+    log(f"[ll] one-call layout, workload {name}")
+    _check_case(w.T, w.H, w.E, w.R, w.k, w.fmt, inp, w.channels, w.depth, w.max_inflight,
+                one_call_layout=True)
+
+
+@pytest.mark.parametrize("case", [c for c in LL_CASES if c[2] <= 1024] +
+                         [(600, 128, 1024, 64, 32, 0, 0.05, 8, 1024, 256),
+                          (5000, 256, 512, 16, 8, 1, 0.1, 8, 1024, 256)],
+                         ids=lambda c: "T%d_H%d_E%d_R%d_k%d_f%d" % c[:6])
+def test_ll_one_call_layout_cases(case):
+    T, H, E, R, k, fmt, drop, C, depth, mif = case
+    rng = np.random.default_rng(3100 + T + E)
+    inp = W.make_random_case(rng, T, H, E, R, k, drop_prob=drop)
+    if T > 0 and k > 1:
+        idx = inp["topk_idx"].copy()
+        idx[::5, 1] = idx[::5, 0]   # repeated experts: one row per choice
+        inp = dict(inp, topk_idx=idx)
+    log(f"[ll] one-call layout, case {case}")
+    _check_case(T, H, E, R, k, fmt, inp, C, depth, mif, one_call_layout=True)
+
+
+def test_ll_one_call_layout_bad_expert():
+    """A bad id is reported and treated as dropped; the rest of the table is
+    the oracle's."""
+    import combine_topk_rank_amd as ep
+    import torch
+    from gpu_helpers import dev, host
+    rng = np.random.default_rng(9)
+    T, H, E, R, k = 1500, 64, 96, 8, 6
+    inp = W.make_random_case(rng, T, H, E, R, k)
+    idx = inp["topk_idx"].copy()
+    idx[3, 2] = E
+    idx[1400, 0] = -4
+    clean = idx.copy()
+    clean[3, 2] = clean[1400, 0] = -1
+    L = oracle.ll_layout(clean, E)
+    b = ep.BuffersLL(ep.shape(T, H, E, R, k))
+    b.expert_slot.fill_(-99)
+    log("[ll] one-call layout with bad expert ids")
+    b.layout_one_call(dev(idx))
+    torch.cuda.synchronize()
+    assert int(b.dev_status.item()) == ep.EP_ERR_BAD_EXPERT
+    for key, got in (("num_tokens_per_expert", b.num_tokens_per_expert),
+                     ("expert_offset", b.expert_offset), ("expert_slot", b.expert_slot)):
+        assert np.array_equal(host(got), L[key]), key
 
 
 def test_ll_repeated_experts_and_repeat_calls():

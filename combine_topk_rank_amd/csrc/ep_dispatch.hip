@@ -251,20 +251,24 @@ __device__ inline void load_rank_view(const PackArgs& a, RankView& v) {
 // Up to N commands per lane, command i on its own channel c[i] (those with
 // bit i of `have`): as ring_publish_n, each command written as soon as its ticket is
 // inside its channel's window, so no command of the wavefront waits for
-// another of the same wavefront.  System-scope slot stores.
+// another of the same wavefront.  System-scope slot stores.  `seen0`, when
+// not NULL, holds the cached consumer position of each command's channel as
+// the caller already loaded it.
 template <int N>
 __device__ void ring_publish_v(const RingDev& g, uint32_t have, const int* c,
-                               const unsigned long long* ticket, const RingCmd* cmd, int32_t* st) {
+                               const unsigned long long* ticket, const RingCmd* cmd, int32_t* st,
+                               const unsigned long long* seen0 = nullptr) {
     if (!__ballot(have != 0)) return;
     const unsigned long long lim = (unsigned long long)g.max_inflight;
     unsigned long long seen[N];
     uint32_t pending = have;
 #pragma unroll
     for (int i = 0; i < N; ++i)
-        seen[i] = ((pending >> i) & 1u) ? __hip_atomic_load(g.tail_cache + (size_t)c[i] * kPad,
-                                                            __ATOMIC_RELAXED,
-                                                            __HIP_MEMORY_SCOPE_AGENT)
-                                        : 0ull;
+        seen[i] = !((pending >> i) & 1u) ? 0ull
+                  : seen0                ? seen0[i]
+                                         : __hip_atomic_load(g.tail_cache + (size_t)c[i] * kPad,
+                                                             __ATOMIC_RELAXED,
+                                                             __HIP_MEMORY_SCOPE_AGENT);
     bool polled = false;
     unsigned long long t0 = 0;
     while (__ballot(pending != 0)) {
@@ -1506,9 +1510,12 @@ __device__ void ll_publish_empty(const PackArgs& a, const int32_t* eo) {
 // The W * k pairs go in rounds of 128, two per lane; a pair adds one arrival
 // (one chunk of one row) to its message.  Within a round every step is
 // issued for both of a lane's pairs at once: one round trip each for the
-// arrivals (with the status word), the WRITE tickets, the experts' message
-// counts and the ATOMIC tickets.  A round's tickets are all written before
-// the next round takes any.
+// arrivals (with the status word and the channels' cached consumer
+// positions), the WRITE tickets, the experts' message counts and the ATOMIC
+// tickets.  The WRITE slots go out while the message counts are on their
+// way back, so a WRITE ticket stays unwritten for one round trip only (the
+// proxy pops in ticket order: an unwritten ticket holds up its channel).  A
+// round's tickets are all written before the next round takes any.
 template <int W>
 __device__ void ll_publish_group(const PackArgs& a, const int32_t* eo, const int32_t* mb,
                                  const int32_t (*row)[kMaxK], const int32_t (*ex)[kMaxK]) {
@@ -1538,8 +1545,14 @@ __device__ void ll_publish_group(const PackArgs& a, const int32_t* eo, const int
             s[i] = f < npairs ? row[f / k][f % k] : -1;
             e[i] = f < npairs ? ex[f / k][f % k] : -1;
         }
-        // arrivals, with the status word
+        // arrivals, with the status word and the channels' cached positions
         const int32_t st0 = read_status(a.st);
+        unsigned long long sn[P];
+#pragma unroll
+        for (int i = 0; i < P; ++i)
+            sn[i] = s[i] >= 0 ? __hip_atomic_load(a.ring.tail_cache + (size_t)((e[i] / a.epr) % C) * kPad,
+                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                              : 0ull;
         int32_t old[P];
 #pragma unroll
         for (int i = 0; i < P; ++i)
@@ -1559,22 +1572,24 @@ __device__ void ll_publish_group(const PackArgs& a, const int32_t* eo, const int
         }
         if (!__ballot(done != 0)) continue;
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        // WRITE tickets, then (once they exist) the experts' message counts;
-        // an expert's last message takes the ATOMIC's ticket after them all
-        int c[2 * P];
-        unsigned long long tk[2 * P];
-        RingCmd cmd[2 * P];
+        // WRITE tickets; once they exist the experts' message counts go out,
+        // and the WRITE slots are written while the counts return.  An
+        // expert's last message then takes the ATOMIC's ticket after every
+        // WRITE ticket of the expert.
+        int c[P];
+        unsigned long long tk[P], ta[P];
+        RingCmd cmd[P], cma[P];
 #pragma unroll
         for (int i = 0; i < P; ++i) {
-            c[i] = c[P + i] = 0;
-            tk[i] = tk[P + i] = 0;
-            cmd[i] = cmd[P + i] = RingCmd{};
+            c[i] = 0;
+            tk[i] = ta[i] = 0;
+            cmd[i] = cma[i] = RingCmd{};
             if (!((done >> i) & 1u)) continue;
             const int r = e[i] / a.epr;
             const int32_t eo_e = eo[e[i]];
             const int32_t m = (s[i] - eo_e) / kMsgRows;
             const int32_t nrows = min(kMsgRows, eo[e[i] + 1] - eo_e - m * kMsgRows);
-            c[i] = c[P + i] = r % C;
+            c[i] = r % C;
             tk[i] = ring_reserve(a.ring, c[i], 1);
             cmd[i] = RingCmd{EP_CMD_WRITE, 0, (uint32_t)nrows, (uint32_t)r, (uint32_t)(nrows * rb),
                              (uint64_t)(eo_e + m * kMsgRows) * rb,
@@ -1585,7 +1600,8 @@ __device__ void ll_publish_group(const PackArgs& a, const int32_t* eo, const int
         for (int i = 0; i < P; ++i)
             dn[i] = ((done >> i) & 1u) ? atomicAdd(&a.msgs_done[e[i]], 1 + (int32_t)(tk[i] >> 62))
                                        : 0;
-        uint32_t have = done;
+        ring_publish_v<P>(a.ring, done, c, tk, cmd, a.st, sn);
+        uint32_t have = 0;
 #pragma unroll
         for (int i = 0; i < P; ++i) {
             if (!((done >> i) & 1u)) continue;
@@ -1593,13 +1609,13 @@ __device__ void ll_publish_group(const PackArgs& a, const int32_t* eo, const int
             if (dn[i] + 1 == (cnt + kMsgRows - 1) / kMsgRows) {
                 a.msgs_done[e[i]] = 0;
                 const int r = e[i] / a.epr;
-                tk[P + i] = ring_reserve(a.ring, c[P + i], 1);
-                cmd[P + i] = RingCmd{EP_CMD_ATOMIC, EP_ATOMIC_ADD, 0, (uint32_t)r, (uint32_t)cnt,
-                                     0, (uint64_t)(4 * (e[i] - r * a.epr))};
-                have |= 1u << (P + i);
+                ta[i] = ring_reserve(a.ring, c[i], 1);
+                cma[i] = RingCmd{EP_CMD_ATOMIC, EP_ATOMIC_ADD, 0, (uint32_t)r, (uint32_t)cnt,
+                                 0, (uint64_t)(4 * (e[i] - r * a.epr))};
+                have |= 1u << i;
             }
         }
-        ring_publish_v<2 * P>(a.ring, have, c, tk, cmd, a.st);
+        ring_publish_v<P>(a.ring, have, c, ta, cma, a.st);
     }
 }
 

@@ -126,19 +126,8 @@ __device__ inline int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
 
 // Broadcast lane `l` (wave-uniform) of a 32-bit value.
 __device__ inline int32_t bcast(int32_t v, int l) { return __builtin_amdgcn_readlane(v, l); }
-__device__ inline uint64_t bcast64(uint64_t v, int l) {
-    uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
-    uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
-    return ((uint64_t)hi << 32) | lo;
-}
 __device__ inline float bcastf(float v, int l) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
-}
-
-// Number of set bits of `m` below this lane.
-__device__ inline int lane_prefix(uint64_t m) {
-    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                          __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
 // Raw buffer resource over `bytes` bytes at p (the untyped-access word 3 of

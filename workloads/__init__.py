@@ -5,7 +5,7 @@ dispatch/combine arithmetic (no rank membership, counts, slots, packing,
 quantisation or reduction); both the CPU oracle and the HIP path consume what it
 returns.
 
-The pages this build follows measure dispatch/combine only on a real
+The source pages measure dispatch/combine only on a real
 DeepSeek-V3 training cluster and on a "MoE simulated load" (UCCL-EP article,
 peacm.com, section 6 "performance data"; NCCL GIN article, bjdmk.com.cn,
 section 4.3 "benchmark methods").  Neither the model nor its routing traces are

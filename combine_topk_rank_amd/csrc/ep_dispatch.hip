@@ -84,6 +84,9 @@ struct PackArgs {
     // one-kernel large batches
     uint32_t* bar;                // grid barrier words (workspace)
     int32_t* wave_cnt;            // [ceil(T/64), R] per-64-token rank counts (workspace)
+    int32_t* exp_part;            // [nparts, E] partial expert counts (workspace)
+    int32_t nparts;               // workgroup b adds into part b % nparts (<= kExpParts)
+    int32_t expert_wg;            // 1: one workgroup more counts the experts
     int32_t npass;                // groups per pack workgroup, at most
 };
 
@@ -680,10 +683,11 @@ constexpr int kPackWavesSmall = 4;
 // wavefront per row, 7 = two.
 constexpr int kPackVplH7168 = 14;
 constexpr int kPackVplFp8H7168 = 14;
-// Pack workgroups per compute unit, at most: with fewer workgroups than
+// Pack workgroups per compute unit by default: with fewer workgroups than
 // groups, each workgroup loops, so rows complete (and descriptors are
 // published) in several generations instead of all at the end of the kernel.
-// Half the compute units already saturate HBM with 16 wavefronts each.
+// Half the compute units with 16 wavefronts each; the rank-mode streaming
+// pack goes up to all of them for large batches (stream_grid_cap).
 constexpr int kPackGridPerCuNum = 1, kPackGridPerCuDen = 2;
 
 // Store chunk `chunk` of token t's row into every destination slot of the
@@ -1098,11 +1102,19 @@ __global__ __launch_bounds__(kPackWavesSmall* kWave) void fused_small_kernel(Pac
 //      first wavefront also writes its send_slot and is_token_in_rank rows.
 // Each wavefront loads its row chunk of pass 0 before the barrier, so the
 // copy's first reads overlap the layout.
-// One workgroup more than the pack's computes the per-expert counts and
-// their scan from topk_idx meanwhile; it takes no part in the barrier.  The
-// slots are those of the layout kernel: integer counts and prefix sums, no
-// atomic decides an order.
+// The per-expert counts and their scan: when the pack's grid leaves room on
+// the chip, one workgroup more computes them from topk_idx meanwhile (off the
+// critical path; it takes no part in the barrier).  When the pack fills the
+// chip, they come from the ballots' ids: the workgroup that takes a block's
+// first group also counts the block's choices per expert in LDS and adds its
+// non-zero counts, after the barrier, to one of a few partial histograms in
+// the workspace (workgroup b to part b mod nparts, so that few workgroups add
+// to one counter); the last workgroup to have added its counts sums the parts
+// into the output and writes their exclusive scan.  The slots are those of
+// the layout kernel: integer counts and prefix sums, no atomic decides an
+// order.
 constexpr int kFusedLargeMaxPasses = 16;
+constexpr int kExpParts = 8;   // partial expert histograms, at most
 
 // Per-expert counts of all T * k choices and their exclusive scan (one
 // workgroup of NT >= kBlock threads).
@@ -1127,6 +1139,48 @@ __device__ void expert_counts(const PackArgs& a, int32_t* s_hist, int32_t* s_par
     __syncthreads();
     for (int e = tid; e < a.E; e += NT) a.cnt_exp_out[e] = s_hist[e];
     block_exclusive_scan_store(s_hist, a.E, a.exp_off_out, s_part);
+}
+
+// After every workgroup's expert counts are added in (one wavefront of each
+// workgroup, once its own atomics are complete): the last one to arrive sums
+// the parts into num_tokens_per_expert (lane l takes experts l, l + 64, ...,
+// so the loads of a part are coalesced, and a lane's loads of all parts are
+// in flight together), keeps the totals in `tot` (LDS) and writes their
+// exclusive scan (lane l taking a contiguous run of experts).
+__device__ void expert_offsets_if_last(const PackArgs& a, int32_t* tot) {
+    const int lane = lane_id();
+    int last = 0;
+    if (lane == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        last = arrive_last(a.arrive) ? 1 : 0;   // acquires every part's atomics
+    }
+    if (!bcast(last, 0)) return;
+    const int E = a.E, np = a.nparts;
+    for (int e = lane; e < E; e += kWave) {
+        int32_t v[kExpParts];
+#pragma unroll
+        for (int q = 0; q < kExpParts; ++q) v[q] = q < np ? a.exp_part[(int64_t)q * E + e] : 0;
+        int32_t c = 0;
+#pragma unroll
+        for (int q = 0; q < kExpParts; ++q) c += v[q];
+        tot[e] = c;
+        a.cnt_exp_out[e] = c;
+    }
+    const int per = (E + kWave - 1) / kWave;
+    const int lo = lane * per, hi = min(lo + per, E);
+    int32_t sum = 0;
+    for (int e = lo; e < hi; ++e) sum += tot[e];
+    int32_t incl = sum;
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int32_t o = __shfl_up(incl, d);
+        if (lane >= d) incl += o;
+    }
+    int32_t run = incl - sum;
+    for (int e = lo; e < hi; ++e) {
+        a.exp_off_out[e] = run;
+        run += tot[e];
+    }
+    if (lane == kWave - 1) a.exp_off_out[E] = incl;
 }
 
 // The rows of one pass of the one-kernel large batch: this wavefront's
@@ -1160,29 +1214,36 @@ __device__ __forceinline__ int32_t fused_rows(const PackArgs& a, int p, int64_t 
     return s_lane;
 }
 
-// Four wavefronts per SIMD (at most 128 registers a lane), so that the pack
-// workgroups and the expert one are resident at once.
+// One workgroup per CU: WAVES / 4 wavefronts per SIMD.
 template <int VPL, int FMT, int WAVES, int PUB>
-__global__ __launch_bounds__(WAVES * kWave, 4) void fused_large_kernel(PackArgs a) {
+__global__ __launch_bounds__(WAVES * kWave, WAVES / 4) void fused_large_kernel(PackArgs a) {
     constexpr int kWaves = WAVES;
     constexpr int kT = WAVES * kWave;
     constexpr int kPass = kFusedLargeMaxPasses;
     static_assert(kWave % kWaves == 0, "a group lies inside one 64-token block");
+    static_assert(kWaves >= 2, "wavefront 1 finishes the expert offsets");
     static_assert(kT >= kBlock, "the expert scan takes at least kBlock threads");
     __shared__ uint64_t s_ball[kPass][kMaxR];   // pass p: ballots of its group's block
     __shared__ int32_t s_base[kPass][kMaxR];    // pass p: slot of the block's first row of r
     __shared__ int32_t s_tot[kMaxR];            // rows of rank r
     __shared__ int32_t s_slot[2][kWaves][kMaxR];
     __shared__ RankView rv;
-    __shared__ int32_t s_hist[kMaxE];           // the expert workgroup
+    __shared__ int32_t s_hist[kMaxE];           // choices per expert (this workgroup's blocks)
     __shared__ int32_t s_part[kT];
     const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
     const int R = a.R;
-    const int64_t G = (int64_t)gridDim.x - 1;   // pack workgroups
+    const bool count_here = !a.expert_wg;         // uniform over the grid
+    const int64_t G = (int64_t)gridDim.x - (count_here ? 0 : 1);   // pack workgroups
     const int64_t b = blockIdx.x;
     if (b == G) {
         expert_counts<kT>(a, s_hist, s_part);
         return;
+    }
+    if (count_here) {
+        // cleared before any global load is in flight, so that this barrier
+        // waits for nothing
+        for (int e = tid; e < a.E; e += kT) s_hist[e] = 0;
+        __syncthreads();
     }
     // 1. ballots of each pass's block (wavefront p % kWaves takes pass p).
     // The ids of a wavefront's first ballot block are loaded first, then its
@@ -1205,20 +1266,26 @@ __global__ __launch_bounds__(WAVES * kWave, 4) void fused_large_kernel(PackArgs 
         if (g < a.ngroups) {
             const int64_t blk = g * kWaves / kWave;
             if (p != wave) load_token_ids(a.idx, blk * kWave + lane, a.T, a.k, ids);
-            const uint64_t mask = rank_mask_of(ids, a.E, a.k, a.epr, a.st, nullptr);
+            // the block's first group is taken exactly once: it also counts
+            // the block's choices per expert
+            const bool first = (g * kWaves) % kWave == 0;
+            const uint64_t mask =
+                rank_mask_of(ids, a.E, a.k, a.epr, a.st, (first && count_here) ? s_hist : nullptr);
             for (int r = 0; r < R; ++r) {
                 const uint64_t bb = __ballot((mask >> r) & 1ull);
                 if (lane == r) mine = bb;
             }
-            if ((g * kWaves) % kWave == 0 && lane < R)
-                a.wave_cnt[blk * R + lane] = (int32_t)__popcll(mine);
+            if (first && lane < R) a.wave_cnt[blk * R + lane] = (int32_t)__popcll(mine);
         }
         if (lane < R) s_ball[p][lane] = mine;
     }
     for (int p = tid; p < kPass * kMaxR; p += kT) (&s_base[0][0])[p] = 0;
     if (tid < kMaxR) s_tot[tid] = 0;
-    // the streaming pack's message counters start at zero
+    // the streaming pack's message counters and the partial expert counts
+    // (added to after the barrier) start at zero
     for (int64_t i = b * kT + tid; i < a.counters_n; i += G * kT) a.msg_arrivals[i] = 0;
+    if (count_here)
+        for (int64_t i = b * kT + tid; i < (int64_t)a.nparts * a.E; i += G * kT) a.exp_part[i] = 0;
 
     // 2. every block's counts are in the table after this
     if (!grid_barrier<false>(a.bar, (uint32_t)G, a.st, gen)) return;
@@ -1313,16 +1380,37 @@ __global__ __launch_bounds__(WAVES * kWave, 4) void fused_large_kernel(PackArgs 
     // pass 0's rows come from the registers loaded before the barrier; every
     // pack workgroup has a pass 0 (b < G <= ngroups)
     int32_t s_lane = fused_rows<VPL, FMT, kWaves>(a, 0, b, G, s_ball, s_base, &v0);
+    // this workgroup's expert counts, into its part (cleared before the
+    // barrier), behind pass 0's row stores: nothing waits for them before
+    // the group's own wait for its rows, and the table reads of step 3 did
+    // not queue behind them
+    if (count_here) {
+        int32_t* part = a.exp_part + (b % a.nparts) * (int64_t)a.E;
+        for (int e = tid; e < a.E; e += kT) {
+            const int32_t h = s_hist[e];
+            if (h) atomicAdd(&part[e], h);
+        }
+    }
     for (int p = 0;;) {
         if (streaming) {   // uniform over the workgroup
             if (lane < R) s_slot[p & 1][wave][lane] = s_lane;
-            wait_vm();
+            wait_vm();   // also this wavefront's expert-count atomics
             __syncthreads();
             if (wave == 0 && pub_ok) publish_group<kWaves>(a, rv, s_slot[p & 1]);
         }
         if (++p >= a.npass || b + (int64_t)p * G >= a.ngroups) break;
         s_lane = fused_rows<VPL, FMT, kWaves>(a, p, b, G, s_ball, s_base, nullptr);
     }
+    // The expert counts' arrival, after the last group: wavefront 1 has no
+    // rows left while wavefront 0 publishes the last group, so the arrival
+    // and the last workgroup's sums run in that shadow.
+    if (!count_here) return;
+    if (!streaming) {   // uniform over the grid
+        wait_vm();
+        __syncthreads();
+    }
+    // its expert-count atomics are complete; s_hist is read no more
+    if (wave == 1) expert_offsets_if_last(a, s_hist);
 }
 
 // ------------------------------------------------------------ per-expert mode
@@ -1901,6 +1989,21 @@ int64_t pack_grid_cap() {
     return cap;
 }
 
+// Workgroups of the rank-mode streaming pack (one-kernel or not): as many
+// as leave every workgroup at least two passes, between half the CUs' worth
+// and all of them.  Publication of a pass overlaps the copy of the next
+// one, so a single pass would leave every descriptor to the end (train
+// dispatch 116 against 99 us on all CUs); with many groups the whole chip
+// copies (skewed 385 against 438 us).
+int64_t stream_grid_cap(int64_t ngroups, int waves) {
+    const int64_t half = pack_grid_cap() * kPackWaves / waves;
+    const int64_t full = 2 * half;
+    int64_t c = ceil_div(ngroups, (int64_t)2);
+    if (c > full) c = full;
+    if (c < half) c = half;
+    return c;
+}
+
 // SMALL: the small-batch configuration (closed-form publication; otherwise
 // streaming with a ring).  LL: the per-expert pack.
 template <int VPL, int FMT, int WAVES, bool SMALL, bool LL>
@@ -1909,8 +2012,11 @@ int launch_pack_fmt(PackArgs a, int64_t waves, hipStream_t stream) {
     a.ngroups = ceil_div(waves, WAVES);
     // keep about the same number of wavefronts resident whatever WAVES is,
     // and give every workgroup the same number of passes (+-1 group), so no
-    // few workgroups run a last pass alone
-    const int64_t cap = pack_grid_cap() * kPackWaves / WAVES;
+    // few workgroups run a last pass alone.  The per-expert pack keeps half
+    // the CUs' worth: more workgroups mean fewer, larger bursts of completed
+    // messages for the in-flight window (train 130 -> 140 us).
+    const int64_t cap = (pub == kPubStream && !LL) ? stream_grid_cap(a.ngroups, WAVES)
+                                                   : pack_grid_cap() * kPackWaves / WAVES;
     const int64_t passes = ceil_div(a.ngroups, cap);
     const int64_t blocks = ceil_div(a.ngroups, passes);
     const dim3 grid((unsigned)blocks), block(WAVES * kWave);
@@ -2048,7 +2154,8 @@ int64_t resident_blocks(K kernel, int threads) {
 template <int VPL, int FMT, int WAVES>
 int launch_fused_large_fmt(PackArgs a, hipStream_t stream, bool dry) {
     a.ngroups = ceil_div(a.T, WAVES);
-    const int64_t cap = pack_grid_cap() * kPackWaves / WAVES;
+    const int64_t cap = a.has_ring ? stream_grid_cap(a.ngroups, WAVES)
+                                   : pack_grid_cap() * kPackWaves / WAVES;
     const int64_t passes = ceil_div(a.ngroups, cap);
     const int64_t blocks = ceil_div(a.ngroups, passes);
     if (passes > kFusedLargeMaxPasses) return kNotTaken;
@@ -2064,11 +2171,13 @@ int launch_fused_large_fmt(PackArgs a, hipStream_t stream, bool dry) {
                                           WAVES * kWave);
         room[a.has_ring ? 1 : 0].store(rm, std::memory_order_relaxed);
     }
-    if (blocks + 1 > rm) return kNotTaken;
+    if (blocks > rm) return kNotTaken;
     if (dry) return EP_OK;
     a.npass = (int32_t)passes;
     a.nchunks = 1;
-    const dim3 grid((unsigned)(blocks + 1)), block(WAVES * kWave);
+    // the expert counts' own workgroup when it fits beside the pack's
+    a.expert_wg = blocks + 1 <= rm ? 1 : 0;
+    const dim3 grid((unsigned)(blocks + a.expert_wg)), block(WAVES * kWave);
     clear_hip_error();
     if (pub == kPubStream)
         hipLaunchKernelGGL((fused_large_kernel<VPL, FMT, WAVES, kPubStream>), grid, block, 0,
@@ -2250,6 +2359,11 @@ extern "C" int ep_dispatch_fused(const ep_shape_t* shape, const void* x, const i
     a.counters_n = w.counters_n;
     a.bar = w.barrier;
     a.wave_cnt = w.wave_rank_cnt;
+    // the per-tile expert table of the layout kernel is free in a one-kernel
+    // call (no per-expert row table reads it afterwards): at least 4 rows of
+    // E here, since the one-kernel large path takes T >= 1024
+    a.exp_part = w.blk_exp_cnt;
+    a.nparts = w.layout_blocks < kExpParts ? w.layout_blocks : kExpParts;
     if (s.T <= kFusedMaxT) return launch_fused(a, s.fmt, stream);
     v = launch_fused_large(a, s.fmt, stream);
     if (v != kNotTaken) return v;

@@ -2205,10 +2205,10 @@ int launch_fused_large(PackArgs& a, int fmt, hipStream_t stream, bool dry = fals
         if (nv <= 1024) return launch_fused_large_fmt<16, EP_FMT_BF16, kPackWaves>(a, stream, dry);
         return kNotTaken;
     }
-    // fp8 rows stay with the two calls: its pack runs 8-wavefront workgroups
-    // at more than 128 registers a lane, one per compute unit, and the
-    // one-kernel version (capped at 128 so that the expert workgroup fits
-    // too) measured slower
+    // fp8 rows stay with the two calls: the one-kernel version (8-wavefront
+    // workgroups at 151 registers a lane, one per compute unit, expert counts
+    // in the pack workgroups) made the fp8 step slower (183-184 against
+    // 175.5 us)
     return kNotTaken;
 }
 

@@ -709,6 +709,27 @@ __device__ inline void load_row_chunk(const PackArgs& a, int64_t t, int chunk, u
     }
 }
 
+// The same with buffer loads bounded by the row's bytes, for the one-kernel
+// dispatches: vectors past the row read as zero with no branch, so nothing
+// forces a wait for the data before its first use.  With the branch of
+// load_row_chunk the compiler waits for the loads at once, so a prefetch
+// issued ahead of the routing loads held them up; the one-kernel large
+// dispatch also needs fewer registers with these (train 197.8 -> 196.3 us
+// per step, skewed 691 -> 681 us).  The two-kernel packs keep load_row_chunk
+// (fp8 was 1 us slower with buffer loads).
+template <int VPL>
+__device__ inline void prefetch_row_chunk(const PackArgs& a, int64_t t, int chunk,
+                                          u32x4 (&v)[VPL]) {
+    const int lane = lane_id();
+    const int v0 = chunk * VPL * kWave;
+    const __amdgpu_buffer_rsrc_t rs =
+        buffer_rsrc(const_cast<u32x4*>(a.x + t * a.nv), a.nv * (int32_t)sizeof(u32x4));
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+        v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, (v0 + lane + i * kWave) * (int)sizeof(u32x4),
+                                                     0, 0);
+}
+
 template <int VPL, int FMT>
 __device__ inline void store_row_chunk_v(const PackArgs& a, int chunk, int32_t s_lane,
                                          uint64_t dmask, const u32x4 (&v)[VPL]);
@@ -977,7 +998,7 @@ __global__ __launch_bounds__(kPackWavesSmall* kWave) void fused_small_kernel(Pac
         const int64_t gw = (int64_t)blockIdx.x * kWaves + wave;
         const int64_t t = gw / a.nchunks;
         if (blockIdx.x < a.ngroups && t < a.T)
-            load_row_chunk<VPL>(a, t, (int)(gw - t * a.nchunks), v);
+            prefetch_row_chunk<VPL>(a, t, (int)(gw - t * a.nchunks), v);
     }
 
     // layout, in every workgroup
@@ -1040,7 +1061,7 @@ __global__ __launch_bounds__(kPackWavesSmall* kWave) void fused_small_kernel(Pac
         const int64_t t = gw / a.nchunks;
         const int chunk = (int)(gw - t * a.nchunks);
         if (t >= a.T) continue;   // wavefront-uniform
-        if (grp != blockIdx.x) load_row_chunk<VPL>(a, t, chunk, v);
+        if (grp != blockIdx.x) prefetch_row_chunk<VPL>(a, t, chunk, v);
         const int tw = (int)(t / kWave), tl = (int)(t % kWave);
         int32_t s_lane = -1;
         uint32_t bit = 0;
@@ -1205,10 +1226,13 @@ __device__ __forceinline__ int32_t fused_rows(const PackArgs& a, int p, int64_t 
             a.in_rank_out[t * R + lane] = (uint8_t)in;
         }
         const uint64_t dmask = __ballot(s_lane >= 0);
-        if (v)
+        if (v) {
             store_row_chunk_v<VPL, FMT>(a, 0, s_lane, dmask, *v);
-        else
-            store_row_chunk<VPL, FMT>(a, t, 0, s_lane, dmask);
+        } else {
+            u32x4 w[VPL];
+            prefetch_row_chunk<VPL>(a, t, 0, w);   // branch-free loads (fewer registers here)
+            store_row_chunk_v<VPL, FMT>(a, 0, s_lane, dmask, w);
+        }
         store_slot_metadata(a, t, s_lane, dmask);
     }
     return s_lane;
@@ -1255,7 +1279,7 @@ __global__ __launch_bounds__(WAVES * kWave, WAVES / 4) void fused_large_kernel(P
                        ids);
     u32x4 v0[VPL];
     const int64_t t0 = b * kWaves + wave;   // this wavefront's token in pass 0
-    if (t0 < a.T) load_row_chunk<VPL>(a, t0, 0, v0);
+    if (t0 < a.T) prefetch_row_chunk<VPL>(a, t0, 0, v0);
     // the barrier's generation, loaded after the ids so that they do not
     // wait behind it
     uint32_t gen = 0;
@@ -1828,7 +1852,7 @@ __global__ __launch_bounds__(kPackWavesSmall* kWave) void ll_fused_small_kernel(
         const int64_t gw = (int64_t)blockIdx.x * kWaves + wave;
         const int64_t t = gw / a.nchunks;
         if (blockIdx.x < a.ngroups && t < a.T)
-            load_row_chunk<VPL>(a, t, (int)(gw - t * a.nchunks), v);
+            prefetch_row_chunk<VPL>(a, t, (int)(gw - t * a.nchunks), v);
     }
 
     // the lane's token and its choices
@@ -1936,7 +1960,7 @@ __global__ __launch_bounds__(kPackWavesSmall* kWave) void ll_fused_small_kernel(
         const int64_t tt = gw / a.nchunks;
         const int chunk = (int)(gw - tt * a.nchunks);
         if (tt >= a.T) continue;   // wavefront-uniform
-        if (grp != blockIdx.x) load_row_chunk<VPL>(a, tt, chunk, v);
+        if (grp != blockIdx.x) prefetch_row_chunk<VPL>(a, tt, chunk, v);
         const int32_t s_lane = lane < k ? s_row[tt][lane] : -1;
         const uint64_t dmask = __ballot(s_lane >= 0);
         store_row_chunk_v<VPL, FMT>(a, chunk, s_lane, dmask, v);

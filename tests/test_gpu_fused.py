@@ -191,6 +191,7 @@ def test_fused_errors(name):
 LARGE_EDGES = [
     (65536, 1032, 4, 2, 1, 0.0, 2),     # 4096 groups on 256 workgroups (all CUs): 16 passes, the maximum
     (32768, 1032, 4, 2, 1, 0.0, 2),     # 2048 groups on 256 workgroups: 8 passes
+    (8192, 1032, 4032, 64, 8, 0.1, 8),  # the grid fills the chip: expert counts in the pack workgroups, E/64 ragged
     (4095, 4104, 7, 7, 3, 0.2, 3),      # one expert per rank, R not a power of two, ragged T
     (1025, 2048, 1, 1, 1, 0.5, 1),      # one rank, half the choices dropped, one token past 1024
     (6000, 7168, 64, 64, 1, 0.0, 8),    # k = 1, 64 ranks

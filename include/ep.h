@@ -204,7 +204,8 @@ int ep_dispatch(const ep_shape_t* shape, const void* x, const int32_t* topk_idx,
  * Otherwise it makes the two calls.  ep_dispatch_fused_plan says which.
  * send_slot must be 16-byte and is_token_in_rank 4-byte aligned when
  * T > 256.  Leaves in the workspace what a following ep_dispatch with the
- * same layout needs. */
+ * same layout needs, but not the per-tile expert counts that
+ * ep_dispatch_layout_ll reads (that one follows ep_dispatch_layout). */
 int ep_dispatch_fused(const ep_shape_t* shape, const void* x, const int32_t* topk_idx,
                       const float* topk_w, int32_t* num_tokens_per_rank,
                       int32_t* num_tokens_per_expert, int32_t* rank_offset,

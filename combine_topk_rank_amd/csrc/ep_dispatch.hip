@@ -2028,6 +2028,21 @@ int64_t stream_grid_cap(int64_t ngroups, int waves) {
     return c;
 }
 
+// Rank-mode bf16 rows that one wavefront covers are split over two
+// wavefronts (8 vectors a lane) when whole rows would make at least 4
+// streaming passes.  Twice the passes halve each pass's burst of completed
+// messages (skewed: about 370 commands a channel at a pass end, above the 256
+// in flight, against about 186) with as many wavefronts in flight: its pack
+// 385-393 -> 354 us.  At 2 passes the split costs more than it saves (train
+// pack 99.5 -> 101-102.5 us).  The one-kernel large dispatch takes one
+// wavefront per token, so split batches take the two calls.
+bool rank_rows_split(const PackArgs& a, int fmt) {
+    if (fmt != EP_FMT_BF16 || !a.has_ring || a.nv <= 512 || a.nv > 896) return false;
+    if ((int64_t)a.T < kPackSmallWaves) return false;
+    const int64_t ngroups = ceil_div((int64_t)a.T, (int64_t)kPackWaves);
+    return ceil_div(ngroups, stream_grid_cap(ngroups, kPackWaves)) >= 4;
+}
+
 // SMALL: the small-batch configuration (closed-form publication; otherwise
 // streaming with a ring).  LL: the per-expert pack.
 template <int VPL, int FMT, int WAVES, bool SMALL, bool LL>
@@ -2106,7 +2121,7 @@ int launch_pack_any(PackArgs& a, int fmt, hipStream_t stream) {
     // half as many tokens in flight, each pass completes half as many
     // messages at once, so the burst of publications at a pass's end fits
     // the in-flight window better (train 139 -> 131 us, skewed 618 -> 542 us)
-    else if (a.nv <= 896) vpl = LL ? 8 : kPackVplH7168;
+    else if (a.nv <= 896) vpl = (LL || rank_rows_split(a, fmt)) ? 8 : kPackVplH7168;
     else vpl = 16;
     a.nchunks = (int32_t)ceil_div(a.nv, (int64_t)vpl * kWave);
     int64_t waves = (int64_t)a.T * a.nchunks;
@@ -2224,8 +2239,10 @@ int launch_fused_large(PackArgs& a, int fmt, hipStream_t stream, bool dry = fals
         if (nv <= 128) return kNotTaken;
         if (nv <= 256) return launch_fused_large_fmt<4, EP_FMT_BF16, kPackWaves>(a, stream, dry);
         if (nv <= 512) return launch_fused_large_fmt<8, EP_FMT_BF16, kPackWaves>(a, stream, dry);
-        if (nv <= 896)
+        if (nv <= 896) {
+            if (rank_rows_split(a, fmt)) return kNotTaken;   // two wavefronts a row
             return launch_fused_large_fmt<kPackVplH7168, EP_FMT_BF16, kPackWaves>(a, stream, dry);
+        }
         if (nv <= 1024) return launch_fused_large_fmt<16, EP_FMT_BF16, kPackWaves>(a, stream, dry);
         return kNotTaken;
     }

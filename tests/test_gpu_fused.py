@@ -55,8 +55,11 @@ def test_fused_workload_parity(name):
                               oracle.row_bytes(w.H, w.fmt), w.channels)
     import combine_topk_rank_amd as ep
     plan = ep.ep_dispatch_fused_plan(ep.shape(w.T, w.H, w.E, w.R, w.k, w.fmt))
-    assert plan == (ep.EP_FUSED_ONE_KERNEL_SMALL if w.T <= 256 else
-                    ep.EP_FUSED_ONE_KERNEL_LARGE if w.fmt == 0 else ep.EP_FUSED_TWO_CALLS)
+    # skewed's 16,384 tokens would make 4 passes of whole rows on the chip:
+    # its rows go two wavefronts each, so it takes the two calls
+    assert plan == {"tiny": ep.EP_FUSED_ONE_KERNEL_SMALL, "decode": ep.EP_FUSED_ONE_KERNEL_SMALL,
+                    "train": ep.EP_FUSED_ONE_KERNEL_LARGE, "fp8": ep.EP_FUSED_TWO_CALLS,
+                    "skewed": ep.EP_FUSED_TWO_CALLS}[name]
     log(f"[fused] workload {name}: T={w.T} H={w.H} R={w.R} k={w.k}, P={P}; one-kernel dispatch")
     g = run_hip(w.T, w.H, w.E, w.R, w.k, w.fmt, inp["x"], inp["topk_idx"], inp["topk_w"],
                 capacity_rows=P + 8,

@@ -22,7 +22,7 @@ def _args(mode="rank"):
                               proxy_threads=4, warmup=2)
 
 
-@pytest.mark.parametrize("name", ["train", "fp8", "decode"])
+@pytest.mark.parametrize("name", ["train", "fp8", "skewed", "decode"])
 def test_bench_step_matches_oracle(name):
     import torch
 

@@ -197,11 +197,13 @@ int ep_dispatch(const ep_shape_t* shape, const void* x, const int32_t* topk_idx,
  * on chip and starts copying rows at once, and the descriptors are published
  * in closed form by the last workgroup to finish its rows.  For T >= 1024
  * with bf16 rows that one wavefront covers (H in (1024, 8192]) it is one
- * kernel too, when its workgroups can all be
- * resident: each computes the rank ballots of its own tokens' 64-token
- * blocks, they meet at a grid barrier, and each derives its slots from a
- * per-block count table, then packs and publishes as ep_dispatch does.
- * Otherwise it makes the two calls.  ep_dispatch_fused_plan says which.
+ * kernel too, when its workgroups can all be resident and the batch is not
+ * so long that ep_dispatch would give each row two wavefronts (whole rows
+ * making 4 or more passes over the chip): each workgroup computes the rank
+ * ballots of its own tokens' 64-token blocks, they meet at a grid barrier,
+ * and each derives its slots from a per-block count table, then packs and
+ * publishes as ep_dispatch does.  Otherwise it makes the two calls.
+ * ep_dispatch_fused_plan says which.
  * send_slot must be 16-byte and is_token_in_rank 4-byte aligned when
  * T > 256.  Leaves in the workspace what a following ep_dispatch with the
  * same layout needs, but not the per-tile expert counts that

@@ -222,3 +222,19 @@ def test_fused_large_edges(case):
     got, st = run_hip_combine(g["buffers"], y, g["d_idx"], g["d_w"])
     assert st == 0
     combine_tolerance_check(got, ref, f"one-kernel large edge {case}")
+
+
+def test_fused_large_row_split_boundary():
+    """bf16 rows of 7168 (one wavefront each) stay in the one-kernel path
+    while whole rows make at most 3 passes over the chip's 256 workgroups;
+    from 4 passes on, ep_dispatch gives each row two wavefronts and the fused
+    call takes the two calls.  Without a ring nothing is split."""
+    import combine_topk_rank_amd as ep
+    for T, want in ((12288, ep.EP_FUSED_ONE_KERNEL_LARGE),    # 768 groups: 3 passes
+                    (12352, ep.EP_FUSED_TWO_CALLS),           # 772 groups: 4 passes
+                    (16384, ep.EP_FUSED_TWO_CALLS)):
+        assert ep.ep_dispatch_fused_plan(ep.shape(T, 7168, 256, 64, 8)) == want, T
+    assert ep.ep_dispatch_fused_plan(ep.shape(16384, 7168, 256, 64, 8), with_ring=False) == \
+        ep.EP_FUSED_ONE_KERNEL_LARGE
+    # fp8 rows always take the two calls
+    assert ep.ep_dispatch_fused_plan(ep.shape(12288, 7168, 256, 64, 8, 1)) == ep.EP_FUSED_TWO_CALLS

@@ -2177,9 +2177,10 @@ int launch_fused(PackArgs& a, int fmt, hipStream_t stream) {
 
 // One-kernel large batch: the work order of the two-kernel pack (same
 // group size and grid), when it has one wavefront per token, at most
-// kFusedLargeMaxPasses groups per workgroup, and room for every workgroup
-// (plus the expert one) at once.  kNotTaken when the batch does not qualify;
-// nothing is launched then.
+// kFusedLargeMaxPasses groups per workgroup, and room for every pack
+// workgroup at once (the expert counts get a workgroup of their own when one
+// more fits, else the pack workgroups take them).  kNotTaken when the batch
+// does not qualify; nothing is launched then.
 constexpr int kNotTaken = -1;   // no status code is negative
 
 template <typename K>
@@ -2232,9 +2233,10 @@ int launch_fused_large_fmt(PackArgs a, hipStream_t stream, bool dry) {
 }
 
 // The vectors per lane of the two-kernel pack for this row size, if one
-// wavefront covers a row and the batch is large enough for the streaming
-// pack (smaller batches and rows take the two-kernel path).  dry: only
-// whether the batch would take the path.
+// wavefront covers a row, the batch is large enough for the streaming pack
+// and the two-kernel pack would not split its rows (smaller batches, smaller
+// or split rows and fp8 take the two-kernel path).  dry: only whether the
+// batch would take the path.
 int launch_fused_large(PackArgs& a, int fmt, hipStream_t stream, bool dry = false) {
     if ((int64_t)a.T < kPackSmallWaves) return kNotTaken;
     const int nv = a.nv;

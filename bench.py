@@ -112,6 +112,7 @@ KERNEL_SOURCES = ["combine_topk_rank_amd/csrc/ep_dispatch.hip",
                   "combine_topk_rank_amd/csrc/ep_combine.hip",
                   "combine_topk_rank_amd/csrc/ep_layout.hip",
                   "combine_topk_rank_amd/csrc/ep_common.h",
+                  "combine_topk_rank_amd/csrc/ep_route.h",
                   "combine_topk_rank_amd/csrc/ep_ring_proto.h"]
 
 

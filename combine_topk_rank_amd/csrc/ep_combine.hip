@@ -83,10 +83,12 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(CombineArgs a) {
             e_l = a.idx[t * a.k + lane];
             w_l = a.w[t * a.k + lane];
         }
+        // e / epr == lane, for e in [0, E), without a division
+        const int first_e = lane * a.epr;
         for (int j = 0; j < a.k; ++j) {
             const int e = bcast(e_l, j);
             const float wj = bcastf(w_l, j);
-            if (e >= 0 && e < a.E && e / a.epr == lane) W += wj;
+            if (e >= 0 && e < a.E && (unsigned)(e - first_e) < (unsigned)a.epr) W += wj;
         }
     }
     if (s_lane >= a.y_rows) {

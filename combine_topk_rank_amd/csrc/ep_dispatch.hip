@@ -853,7 +853,7 @@ __device__ inline void store_slot_metadata(const PackArgs& a, int64_t t, int32_t
         const int32_t s = bcast(s_lane, r);
         if (s >= a.cap) continue;
         if (lane < a.k) {
-            const bool local = e >= 0 && e < a.E && e / a.epr == r;
+            const bool local = e >= 0 && e < a.E && (unsigned)(e - r * a.epr) < (unsigned)a.epr;
             a.slot_local_idx[(int64_t)s * a.k + lane] = local ? e - r * a.epr : -1;
             a.slot_local_w[(int64_t)s * a.k + lane] = local ? wt : 0.0f;
         }

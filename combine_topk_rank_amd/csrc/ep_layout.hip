@@ -125,10 +125,12 @@ __global__ __launch_bounds__(kBlock) void layout_count_kernel(
     __shared__ int32_t s_wcnt[kBlock / kWave][kMaxR];
     const int tid = threadIdx.x;
     const int wave = tid / kWave;
+    const int64_t t = (int64_t)blockIdx.x * kLayoutTile + tid;
+    int32_t ids[kMaxK];
+    load_token_ids(idx, t, T, k, ids);   // in flight while the histogram clears
     for (int e = tid; e < E; e += kBlock) s_hist[e] = 0;
     __syncthreads();
-    const int64_t t = (int64_t)blockIdx.x * kLayoutTile + tid;
-    uint64_t mask = token_rank_mask(idx, t, T, E, k, epr, st, s_hist);
+    uint64_t mask = rank_mask_of(ids, E, k, epr, st, s_hist);
     wave_rank_counts(mask, R, s_wcnt[wave]);
     __syncthreads();
     if (tid < R) {
@@ -178,15 +180,20 @@ __global__ __launch_bounds__(kBlock) void layout_main_kernel(
     uint32_t gen = 0;
     if (FUSED && tid == 0) gen = grid_barrier_generation(bar);
 
+    const int64_t t_first = (int64_t)b * kLayoutTile;
+    const int64_t t = t_first + tid;
+    // the token's expert ids are requested first, so that their latency
+    // overlaps the clearing of the histogram (the expert workgroup's tokens
+    // are all past T: nothing is loaded there)
+    int32_t ids[kMaxK];
+    load_token_ids(idx, t, T, k, ids);
     if (SINGLE || FUSED) {
         for (int e = tid; e < E; e += kBlock) s_hist[e] = 0;
         __syncthreads();
     }
-    const int64_t t_first = (int64_t)b * kLayoutTile;
-    const int64_t t = t_first + tid;
     uint64_t mask = 0, my_ball = 0;
     if (!expert_wg) {
-        mask = token_rank_mask(idx, t, T, E, k, epr, st, (SINGLE || FUSED) ? s_hist : nullptr);
+        mask = rank_mask_of(ids, E, k, epr, st, (SINGLE || FUSED) ? s_hist : nullptr);
         my_ball = wave_rank_counts(mask, R, s_wcnt[wave], s_ball[wave]);
     }
     __syncthreads();
@@ -281,8 +288,37 @@ __global__ __launch_bounds__(kBlock) void layout_main_kernel(
     const int32_t* wbase = s_wbase[wave];
     int32_t* slot_out = send_slot + t_wave * R;
     uint8_t* in_out = in_rank + t_wave * R;
-    if ((kWave % R) == 0) {
-        // R divides 64: lane l serves rank l % R of token (j * 64 + l) / R,
+    if ((R & 3) == 0 && (kWave % R) == 0) {
+        // R in {4, 8, 16, 32, 64}: lane l serves ranks r0 .. r0+3, r0 =
+        // 4 (l mod R/4), of tokens l / (R/4), l / (R/4) + 256 / R, ...: per
+        // token one 16-byte slot store and one 4-byte flag store, the wave's
+        // lanes covering 64 * 16 consecutive bytes of send_slot per store.
+        // The lane's four ballots and bases stay in registers throughout.
+        const int q = R >> 2;          // lanes per token
+        const int step = kWave / q;    // tokens per pass of the wave
+        const int r0 = (lane % q) * 4;
+        uint64_t bl[4];
+        int32_t wb[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            bl[u] = ball[r0 + u];
+            wb[u] = wbase[r0 + u];
+        }
+        for (int i = lane / q; i < n; i += step) {
+            const uint64_t below = (1ull << i) - 1ull;   // i < 64
+            int32_t v[4];
+            uint32_t bytes = 0;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t bit = (uint32_t)(bl[u] >> i) & 1u;
+                v[u] = bit ? wb[u] + (int32_t)__popcll(bl[u] & below) : -1;
+                bytes |= bit << (8 * u);
+            }
+            *reinterpret_cast<int4*>(slot_out + (int64_t)i * R + r0) = int4{v[0], v[1], v[2], v[3]};
+            *reinterpret_cast<uint32_t*>(in_out + (int64_t)i * R + r0) = bytes;
+        }
+    } else if ((kWave % R) == 0) {
+        // R = 1 or 2: lane l serves rank l % R of token (j * 64 + l) / R,
         // so each store covers 64 consecutive entries; the ballot and base
         // are already in the lane's registers.
         const int G = kWave / R;

@@ -16,22 +16,37 @@ __device__ inline void load_token_ids(const int32_t* __restrict__ idx, int64_t t
     for (int j = 0; j < kMaxK; ++j) ids[j] = (t < T && j < k) ? row[j] : -1;
 }
 
-// Rank mask of a token from its ids; bad ids are reported and skipped.  When
-// `hist` is given, the token's valid experts are counted in it (LDS).
+// Owner rank e / epr of expert e in [0, E), by one float multiply instead of
+// an integer division (a long dependent sequence of quarter-rate multiplies).
+// Exact: E <= 4096 and R = E / epr <= 64, so the quotient (e + 1/2) / epr is
+// at most 64 and lies at least 1/(2 epr) >= 2^-13 from every integer, while
+// the float product, with inv_epr = 1/epr correctly rounded, is within
+// 64 * 2^-23 = 2^-17 of it; truncation therefore gives floor(e / epr).
+__device__ inline float inv_experts_per_rank(int epr) { return 1.0f / (float)epr; }
+__device__ inline int rank_of_expert(int e, float inv_epr) {
+    return (int)(((float)e + 0.5f) * inv_epr);
+}
+
+// Rank mask of a token from its ids; bad ids are reported (once per token)
+// and skipped.  When `hist` is given, the token's valid experts are counted
+// in it (LDS).
 __device__ inline uint64_t rank_mask_of(const int32_t (&ids)[kMaxK], int E, int k, int epr,
                                         int32_t* st, int32_t* hist) {
+    const float inv_epr = inv_experts_per_rank(epr);
     uint64_t m = 0;
+    bool bad = false;
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j) {
         const int e = ids[j];
         if (j >= k || e == -1) continue;
-        if (e < -1 || e >= E) {
-            set_error(st, EP_ERR_BAD_EXPERT);
+        if ((unsigned)e >= (unsigned)E) {   // below -1, or E and above
+            bad = true;
             continue;
         }
-        m |= 1ull << (e / epr);
+        m |= 1ull << rank_of_expert(e, inv_epr);
         if (hist) atomicAdd(&hist[e], 1);
     }
+    if (bad) set_error(st, EP_ERR_BAD_EXPERT);
     return m;
 }
 
@@ -47,15 +62,55 @@ __device__ inline uint64_t token_rank_mask(const int32_t* __restrict__ idx, int6
 // Lane l ends up holding ball_{l mod R} (all lanes, so that every group of R
 // lanes has the full set); lanes < R write their count to wcnt[r] and, when
 // given, the ballot to ball[r].
+//
+// The ballots are the transpose of the wave's 64 x 64 bit matrix (lane =
+// token, bit = rank), done in six butterfly steps instead of one ballot per
+// rank: at step s, lanes i and i ^ s (i without bit s) swap the off-diagonal
+// blocks, i's bits at positions with bit s set against its partner's bits at
+// positions with bit s clear.  One 32-bit shuffle per step: for s = 32 a lane
+// sends the word its partner takes; below that, the 16 bits wanted of each
+// half are packed into one word.  A last shuffle gives lanes >= R the
+// ballot of lane mod R (the transpose leaves them zero).
 __device__ inline uint64_t wave_rank_counts(uint64_t mask, int R, int32_t* wcnt,
                                             uint64_t* ball = nullptr) {
     const int lane = lane_id();
-    const int my_r = lane % R;
-    uint64_t mine = 0;
-    for (int r = 0; r < R; ++r) {
-        const uint64_t b = __ballot((mask >> r) & 1ull);
-        if (my_r == r) mine = b;
+    uint32_t lo = (uint32_t)mask, hi = (uint32_t)(mask >> 32);
+    {
+        const bool up = (lane & 32) != 0;
+        const uint32_t got = (uint32_t)__shfl_xor((int)(up ? lo : hi), 32);
+        if (up)
+            lo = got;
+        else
+            hi = got;
     }
+#pragma unroll
+    for (int step = 0; step < 5; ++step) {
+        const int s = 16 >> step;
+        // the positions with bit s clear
+        const uint32_t m = step == 0 ? 0x0000FFFFu
+                         : step == 1 ? 0x00FF00FFu
+                         : step == 2 ? 0x0F0F0F0Fu
+                         : step == 3 ? 0x33333333u
+                                     : 0x55555555u;
+        const bool up = (lane & s) != 0;
+        const uint32_t send_lo = up ? (lo & m) : ((lo >> s) & m);
+        const uint32_t send_hi = up ? (hi & m) : ((hi >> s) & m);
+        const uint32_t got = (uint32_t)__shfl_xor((int)(send_lo | (send_hi << s)), s);
+        const uint32_t glo = got & m, ghi = (got >> s) & m;
+        if (up) {
+            lo = glo | (lo & ~m);
+            hi = ghi | (hi & ~m);
+        } else {
+            lo = (lo & m) | (glo << s);
+            hi = (hi & m) | (ghi << s);
+        }
+    }
+    if (R < kWave) {
+        const int src = lane % R;
+        lo = (uint32_t)__shfl((int)lo, src);
+        hi = (uint32_t)__shfl((int)hi, src);
+    }
+    const uint64_t mine = ((uint64_t)hi << 32) | lo;
     if (lane < R) {
         wcnt[lane] = (int32_t)__popcll(mine);
         if (ball) ball[lane] = mine;

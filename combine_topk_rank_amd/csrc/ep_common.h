@@ -54,6 +54,7 @@ __device__ inline bool ring_check_completion(const RingDev& g, int c, unsigned l
 // counters).
 constexpr size_t kArriveStride = 32;   // words
 constexpr int kBarGroups = 8;
+constexpr int kBarFlatMax = 128;   // grids up to this size count arrivals in one level
 constexpr size_t kBarGen = (1 + kBarGroups) * kArriveStride;   // word of the generation
 constexpr size_t kBarrierBytes = 10 * kArriveStride * 4;
 constexpr size_t kWsHeader = kBarrierBytes + 16 * kArriveStride * 4;
@@ -151,11 +152,14 @@ constexpr int kStoreSystem = kCacheSc0 | kCacheSc1;
 // covers another wavefront's stores only if that wavefront waited first.
 __device__ inline void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// Grid-wide barrier for a grid whose workgroups are all resident.  Arrivals
-// are counted in two levels so that no single word takes every atomic:
-// workgroup b counts into group counter b % kBarGroups, the last of a group
-// into the top counter, and the last of all bumps the generation, which
-// releases the others.  Each workgroup reads the generation before it
+// Grid-wide barrier for a grid whose workgroups are all resident.  Grids of
+// more than kBarFlatMax workgroups count arrivals in two levels so that no
+// single word takes every atomic: workgroup b counts into group counter
+// b % kBarGroups, the last of a group into the top counter.  Smaller grids
+// count straight into the top counter, which saves the group level's atomic
+// round trip and cache maintenance on the path of the last arrival (about
+// 0.6-0.9 us of a 17-65 workgroup layout).  The last of all bumps the
+// generation, which releases the others.  Each workgroup reads the generation before it
 // arrives (thread 0 passes what it loaded with grid_barrier_generation, as
 // early as it likes: the generation cannot move before this workgroup
 // arrives).  Every counter is reset by the arrival that completes it, so the
@@ -185,7 +189,15 @@ __device__ bool grid_barrier(uint32_t* bar, uint32_t nblocks, int32_t* st, uint3
         const uint32_t in_g = (nblocks - g + kBarGroups - 1) / kBarGroups;
         uint32_t* cg = bar + (size_t)(1 + g) * kArriveStride;
         bool last = false;
-        if (__hip_atomic_fetch_add(cg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == in_g - 1) {
+        if (nblocks <= (uint32_t)kBarFlatMax) {
+            if (__hip_atomic_fetch_add(&bar[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                nblocks - 1) {
+                __hip_atomic_store(&bar[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");
+                last = true;
+            }
+        } else if (__hip_atomic_fetch_add(cg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                   in_g - 1) {
             __hip_atomic_store(cg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             // what the group's workgroups released goes on with the top arrival
             __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");

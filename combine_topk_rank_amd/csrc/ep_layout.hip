@@ -29,73 +29,59 @@
 
 namespace ep {
 
-// Sum the [nrows, ncols] int32 matrix m over its rows into LDS acc[ncols]
-// (zeroed by the caller); rows < split also go to acc_pre (may be null).
-// Flat and fully parallel: 16-byte loads when ncols % 4 == 0, issued in
-// batches of kSumBatch before any of them is added (one memory latency per
-// batch, not per load), then LDS atomics.
-constexpr int kSumBatch = 4;
-__device__ inline void column_sums(const int32_t* __restrict__ m, int nrows, int ncols, int split,
-                                   int32_t* acc, int32_t* acc_pre) {
-    const int64_t n = (int64_t)nrows * ncols;
-    if ((ncols & 3) == 0) {
-        const int4* m4 = reinterpret_cast<const int4*>(m);
-        const int64_t n4 = n >> 2;
-        for (int64_t i0 = threadIdx.x; i0 < n4; i0 += (int64_t)kBlock * kSumBatch) {
-            int4 q[kSumBatch];
+// Column totals of the [nrows, R] int32 matrix m (the tiles' rank counts,
+// nrows >= 1) and its sums over rows < split, for lanes < R of wavefront 0
+// (*tot, *pre; other threads get zeros).  Lane c < R of wavefront w adds
+// column c over rows w, w + 4, ..., kColBatch loads in flight at a time (one
+// memory latency for up to 4 * kColBatch rows); wavefront 0 then adds the
+// four partials from LDS (part_tot, part_pre: kBlock entries each).  Loads
+// past the last row re-read it and count nothing, so no load is predicated;
+// every load is coalesced and no LDS atomic is involved.  Contains a
+// workgroup barrier.
+constexpr int kColBatch = 8;
+__device__ inline void rank_column_sums(const int32_t* __restrict__ m, int nrows, int R, int split,
+                                        int32_t* part_tot, int32_t* part_pre, int32_t* tot,
+                                        int32_t* pre) {
+    constexpr int NW = kBlock / kWave;
+    const int lane = lane_id(), w = threadIdx.x / kWave;
+    if (lane < R) {
+        int32_t st = 0, sp = 0;
+        for (int r0 = w; r0 < nrows; r0 += kColBatch * NW) {
+            int32_t q[kColBatch];
 #pragma unroll
-            for (int u = 0; u < kSumBatch; ++u) {
-                const int64_t i = i0 + (int64_t)u * kBlock;
-                q[u] = i < n4 ? m4[i] : int4{0, 0, 0, 0};
-            }
+            for (int u = 0; u < kColBatch; ++u)
+                q[u] = m[(int64_t)min(r0 + u * NW, nrows - 1) * R + lane];
 #pragma unroll
-            for (int u = 0; u < kSumBatch; ++u) {
-                const int64_t i = i0 + (int64_t)u * kBlock;
-                if (i >= n4) break;
-                const int e0 = (int)(i * 4);
-                const int row = e0 / ncols;
-                const int col = e0 - row * ncols;
-                atomicAdd(&acc[col], q[u].x);
-                atomicAdd(&acc[col + 1], q[u].y);
-                atomicAdd(&acc[col + 2], q[u].z);
-                atomicAdd(&acc[col + 3], q[u].w);
-                if (acc_pre && row < split) {
-                    atomicAdd(&acc_pre[col], q[u].x);
-                    atomicAdd(&acc_pre[col + 1], q[u].y);
-                    atomicAdd(&acc_pre[col + 2], q[u].z);
-                    atomicAdd(&acc_pre[col + 3], q[u].w);
-                }
+            for (int u = 0; u < kColBatch; ++u) {
+                const int r = r0 + u * NW;
+                st += r < nrows ? q[u] : 0;
+                sp += r < split ? q[u] : 0;
             }
         }
-    } else {
-        for (int64_t i0 = threadIdx.x; i0 < n; i0 += (int64_t)kBlock * kSumBatch) {
-            int32_t q[kSumBatch];
+        part_tot[w * kWave + lane] = st;
+        part_pre[w * kWave + lane] = sp;
+    }
+    __syncthreads();
+    int32_t a = 0, p = 0;
+    if (w == 0 && lane < R) {
 #pragma unroll
-            for (int u = 0; u < kSumBatch; ++u) {
-                const int64_t i = i0 + (int64_t)u * kBlock;
-                q[u] = i < n ? m[i] : 0;
-            }
-#pragma unroll
-            for (int u = 0; u < kSumBatch; ++u) {
-                const int64_t i = i0 + (int64_t)u * kBlock;
-                if (i >= n) break;
-                const int row = (int)i / ncols;
-                const int col = (int)i - row * ncols;
-                atomicAdd(&acc[col], q[u]);
-                if (acc_pre && row < split) atomicAdd(&acc_pre[col], q[u]);
-            }
+        for (int h = 0; h < NW; ++h) {
+            a += part_tot[h * kWave + lane];
+            p += part_pre[h * kWave + lane];
         }
     }
+    *tot = a;
+    *pre = p;
 }
 
 // Totals of the [nrows, ncols] int32 matrix m over its rows, one column per
 // thread (consecutive threads read consecutive columns, so every load is
-// coalesced), kSumBatch * 4 rows in flight per thread; into LDS acc[ncols].
+// coalesced), 16 rows in flight per thread; into LDS acc[ncols].
 // Each column of m is replaced by its exclusive prefix over the rows (row i:
 // the sum of rows < i), which the per-expert row table reads.
 __device__ inline void column_totals(int32_t* __restrict__ m, int nrows, int ncols,
                                      int32_t* acc) {
-    constexpr int kRows = kSumBatch * 4;
+    constexpr int kRows = 16;
     for (int c = threadIdx.x; c < ncols; c += kBlock) {
         int32_t sum = 0;
         for (int r0 = 0; r0 < nrows; r0 += kRows) {
@@ -117,6 +103,7 @@ __device__ inline void zero_counters(int32_t* p, int64_t n, int64_t first, int64
     for (int64_t i = first; i < n; i += stride) p[i] = 0;
 }
 
+template <int KMAX>
 __global__ __launch_bounds__(kBlock) void layout_count_kernel(
     const int32_t* __restrict__ idx, int T, int E, int R, int k, int epr,
     int32_t* __restrict__ blk_rank_cnt, int32_t* __restrict__ blk_exp_cnt,
@@ -126,7 +113,7 @@ __global__ __launch_bounds__(kBlock) void layout_count_kernel(
     const int tid = threadIdx.x;
     const int wave = tid / kWave;
     const int64_t t = (int64_t)blockIdx.x * kLayoutTile + tid;
-    int32_t ids[kMaxK];
+    int32_t ids[KMAX];
     load_token_ids(idx, t, T, k, ids);   // in flight while the histogram clears
     for (int e = tid; e < E; e += kBlock) s_hist[e] = 0;
     __syncthreads();
@@ -149,7 +136,7 @@ __global__ __launch_bounds__(kBlock) void layout_count_kernel(
 //         (used only when every tile can be resident at once).
 // In modes 1 and 2 the grid has nblocks + 1 workgroups: workgroup nblocks
 // owns no tokens and computes the expert totals and offsets.
-template <int MODE>
+template <int MODE, int KMAX>
 __global__ __launch_bounds__(kBlock) void layout_main_kernel(
     const int32_t* __restrict__ idx, int T, int E, int R, int k, int epr, int nblocks,
     int32_t* __restrict__ blk_rank_cnt, int32_t* __restrict__ blk_exp_cnt,
@@ -163,10 +150,9 @@ __global__ __launch_bounds__(kBlock) void layout_main_kernel(
     __shared__ int32_t s_hist[(SINGLE || FUSED) ? kMaxE : 1];
     __shared__ int32_t s_exp[kMaxE];
     __shared__ int32_t s_wcnt[kBlock / kWave][kMaxR];
-    __shared__ int32_t s_pre[kMaxR];     // rows of rank r in earlier tiles
-    __shared__ int32_t s_tot[kMaxR];     // rows of rank r in all tiles
     __shared__ int32_t s_base[kMaxR];    // first slot of rank r in this tile
     __shared__ int32_t s_part[kBlock];
+    __shared__ int32_t s_part2[kBlock];
     __shared__ uint64_t s_ball[kBlock / kWave][kMaxR];   // per-wave rank ballots
     __shared__ int32_t s_wbase[kBlock / kWave][kMaxR];   // first slot of rank r in the wave
     const int tid = threadIdx.x;
@@ -185,7 +171,7 @@ __global__ __launch_bounds__(kBlock) void layout_main_kernel(
     // the token's expert ids are requested first, so that their latency
     // overlaps the clearing of the histogram (the expert workgroup's tokens
     // are all past T: nothing is loaded there)
-    int32_t ids[kMaxK];
+    int32_t ids[KMAX];
     load_token_ids(idx, t, T, k, ids);
     if (SINGLE || FUSED) {
         for (int e = tid; e < E; e += kBlock) s_hist[e] = 0;
@@ -225,26 +211,17 @@ __global__ __launch_bounds__(kBlock) void layout_main_kernel(
         return;
     }
 
-    // rank totals and the prefix over earlier tiles
+    // rank totals and the prefix over earlier tiles, in lanes < R of wave 0
+    int32_t my_tot = 0, my_pre = 0;
     if (SINGLE) {
-        if (tid < R) {
-            int32_t tot = 0;
-            for (int w = 0; w < kBlock / kWave; ++w) tot += s_wcnt[w][tid];
-            s_pre[tid] = 0;
-            s_tot[tid] = tot;
-        }
+        if (tid < R)
+            for (int w = 0; w < kBlock / kWave; ++w) my_tot += s_wcnt[w][tid];
     } else {
-        if (tid < R) {
-            s_pre[tid] = 0;
-            s_tot[tid] = 0;
-        }
-        __syncthreads();
-        column_sums(blk_rank_cnt, nblocks, R, b, s_tot, s_pre);
+        rank_column_sums(blk_rank_cnt, nblocks, R, b, s_part, s_part2, &my_tot, &my_pre);
     }
-    __syncthreads();
     if (wave == 0) {
         // exclusive scan of the rank totals across lanes (R <= 64)
-        int32_t tot = lane < R ? s_tot[lane] : 0;
+        int32_t tot = lane < R ? my_tot : 0;
         int32_t msgs = (tot + kMsgRows - 1) / kMsgRows;
         int32_t incl = tot, mincl = msgs;
         for (int d = 1; d < kWave; d <<= 1) {
@@ -256,7 +233,7 @@ __global__ __launch_bounds__(kBlock) void layout_main_kernel(
             }
         }
         int32_t off = incl - tot;
-        if (lane < R) s_base[lane] = off + s_pre[lane];
+        if (lane < R) s_base[lane] = off + my_pre;
         if (b == 0) {
             if (lane < R) {
                 cnt_rank[lane] = tot;
@@ -683,6 +660,7 @@ int64_t max_resident_ll_tiles() {
 
 // Tiles of the one-kernel layout that can be resident at once on the current
 // device (workgroups per CU from the occupancy calculator x CUs), or 0.
+template <int KMAX>
 int64_t max_resident_layout_tiles() {
     // per process (the library targets one GPU model); threads that race to
     // fill it compute the same value
@@ -693,7 +671,7 @@ int64_t max_resident_layout_tiles() {
         if (hipGetDevice(&dev) == hipSuccess &&
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
             hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &per_cu, reinterpret_cast<const void*>(layout_main_kernel<2>), kBlock, 0) ==
+                &per_cu, reinterpret_cast<const void*>(layout_main_kernel<2, KMAX>), kBlock, 0) ==
                 hipSuccess)
             v = (int64_t)cus * per_cu;
         else
@@ -701,6 +679,41 @@ int64_t max_resident_layout_tiles() {
         cached.store(v, std::memory_order_relaxed);
     }
     return v;
+}
+
+// The layout's kernels for k <= KMAX: one workgroup when T fits one tile,
+// else the one-kernel form when every tile (and the expert workgroup) can be
+// resident at once, else the counting pass and the second pass.
+template <int KMAX>
+void launch_layout(const ep_shape_t& s, const Workspace& w, const int32_t* topk_idx,
+                   int32_t* num_tokens_per_rank, int32_t* num_tokens_per_expert,
+                   int32_t* rank_offset, int32_t* expert_offset, uint8_t* is_token_in_rank,
+                   int32_t* send_slot, int32_t* dev_status, hipStream_t stream) {
+    const int epr = s.E / s.R;
+    const int nb = w.layout_blocks;
+    int32_t* counters = w.msg_arrivals;
+    if (nb == 1) {
+        hipLaunchKernelGGL((layout_main_kernel<0, KMAX>), dim3(1), dim3(kBlock), 0, stream,
+                           topk_idx, s.T, s.E, s.R, s.k, epr, 1, (int32_t*)nullptr,
+                           (int32_t*)nullptr, num_tokens_per_rank, num_tokens_per_expert,
+                           rank_offset, expert_offset, w.msg_base, is_token_in_rank, send_slot,
+                           counters, w.counters_n, w.barrier, dev_status);
+    } else if (nb + 1 <= max_resident_layout_tiles<KMAX>()) {
+        hipLaunchKernelGGL((layout_main_kernel<2, KMAX>), dim3(nb + 1), dim3(kBlock), 0, stream,
+                           topk_idx, s.T, s.E, s.R, s.k, epr, nb, w.blk_rank_cnt, w.blk_exp_cnt,
+                           num_tokens_per_rank, num_tokens_per_expert, rank_offset, expert_offset,
+                           w.msg_base, is_token_in_rank, send_slot, counters, w.counters_n,
+                           w.barrier, dev_status);
+    } else {
+        hipLaunchKernelGGL((layout_count_kernel<KMAX>), dim3(nb), dim3(kBlock), 0, stream,
+                           topk_idx, s.T, s.E, s.R, s.k, epr, w.blk_rank_cnt, w.blk_exp_cnt,
+                           counters, w.counters_n, dev_status);
+        hipLaunchKernelGGL((layout_main_kernel<1, KMAX>), dim3(nb + 1), dim3(kBlock), 0, stream,
+                           topk_idx, s.T, s.E, s.R, s.k, epr, nb, w.blk_rank_cnt, w.blk_exp_cnt,
+                           num_tokens_per_rank, num_tokens_per_expert, rank_offset, expert_offset,
+                           w.msg_base, is_token_in_rank, send_slot, counters, w.counters_n,
+                           w.barrier, dev_status);
+    }
 }
 
 }  // namespace ep
@@ -722,32 +735,14 @@ extern "C" int ep_dispatch_layout(const ep_shape_t* shape, const int32_t* topk_i
     if (((uintptr_t)send_slot & 15) || ((uintptr_t)is_token_in_rank & 3)) return EP_ERR_INVALID_ARG;
     if (ws_bytes < workspace_bytes(s)) return EP_ERR_INVALID_ARG;
     Workspace w = carve_workspace(s, workspace);
-    const int epr = s.E / s.R;
-    const int nb = w.layout_blocks;
-    int32_t* counters = w.msg_arrivals;
     clear_hip_error();
-    if (nb == 1) {
-        hipLaunchKernelGGL(layout_main_kernel<0>, dim3(1), dim3(kBlock), 0, stream, topk_idx, s.T,
-                           s.E, s.R, s.k, epr, 1, (int32_t*)nullptr, (int32_t*)nullptr,
-                           num_tokens_per_rank, num_tokens_per_expert, rank_offset, expert_offset,
-                           w.msg_base, is_token_in_rank, send_slot, counters, w.counters_n,
-                           w.barrier, dev_status);
-    } else if (nb + 1 <= max_resident_layout_tiles()) {
-        hipLaunchKernelGGL(layout_main_kernel<2>, dim3(nb + 1), dim3(kBlock), 0, stream, topk_idx, s.T,
-                           s.E, s.R, s.k, epr, nb, w.blk_rank_cnt, w.blk_exp_cnt,
-                           num_tokens_per_rank, num_tokens_per_expert, rank_offset, expert_offset,
-                           w.msg_base, is_token_in_rank, send_slot, counters, w.counters_n,
-                           w.barrier, dev_status);
-    } else {
-        hipLaunchKernelGGL(layout_count_kernel, dim3(nb), dim3(kBlock), 0, stream, topk_idx, s.T,
-                           s.E, s.R, s.k, epr, w.blk_rank_cnt, w.blk_exp_cnt, counters,
-                           w.counters_n, dev_status);
-        hipLaunchKernelGGL(layout_main_kernel<1>, dim3(nb + 1), dim3(kBlock), 0, stream, topk_idx, s.T,
-                           s.E, s.R, s.k, epr, nb, w.blk_rank_cnt, w.blk_exp_cnt,
-                           num_tokens_per_rank, num_tokens_per_expert, rank_offset, expert_offset,
-                           w.msg_base, is_token_in_rank, send_slot, counters, w.counters_n,
-                           w.barrier, dev_status);
-    }
+    if (s.k <= 8)
+        launch_layout<8>(s, w, topk_idx, num_tokens_per_rank, num_tokens_per_expert, rank_offset,
+                         expert_offset, is_token_in_rank, send_slot, dev_status, stream);
+    else
+        launch_layout<kMaxK>(s, w, topk_idx, num_tokens_per_rank, num_tokens_per_expert,
+                             rank_offset, expert_offset, is_token_in_rank, send_slot, dev_status,
+                             stream);
     EP_HIP_CHECK(hipGetLastError());
     return EP_OK;
 }

@@ -8,12 +8,14 @@
 namespace ep {
 
 // The k expert ids of token t (-1 past k, and for t >= T), all loads
-// issued before any is used (one memory latency, not k).
+// issued before any is used (one memory latency, not k).  KMAX >= k bounds
+// the unrolled code: kernels built for k <= 8 carry a quarter of it.
+template <int KMAX>
 __device__ inline void load_token_ids(const int32_t* __restrict__ idx, int64_t t, int T, int k,
-                                      int32_t (&ids)[kMaxK]) {
+                                      int32_t (&ids)[KMAX]) {
     const int32_t* row = idx + t * k;
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j) ids[j] = (t < T && j < k) ? row[j] : -1;
+    for (int j = 0; j < KMAX; ++j) ids[j] = (t < T && j < k) ? row[j] : -1;
 }
 
 // Owner rank e / epr of expert e in [0, E), by one float multiply instead of
@@ -30,13 +32,14 @@ __device__ inline int rank_of_expert(int e, float inv_epr) {
 // Rank mask of a token from its ids; bad ids are reported (once per token)
 // and skipped.  When `hist` is given, the token's valid experts are counted
 // in it (LDS).
-__device__ inline uint64_t rank_mask_of(const int32_t (&ids)[kMaxK], int E, int k, int epr,
+template <int KMAX>
+__device__ inline uint64_t rank_mask_of(const int32_t (&ids)[KMAX], int E, int k, int epr,
                                         int32_t* st, int32_t* hist) {
     const float inv_epr = inv_experts_per_rank(epr);
     uint64_t m = 0;
     bool bad = false;
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
+    for (int j = 0; j < KMAX; ++j) {
         const int e = ids[j];
         if (j >= k || e == -1) continue;
         if ((unsigned)e >= (unsigned)E) {   // below -1, or E and above

@@ -125,6 +125,12 @@ CASES = [
     (200, 640, 64, 16, 4, 1, 0.0, 3, 1024, 256),
     (1500, 6400, 256, 32, 8, 1, 0.0, 8, 1024, 256),
     (700, 8320, 64, 16, 4, 1, 0.05, 8, 1024, 256),
+    # layout store paths and unroll bounds: two ranks (lane per rank), a
+    # rank count that neither divides 64 nor is a multiple of 4 (4-entry
+    # groups), and k above 8 in one tile and in several
+    (200, 64, 8, 2, 3, 0, 0.1, 2, 64, 16),
+    (250, 64, 96, 12, 12, 0, 0.1, 4, 64, 16),
+    (3000, 32, 48, 24, 9, 0, 0.0, 4, 1024, 256),
 ]
 
 
@@ -187,16 +193,18 @@ def test_layout_many_tiles():
     assert_layout_equal(g, L)
 
 
-def test_layout_more_tiles_than_resident():
+@pytest.mark.parametrize("k", [4, 10])
+def test_layout_more_tiles_than_resident(k):
     """300,000 tokens (1172 tiles) exceed what can be resident at once, so the
-    layout takes its two-kernel path; the result is the same."""
-    T, E, R, k = 300000, 64, 64, 4
-    rng = np.random.default_rng(18)
+    layout takes its two-kernel path; the result is the same (kernels built
+    for k <= 8 and for larger k)."""
+    T, E, R = 300000, 64, 64
+    rng = np.random.default_rng(18 + k)
     keys = rng.random((T, E), dtype=np.float32)
     idx = np.ascontiguousarray(np.argpartition(-keys, k, axis=1)[:, :k].astype(np.int32))
     del keys
     L = oracle.layout(idx, E, R)
-    log("[parity] layout T=300000 R=64 (two-kernel path)")
+    log(f"[parity] layout T=300000 R=64 k={k} (two-kernel path)")
     x = np.zeros((T, 8), np.uint16)
     w = np.ones((T, k), np.float32)
     g = run_hip(T, 8, E, R, k, 0, x, idx, w, capacity_rows=1, ring_cfg=None)

@@ -975,7 +975,7 @@ __global__ __launch_bounds__(WAVES * kWave) void pack_kernel(PackArgs a) {
 // closed-form publication are those of the small-batch pack.
 constexpr int kFusedMaxT = kPackWavesSmall * kWave;
 
-template <int VPL, int FMT>
+template <int VPL, int FMT, int KMAX>
 __global__ __launch_bounds__(kPackWavesSmall* kWave) void fused_small_kernel(PackArgs a) {
     constexpr int kWaves = kPackWavesSmall;
     static_assert(kWaves * kWave == kBlock, "the expert scan takes a kBlock-thread workgroup");
@@ -1005,8 +1005,8 @@ __global__ __launch_bounds__(kPackWavesSmall* kWave) void fused_small_kernel(Pac
     if (first)
         for (int e = tid; e < a.E; e += kBlock) s_hist[e] = 0;
     __syncthreads();
-    const uint64_t mask = token_rank_mask(a.idx, (int64_t)wave * kWave + lane, a.T, a.E, a.k,
-                                          a.epr, a.st, first ? s_hist : nullptr);
+    const uint64_t mask = token_rank_mask<KMAX>(a.idx, (int64_t)wave * kWave + lane, a.T, a.E,
+                                                a.k, a.epr, a.st, first ? s_hist : nullptr);
     wave_rank_counts(mask, R, s_cnt[wave], s_ball[wave]);
     __syncthreads();
     if (wave == 0) {
@@ -1238,8 +1238,8 @@ __device__ __forceinline__ int32_t fused_rows(const PackArgs& a, int p, int64_t 
     return s_lane;
 }
 
-// One workgroup per CU: WAVES / 4 wavefronts per SIMD.
-template <int VPL, int FMT, int WAVES, int PUB>
+// One workgroup per CU: WAVES / 4 wavefronts per SIMD.  Built for k <= KMAX.
+template <int VPL, int FMT, int WAVES, int PUB, int KMAX>
 __global__ __launch_bounds__(WAVES * kWave, WAVES / 4) void fused_large_kernel(PackArgs a) {
     constexpr int kWaves = WAVES;
     constexpr int kT = WAVES * kWave;
@@ -1272,7 +1272,7 @@ __global__ __launch_bounds__(WAVES * kWave, WAVES / 4) void fused_large_kernel(P
     // 1. ballots of each pass's block (wavefront p % kWaves takes pass p).
     // Only the ids are loaded before them: a wavefront's memory counter
     // retires in order, so anything issued earlier would hold them up.
-    int32_t ids[kMaxK];
+    int32_t ids[KMAX];
     if (wave < a.npass && b + (int64_t)wave * G < a.ngroups)
         load_token_ids(a.idx, (b + (int64_t)wave * G) * kWaves / kWave * kWave + lane, a.T, a.k,
                        ids);
@@ -1287,10 +1287,7 @@ __global__ __launch_bounds__(WAVES * kWave, WAVES / 4) void fused_large_kernel(P
             const bool first = (g * kWaves) % kWave == 0;
             const uint64_t mask =
                 rank_mask_of(ids, a.E, a.k, a.epr, a.st, (first && count_here) ? s_hist : nullptr);
-            for (int r = 0; r < R; ++r) {
-                const uint64_t bb = __ballot((mask >> r) & 1ull);
-                if (lane == r) mine = bb;
-            }
+            mine = wave_bit_transpose(mask);   // lane r < R: the ballot of rank r; others 0
             if (first && lane < R) a.wave_cnt[blk * R + lane] = (int32_t)__popcll(mine);
         }
         if (lane < R) s_ball[p][lane] = mine;
@@ -2156,8 +2153,12 @@ int launch_fused_fmt(PackArgs a, int64_t waves, hipStream_t stream) {
     const int64_t passes = ceil_div(a.ngroups, cap);
     const int64_t blocks = ceil_div(a.ngroups, passes);
     clear_hip_error();
-    hipLaunchKernelGGL((fused_small_kernel<VPL, FMT>), dim3((unsigned)blocks),
-                       dim3(kPackWavesSmall * kWave), 0, stream, a);
+    if (a.k <= 8)
+        hipLaunchKernelGGL((fused_small_kernel<VPL, FMT, 8>), dim3((unsigned)blocks),
+                           dim3(kPackWavesSmall * kWave), 0, stream, a);
+    else
+        hipLaunchKernelGGL((fused_small_kernel<VPL, FMT, kMaxK>), dim3((unsigned)blocks),
+                           dim3(kPackWavesSmall * kWave), 0, stream, a);
     EP_HIP_CHECK(hipGetLastError());
     return EP_OK;
 }
@@ -2194,7 +2195,7 @@ int64_t resident_blocks(K kernel, int threads) {
     return (int64_t)cus * per_cu;
 }
 
-template <int VPL, int FMT, int WAVES>
+template <int VPL, int FMT, int WAVES, int KMAX>
 int launch_fused_large_fmt(PackArgs a, hipStream_t stream, bool dry) {
     a.ngroups = ceil_div(a.T, WAVES);
     const int64_t cap = a.has_ring ? stream_grid_cap(a.ngroups, WAVES)
@@ -2208,9 +2209,9 @@ int launch_fused_large_fmt(PackArgs a, hipStream_t stream, bool dry) {
     const int pub = a.has_ring ? kPubStream : kPubNone;
     int64_t rm = room[a.has_ring ? 1 : 0].load(std::memory_order_relaxed);
     if (rm < 0) {
-        rm = a.has_ring ? resident_blocks(fused_large_kernel<VPL, FMT, WAVES, kPubStream>,
+        rm = a.has_ring ? resident_blocks(fused_large_kernel<VPL, FMT, WAVES, kPubStream, KMAX>,
                                           WAVES * kWave)
-                        : resident_blocks(fused_large_kernel<VPL, FMT, WAVES, kPubNone>,
+                        : resident_blocks(fused_large_kernel<VPL, FMT, WAVES, kPubNone, KMAX>,
                                           WAVES * kWave);
         room[a.has_ring ? 1 : 0].store(rm, std::memory_order_relaxed);
     }
@@ -2223,11 +2224,11 @@ int launch_fused_large_fmt(PackArgs a, hipStream_t stream, bool dry) {
     const dim3 grid((unsigned)(blocks + a.expert_wg)), block(WAVES * kWave);
     clear_hip_error();
     if (pub == kPubStream)
-        hipLaunchKernelGGL((fused_large_kernel<VPL, FMT, WAVES, kPubStream>), grid, block, 0,
-                           stream, a);
+        hipLaunchKernelGGL((fused_large_kernel<VPL, FMT, WAVES, kPubStream, KMAX>), grid, block,
+                           0, stream, a);
     else
-        hipLaunchKernelGGL((fused_large_kernel<VPL, FMT, WAVES, kPubNone>), grid, block, 0, stream,
-                           a);
+        hipLaunchKernelGGL((fused_large_kernel<VPL, FMT, WAVES, kPubNone, KMAX>), grid, block, 0,
+                           stream, a);
     EP_HIP_CHECK(hipGetLastError());
     return EP_OK;
 }
@@ -2237,18 +2238,24 @@ int launch_fused_large_fmt(PackArgs a, hipStream_t stream, bool dry) {
 // and the two-kernel pack would not split its rows (smaller batches, smaller
 // or split rows and fp8 take the two-kernel path).  dry: only whether the
 // batch would take the path.
+template <int VPL, int FMT, int WAVES>
+int launch_fused_large_k(PackArgs& a, hipStream_t stream, bool dry) {
+    return a.k <= 8 ? launch_fused_large_fmt<VPL, FMT, WAVES, 8>(a, stream, dry)
+                    : launch_fused_large_fmt<VPL, FMT, WAVES, kMaxK>(a, stream, dry);
+}
+
 int launch_fused_large(PackArgs& a, int fmt, hipStream_t stream, bool dry = false) {
     if ((int64_t)a.T < kPackSmallWaves) return kNotTaken;
     const int nv = a.nv;
     if (fmt == EP_FMT_BF16) {
         if (nv <= 128) return kNotTaken;
-        if (nv <= 256) return launch_fused_large_fmt<4, EP_FMT_BF16, kPackWaves>(a, stream, dry);
-        if (nv <= 512) return launch_fused_large_fmt<8, EP_FMT_BF16, kPackWaves>(a, stream, dry);
+        if (nv <= 256) return launch_fused_large_k<4, EP_FMT_BF16, kPackWaves>(a, stream, dry);
+        if (nv <= 512) return launch_fused_large_k<8, EP_FMT_BF16, kPackWaves>(a, stream, dry);
         if (nv <= 896) {
             if (rank_rows_split(a, fmt)) return kNotTaken;   // two wavefronts a row
-            return launch_fused_large_fmt<kPackVplH7168, EP_FMT_BF16, kPackWaves>(a, stream, dry);
+            return launch_fused_large_k<kPackVplH7168, EP_FMT_BF16, kPackWaves>(a, stream, dry);
         }
-        if (nv <= 1024) return launch_fused_large_fmt<16, EP_FMT_BF16, kPackWaves>(a, stream, dry);
+        if (nv <= 1024) return launch_fused_large_k<16, EP_FMT_BF16, kPackWaves>(a, stream, dry);
         return kNotTaken;
     }
     // fp8 rows stay with the two calls: the one-kernel version (8-wavefront

@@ -53,29 +53,25 @@ __device__ inline uint64_t rank_mask_of(const int32_t (&ids)[KMAX], int E, int k
     return m;
 }
 
-// Rank mask of token t (0 for t >= T), as above.
+// Rank mask of token t (0 for t >= T), as above, for k <= KMAX.
+template <int KMAX>
 __device__ inline uint64_t token_rank_mask(const int32_t* __restrict__ idx, int64_t t, int T,
                                            int E, int k, int epr, int32_t* st, int32_t* hist) {
-    int32_t ids[kMaxK];
+    int32_t ids[KMAX];
     load_token_ids(idx, t, T, k, ids);
     return rank_mask_of(ids, E, k, epr, st, hist);
 }
 
-// Per-wave rank ballots: bit i of ball_r = the wave's token i goes to rank r.
-// Lane l ends up holding ball_{l mod R} (all lanes, so that every group of R
-// lanes has the full set); lanes < R write their count to wcnt[r] and, when
-// given, the ballot to ball[r].
-//
-// The ballots are the transpose of the wave's 64 x 64 bit matrix (lane =
-// token, bit = rank), done in six butterfly steps instead of one ballot per
-// rank: at step s, lanes i and i ^ s (i without bit s) swap the off-diagonal
-// blocks, i's bits at positions with bit s set against its partner's bits at
-// positions with bit s clear.  One 32-bit shuffle per step: for s = 32 a lane
-// sends the word its partner takes; below that, the 16 bits wanted of each
-// half are packed into one word.  A last shuffle gives lanes >= R the
-// ballot of lane mod R (the transpose leaves them zero).
-__device__ inline uint64_t wave_rank_counts(uint64_t mask, int R, int32_t* wcnt,
-                                            uint64_t* ball = nullptr) {
+// Transpose of the wave's 64 x 64 bit matrix whose row l is lane l's
+// `mask`: lane j receives the word whose bit i is bit j of lane i's mask
+// (with lane = token and bit = rank, lane r gets the ballot of rank r; lanes
+// past the highest rank get zero).  Six butterfly steps instead of one ballot
+// per rank: at step s, lanes i and i ^ s (i without bit s) swap the
+// off-diagonal blocks, i's bits at positions with bit s set against its
+// partner's bits at positions with bit s clear.  One 32-bit shuffle per step:
+// for s = 32 a lane sends the word its partner takes; below that, the 16 bits
+// wanted of each half are packed into one word.  All lanes must be active.
+__device__ inline uint64_t wave_bit_transpose(uint64_t mask) {
     const int lane = lane_id();
     uint32_t lo = (uint32_t)mask, hi = (uint32_t)(mask >> 32);
     {
@@ -108,12 +104,25 @@ __device__ inline uint64_t wave_rank_counts(uint64_t mask, int R, int32_t* wcnt,
             hi = (hi & m) | (ghi << s);
         }
     }
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Per-wave rank ballots: bit i of ball_r = the wave's token i goes to rank r.
+// Lane l ends up holding ball_{l mod R} (all lanes, so that every group of R
+// lanes has the full set); lanes < R write their count to wcnt[r] and, when
+// given, the ballot to ball[r].  The ballots are the transpose of the
+// tokens' rank masks; one more shuffle gives lanes >= R the ballot of lane
+// mod R.
+__device__ inline uint64_t wave_rank_counts(uint64_t mask, int R, int32_t* wcnt,
+                                            uint64_t* ball = nullptr) {
+    const int lane = lane_id();
+    uint64_t mine = wave_bit_transpose(mask);
     if (R < kWave) {
         const int src = lane % R;
-        lo = (uint32_t)__shfl((int)lo, src);
-        hi = (uint32_t)__shfl((int)hi, src);
+        const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)mine, src);
+        const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(mine >> 32), src);
+        mine = ((uint64_t)hi << 32) | lo;
     }
-    const uint64_t mine = ((uint64_t)hi << 32) | lo;
     if (lane < R) {
         wcnt[lane] = (int32_t)__popcll(mine);
         if (ball) ball[lane] = mine;

@@ -198,6 +198,7 @@ LARGE_EDGES = [
     (4095, 4104, 7, 7, 3, 0.2, 3),      # one expert per rank, R not a power of two, ragged T
     (1025, 2048, 1, 1, 1, 0.5, 1),      # one rank, half the choices dropped, one token past 1024
     (6000, 7168, 64, 64, 1, 0.0, 8),    # k = 1, 64 ranks
+    (4096, 2048, 256, 32, 12, 0.05, 4), # k = 12: the kernel built for k <= 32
 ]
 
 

@@ -588,9 +588,9 @@ def bench_workload(w, args, scratch, sink, dev) -> dict:
         if run.plan == run.ep.EP_FUSED_ONE_KERNEL_LARGE and prefix == "fused_large_kernel":
             entry["roofline"]["note"] += (
                 "; this kernel is the routing layout and the pack in one launch, so its time "
-                "includes the layout's latency (about 14 us of id loads, ballots, a grid barrier "
-                "and a table read before the first row store): algorithmic bytes are the "
-                "layout's and the pack's")
+                "includes the layout's latency (id loads, ballots, a grid barrier and a table "
+                "read before the first row store): algorithmic bytes are the layout's and the "
+                "pack's")
 
     if run.graphs is None and args.flush_reps > 0:
         d, fevs = flushed_steps(run, args.flush_reps, scratch, sink)

@@ -500,7 +500,6 @@ __global__ __launch_bounds__(kBlock) void ll_layout_kernel(
     __shared__ int32_t s_base[kLLLayoutMaxE];                  // offset + earlier tiles
     __shared__ int32_t s_tot[kLLLayoutMaxE];
     __shared__ int32_t s_wsum[kW];
-    __shared__ int s_rounds;
     const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
     const int b = blockIdx.x;
     uint32_t gen = 0;
@@ -517,7 +516,6 @@ __global__ __launch_bounds__(kBlock) void ll_layout_kernel(
         s_whist[wave][e] = 0;
         s_mask[wave][e] = 0ull;
     }
-    if (tid == 0) s_rounds = 0;
 #pragma unroll
     for (int j = 0; j < KMAX; ++j)
         if (ids[j] < -1 || ids[j] >= E) {
@@ -536,33 +534,40 @@ __global__ __launch_bounds__(kBlock) void ll_layout_kernel(
         if (ids[j] >= 0 && o + 1 > my_rounds) my_rounds = o + 1;
     }
     __syncthreads();
-    if (my_rounds) atomicMax(&s_rounds, my_rounds);
 #pragma unroll
     for (int j = 0; j < KMAX; ++j)
         if (ids[j] >= 0) atomicAdd(&s_whist[wave][ids[j]], 1);
     __syncthreads();
-    // 1. the tile's histogram for the others; the dispatch's counters start at zero
+    // 1. the tile's histogram for the others (the per-wavefront counts become
+    // their exclusive prefix over the wavefronts, which step 4 reads); the
+    // dispatch's counters start at zero
     for (int e = tid; e < E; e += kBlock) {
         int32_t c = 0;
 #pragma unroll
-        for (int w = 0; w < kW; ++w) c += s_whist[w][e];
+        for (int w = 0; w < kW; ++w) {
+            const int32_t h = s_whist[w][e];
+            s_whist[w][e] = c;
+            c += h;
+        }
         blk_exp_cnt[(int64_t)b * E + e] = c;
     }
     zero_counters(counters, counters_n, (int64_t)b * kBlock + tid, (int64_t)gridDim.x * kBlock);
     // 2. every tile's histogram is in the table after this
     if (!grid_barrier<false>(bar, (uint32_t)gridDim.x, st, gen)) return;
-    // 3. column sums: totals, and the rows in earlier tiles
-    constexpr int kRows = 16;
+    // 3. column sums: totals, and the rows in earlier tiles (32 rows in
+    // flight per thread; loads past the last row re-read it and count
+    // nothing, so none is predicated)
+    constexpr int kRows = 32;
     for (int e = tid; e < E; e += kBlock) {
         int32_t tot = 0, pre = 0;
         for (int r0 = 0; r0 < nblocks; r0 += kRows) {
             int32_t q[kRows];
 #pragma unroll
             for (int u = 0; u < kRows; ++u)
-                q[u] = r0 + u < nblocks ? blk_exp_cnt[(int64_t)(r0 + u) * E + e] : 0;
+                q[u] = blk_exp_cnt[(int64_t)min(r0 + u, nblocks - 1) * E + e];
 #pragma unroll
             for (int u = 0; u < kRows; ++u) {
-                tot += q[u];
+                tot += r0 + u < nblocks ? q[u] : 0;
                 pre += r0 + u < b ? q[u] : 0;
             }
         }
@@ -606,27 +611,31 @@ __global__ __launch_bounds__(kBlock) void ll_layout_kernel(
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
         pos[j] = occ[j];
-        if (ids[j] >= 0) {
-            int32_t p = s_base[ids[j]];
-            for (int w = 0; w < wave; ++w) p += s_whist[w][ids[j]];
-            pos[j] += p;
-        }
+        if (ids[j] >= 0) pos[j] += s_base[ids[j]] + s_whist[wave][ids[j]];
     }
+    // The rounds are the wavefront's own (its masks are its own LDS rows):
+    // their count is the wavefront's maximum, and a wavefront-scope fence
+    // between the steps orders them (a wavefront's LDS operations complete
+    // in order), so no workgroup barrier is needed.
     const unsigned long long below = (1ull << lane) - 1ull;
-    const int rounds = s_rounds;
+    int rounds = my_rounds;
+    for (int d = 1; d < kWave; d <<= 1) rounds = max(rounds, __shfl_xor(rounds, d));
     for (int o = 0; o < rounds; ++o) {
 #pragma unroll
         for (int j = 0; j < KMAX; ++j)
             if (ids[j] >= 0 && occ[j] == o) atomicOr(&s_mask[wave][ids[j]], 1ull << lane);
-        __syncthreads();
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int j = 0; j < KMAX; ++j)
             if (ids[j] >= 0) pos[j] += __popcll(s_mask[wave][ids[j]] & below);
-        __syncthreads();
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int j = 0; j < KMAX; ++j)
             if (ids[j] >= 0) s_mask[wave][ids[j]] = 0ull;
-        __syncthreads();
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
     }
     if (t < T) {
 #pragma unroll

@@ -1841,7 +1841,7 @@ __global__ __launch_bounds__(kPackWavesSmall* kWave) void ll_fused_small_kernel(
     __shared__ int32_t s_tot[kLLFusedMaxE];
     __shared__ int32_t s_row[kFusedMaxT][KMAX];                 // row of choice (t, j), or -1
     __shared__ int32_t s_part[kBlock];
-    __shared__ int s_rounds, s_last;
+    __shared__ int s_last;
     const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
     const bool first = blockIdx.x == 0;
     const int E = a.E, k = a.k;
@@ -1861,11 +1861,13 @@ __global__ __launch_bounds__(kPackWavesSmall* kWave) void ll_fused_small_kernel(
     const int32_t* row = a.idx + t * k;
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) ids[j] = (j < k && t < a.T) ? row[j] : -1;
+    // s_cnt[wave] and s_mask[wave] are this wavefront's own LDS rows: it
+    // clears them and runs its rounds alone, the steps ordered by
+    // wavefront fences (a wavefront's LDS operations complete in order)
     for (int e = lane; e < E; e += kWave) {
         s_cnt[wave][e] = 0;
         s_mask[wave][e] = 0ull;
     }
-    if (tid == 0) s_rounds = 0;
 #pragma unroll
     for (int j = 0; j < KMAX; ++j)
         if (ids[j] < -1 || ids[j] >= E) {
@@ -1882,10 +1884,10 @@ __global__ __launch_bounds__(kPackWavesSmall* kWave) void ll_fused_small_kernel(
         occ[j] = o;
         if (ids[j] >= 0 && o + 1 > my_rounds) my_rounds = o + 1;
     }
-    __syncthreads();
-    if (my_rounds) atomicMax(&s_rounds, my_rounds);
-    __syncthreads();
-    const int rounds = s_rounds;
+    int rounds = my_rounds;   // the wavefront's maximum
+    for (int d = 1; d < kWave; d <<= 1) rounds = max(rounds, __shfl_xor(rounds, d));
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
     const unsigned long long below = (1ull << lane) - 1ull;
     int32_t pos[KMAX];
 #pragma unroll
@@ -1894,15 +1896,19 @@ __global__ __launch_bounds__(kPackWavesSmall* kWave) void ll_fused_small_kernel(
 #pragma unroll
         for (int j = 0; j < KMAX; ++j)
             if (ids[j] >= 0 && occ[j] == o) atomicOr(&s_mask[wave][ids[j]], 1ull << lane);
-        __syncthreads();
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int j = 0; j < KMAX; ++j)
             if (ids[j] >= 0) pos[j] += __popcll(s_mask[wave][ids[j]] & below);
         for (int e = lane; e < E; e += kWave) s_cnt[wave][e] += __popcll(s_mask[wave][e]);
-        __syncthreads();
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
         for (int e = lane; e < E; e += kWave) s_mask[wave][e] = 0ull;
-        __syncthreads();
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
     }
+    __syncthreads();   // every wavefront's counts
     // totals, per-wavefront bases, offsets
     for (int e = tid; e < E; e += kT) {
         int32_t run = 0;

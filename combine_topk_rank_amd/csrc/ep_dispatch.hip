@@ -717,10 +717,17 @@ __device__ inline void load_row_chunk(const PackArgs& a, int64_t t, int chunk, u
 // dispatch also needs fewer registers with these (train 197.8 -> 196.3 us
 // per step, skewed 691 -> 681 us).  The two-kernel packs keep load_row_chunk
 // (fp8 was 1 us slower with buffer loads).
+// t and chunk are the same on every lane, but the compiler cannot see that
+// (they derive from threadIdx.x / 64): read from the first lane, the buffer
+// descriptor is scalar, and each load is one instruction instead of a loop
+// over the distinct descriptors of the lanes.
 template <int VPL>
 __device__ inline void prefetch_row_chunk(const PackArgs& a, int64_t t, int chunk,
                                           u32x4 (&v)[VPL]) {
     const int lane = lane_id();
+    t = (int64_t)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)t >> 32)) << 32) |
+                  (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)t));
+    chunk = __builtin_amdgcn_readfirstlane(chunk);
     const int v0 = chunk * VPL * kWave;
     const __amdgpu_buffer_rsrc_t rs =
         buffer_rsrc(const_cast<u32x4*>(a.x + t * a.nv), a.nv * (int32_t)sizeof(u32x4));

@@ -721,8 +721,8 @@ __device__ inline void load_row_chunk(const PackArgs& a, int64_t t, int chunk, u
 // load_row_chunk the compiler waits for the loads at once, so a prefetch
 // issued ahead of the routing loads held them up; the one-kernel large
 // dispatch also needs fewer registers with these (train 197.8 -> 196.3 us
-// per step, skewed 691 -> 681 us).  The two-kernel packs keep load_row_chunk
-// (fp8 was 1 us slower with buffer loads).
+// per step, skewed 691 -> 681 us).  The two-kernel bf16 pack keeps
+// load_row_chunk.
 // t and chunk are the same on every lane, but the compiler cannot see that
 // (they derive from threadIdx.x / 64): read from the first lane, the buffer
 // descriptor is scalar, and each load is one instruction instead of a loop
@@ -924,12 +924,20 @@ __global__ __launch_bounds__(WAVES * kWave) void pack_kernel(PackArgs a) {
     int32_t s_lane = -1;
     uint64_t dmask = 0;
     if (active) {
+        // fp8 rows: the chunk's loads go out before the slot entry's (one
+        // memory latency for both; fp8 step 170.1 -> 169.0 us in alternating
+        // runs).  bf16 rows keep the order below (skewed was 3 us slower).
+        u32x4 v[VPL];
+        if (FMT != EP_FMT_BF16) prefetch_row_chunk<VPL>(a, t, chunk, v);
         if (lane < a.R) s_lane = a.send_slot[t * a.R + lane];
         dmask = __ballot(s_lane >= 0);
         if (PUB == kPubClosed && s_lane >= 0 && (s_lane < a.rank_off[lane] || s_lane >= a.rank_off[lane + 1]))
             set_error(a.st, EP_ERR_INVALID_ARG);   // send_slot not from this rank_offset
 
-        store_row_chunk<VPL, FMT>(a, t, chunk, s_lane, dmask);
+        if (FMT != EP_FMT_BF16)
+            store_row_chunk_v<VPL, FMT>(a, chunk, s_lane, dmask, v);
+        else
+            store_row_chunk<VPL, FMT>(a, t, chunk, s_lane, dmask);
 
         // per-slot metadata, written by the token's first chunk
         if (chunk == 0) store_slot_metadata(a, t, s_lane, dmask);

@@ -112,6 +112,21 @@ def test_ll_one_call_layout_cases(case):
     _check_case(T, H, E, R, k, fmt, inp, C, depth, mif, one_call_layout=True)
 
 
+def test_ll_one_call_layout_uneven_rounds():
+    """Wavefronts with different numbers of repeat rounds in one tile: ten
+    tokens of one wavefront name a single expert k times (k rounds there),
+    one token of another names it twice, the rest once."""
+    rng = np.random.default_rng(41)
+    T, H, E, R, k = 1000, 64, 64, 8, 6
+    inp = W.make_random_case(rng, T, H, E, R, k)
+    idx = inp["topk_idx"].copy()
+    idx[100:110, :] = idx[100:110, :1]
+    idx[200, 3] = idx[200, 2]
+    inp = dict(inp, topk_idx=idx)
+    log("[ll] one-call layout, uneven repeat rounds")
+    _check_case(T, H, E, R, k, 0, inp, 2, 64, 16, one_call_layout=True)
+
+
 def test_ll_one_call_layout_bad_expert():
     """A bad id is reported and treated as dropped; the rest of the table is
     the oracle's."""
@@ -296,6 +311,19 @@ def test_ll_fused_repeated_experts_and_repeat_calls():
     inp = dict(inp, topk_idx=idx)
     log("[ll-fused] repeated experts, three calls")
     _check_case(T, H, E, R, k, 0, inp, 3, 16, 4, repeat=3, fused=True)
+
+
+def test_ll_fused_uneven_rounds():
+    """One-call path, wavefronts with different numbers of repeat rounds:
+    only wavefront 1's tokens 70..74 name one expert k times."""
+    rng = np.random.default_rng(79)
+    T, H, E, R, k = 200, 64, 32, 8, 4
+    inp = W.make_random_case(rng, T, H, E, R, k)
+    idx = inp["topk_idx"].copy()
+    idx[70:75, :] = idx[70:75, :1]
+    inp = dict(inp, topk_idx=idx)
+    log("[ll-fused] uneven repeat rounds")
+    _check_case(T, H, E, R, k, 0, inp, 3, 64, 16, fused=True)
 
 
 def test_ll_fused_errors():

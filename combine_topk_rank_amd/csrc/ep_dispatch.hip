@@ -501,7 +501,8 @@ __device__ inline ClosedOrder closed_order(const PackArgs& a, const int32_t* ro)
 // Publish command g of the concatenated closed-form order (lanes with
 // `have`); base[c] is the first ticket of channel c.
 __device__ void closed_publish(const PackArgs& a, const ClosedOrder& z,
-                               const unsigned long long* base, int32_t g, bool have) {
+                               const unsigned long long* base, const unsigned long long* seen,
+                               int32_t g, bool have) {
     int j = 0;   // position holding command g
     for (int p = 1; p < a.R; ++p)
         if (bcast(z.start, p) <= g) j = p;
@@ -514,18 +515,21 @@ __device__ void closed_publish(const PackArgs& a, const ClosedOrder& z,
     const bool write = local < nmsg;
     const int32_t rows = write ? min(kMsgRows, cnt - local * kMsgRows) : 0;
     const uint64_t rb = (uint64_t)a.row_bytes;
-    ring_publish<false>(a.ring, have, c, ticket, write ? EP_CMD_WRITE : EP_CMD_ATOMIC,
-                        write ? 0 : EP_ATOMIC_ADD, (uint32_t)rows, (uint32_t)r,
-                        write ? (uint32_t)(rows * rb) : (uint32_t)cnt,
-                        write ? (uint64_t)(o + local * kMsgRows) * rb : 0,
-                        write ? (uint64_t)(local * kMsgRows) * rb : 0, a.st);
+    const RingCmd cmd{write ? (uint32_t)EP_CMD_WRITE : (uint32_t)EP_CMD_ATOMIC,
+                      write ? 0u : (uint32_t)EP_ATOMIC_ADD, (uint32_t)rows, (uint32_t)r,
+                      write ? (uint32_t)(rows * rb) : (uint32_t)cnt,
+                      write ? (uint64_t)(o + local * kMsgRows) * rb : 0,
+                      write ? (uint64_t)(local * kMsgRows) * rb : 0};
+    // the channel's cached consumer position came with the reservation
+    ring_publish_n<1, false>(a.ring, have ? 1 : 0, c, &ticket, &cmd, a.st,
+                             have ? seen[c] : ~0ull);
 }
 
 // One ticket reservation per channel for all of its commands (wavefront-wide;
 // lane of a channel's first rank reserves), bases stored to base[c]; the
 // channel's first command and command count go to cstart[c] and cnum[c].
 __device__ void closed_reserve(const PackArgs& a, const ClosedOrder& z, unsigned long long* base,
-                               int32_t* cstart, int32_t* cnum) {
+                               unsigned long long* seen, int32_t* cstart, int32_t* cnum) {
     const int lane = lane_id();
     const int C = a.ring.channels, R = a.R;
     const int q = R / C, rem = R % C;
@@ -534,7 +538,12 @@ __device__ void closed_reserve(const PackArgs& a, const ClosedOrder& z, unsigned
     const int32_t nxt_start = __shfl(z.start, nxt < kWave ? nxt : kWave - 1);
     if (lane < R && z.start == z.cstart) {   // lane of a channel's first rank
         const int32_t n = (nxt < R ? nxt_start : z.total) - z.cstart;
+        // the cached consumer position travels with the reservation (one
+        // latency for both); the writes check their tickets against it
+        const unsigned long long sn = __hip_atomic_load(
+            a.ring.tail_cache + (size_t)z.c * kPad, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         base[z.c] = ring_reserve(a.ring, z.c, (unsigned)n);
+        seen[z.c] = sn;
         cstart[z.c] = z.cstart;
         cnum[z.c] = n;
     }
@@ -547,8 +556,8 @@ __device__ void closed_reserve(const PackArgs& a, const ClosedOrder& z, unsigned
 // one channel after another.
 template <int NT>
 __device__ void closed_publish_all(const PackArgs& a, const ClosedOrder& z,
-                                   const unsigned long long* base, const int32_t* cstart,
-                                   const int32_t* cnum) {
+                                   const unsigned long long* base, const unsigned long long* seen,
+                                   const int32_t* cstart, const int32_t* cnum) {
     const int nch = a.ring.channels < a.R ? a.ring.channels : a.R;
     const int per_round = NT / nch;
     int32_t nmax = 0;
@@ -558,7 +567,7 @@ __device__ void closed_publish_all(const PackArgs& a, const ClosedOrder& z,
     for (int32_t j0 = 0; j0 < nmax; j0 += per_round) {
         const int32_t j = j0 + jt;
         const bool have = jt < per_round && j < cnum[c];
-        closed_publish(a, z, base, have ? cstart[c] + j : 0, have);
+        closed_publish(a, z, base, seen, have ? cstart[c] + j : 0, have);
     }
 }
 
@@ -990,9 +999,10 @@ __global__ __launch_bounds__(WAVES * kWave) void pack_kernel(PackArgs a) {
         __syncthreads();
         if (!s_last) return;
         __shared__ int32_t s_cstart[kMaxR], s_cnum[kMaxR];
-        if (wave == 0) closed_reserve(a, z, s_base, s_cstart, s_cnum);
+        __shared__ unsigned long long s_seen[kMaxR];
+        if (wave == 0) closed_reserve(a, z, s_base, s_seen, s_cstart, s_cnum);
         __syncthreads();
-        closed_publish_all<kWaves * kWave>(a, z, s_base, s_cstart, s_cnum);
+        closed_publish_all<kWaves * kWave>(a, z, s_base, s_seen, s_cstart, s_cnum);
     }
 }
 
@@ -1135,9 +1145,10 @@ __global__ __launch_bounds__(kPackWavesSmall* kWave) void fused_small_kernel(Pac
     __syncthreads();
     if (!s_last) return;
     __shared__ int32_t s_cstart[kMaxR], s_cnum[kMaxR];
-    if (wave == 0) closed_reserve(a, z, s_base, s_cstart, s_cnum);
+    __shared__ unsigned long long s_seen[kMaxR];
+    if (wave == 0) closed_reserve(a, z, s_base, s_seen, s_cstart, s_cnum);
     __syncthreads();
-    closed_publish_all<kWaves * kWave>(a, z, s_base, s_cstart, s_cnum);
+    closed_publish_all<kWaves * kWave>(a, z, s_base, s_seen, s_cstart, s_cnum);
 }
 
 // ------------------------------------------------- one-kernel large batches
